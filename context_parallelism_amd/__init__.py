@@ -1,0 +1,43 @@
+"""MI355X-native per-rank attention of load-balanced context parallelism.
+
+The C ABI (include/cpattn.h) is exposed under the same names
+(``cp_partition_index``, ``cp_attn_rank_fwd``, ...); ``rank_fwd`` and
+friends are tensor-level helpers over it. Every step of the computation runs
+in libcpattn.so (hand-written gfx950 kernels); importing this package fails
+if the library has not been built.
+"""
+from ._lib import (  # noqa: F401
+    CP_DTYPE_BF16,
+    CP_DTYPE_F32,
+    CP_EHIP,
+    CP_EINVAL,
+    CP_ENOSPC,
+    CP_EUNSUPPORTED,
+    CP_MAX_CP_SIZE,
+    CP_OK,
+    LIB_PATH,
+    SIGNATURES,
+    CpError,
+    check,
+    cp_attn_rank_fwd,
+    cp_attn_rank_plan_stats,
+    cp_attn_rank_workspace_size,
+    cp_gather_rows,
+    cp_lse_merge,
+    cp_pair_counts,
+    cp_partition_index,
+    cp_status_string,
+    load,
+)
+from .api import (  # noqa: F401
+    RankAttention,
+    gather_rows,
+    lse_merge,
+    pair_counts,
+    partition_index,
+    plan_stats,
+    rank_fwd,
+    workspace_size,
+)
+
+load()

@@ -1,0 +1,173 @@
+"""Tensor-level helpers over the C ABI.
+
+torch supplies device memory and the current stream; every step of the
+computation runs in the HIP library. Inputs must already be GPU tensors:
+there is no CPU path.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Sequence, Tuple
+
+import numpy as np
+
+from . import _lib
+from ._lib import CP_DTYPE_BF16, CP_DTYPE_F32, check
+
+_I32P = ctypes.POINTER(ctypes.c_int32)
+
+
+def _meta(n_img, cu_seqlens):
+    """Host int32 arrays (kept alive by the caller) and their pointers."""
+    cu = None if cu_seqlens is None else np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
+    img = None if n_img is None else np.ascontiguousarray(np.asarray(n_img, dtype=np.int32)).reshape(-1)
+    n_samples = 1 if cu is None else len(cu) - 1
+    cu_p = None if cu is None else cu.ctypes.data_as(_I32P)
+    img_p = None if img is None else img.ctypes.data_as(_I32P)
+    return (cu, img), cu_p, img_p, n_samples
+
+
+def partition_index(seq_len: int, n_img=None, cu_seqlens=None, *, cp_size: int, cp_rank: int
+                    ) -> Tuple[np.ndarray, np.ndarray]:
+    """(index int32[R], cu_rows int32[n_samples+1]) of one CP rank."""
+    keep, cu_p, img_p, n = _meta(n_img, cu_seqlens)
+    rows = ctypes.c_int64(0)
+    check(_lib.cp_partition_index(seq_len, img_p, cu_p, n, cp_size, cp_rank, None, 0,
+                                  ctypes.byref(rows), None), "cp_partition_index")
+    index = np.zeros(rows.value, dtype=np.int32)
+    cu_rows = np.zeros(n + 1, dtype=np.int32)
+    check(_lib.cp_partition_index(seq_len, img_p, cu_p, n, cp_size, cp_rank,
+                                  index.ctypes.data_as(_I32P), rows.value, ctypes.byref(rows),
+                                  cu_rows.ctypes.data_as(_I32P)), "cp_partition_index")
+    return index, cu_rows
+
+
+def pair_counts(seq_len: int, n_img=None, cu_seqlens=None, *, cp_size: int, cp_rank: int
+                ) -> Tuple[int, int]:
+    """(padded, real) unmasked pairs per head on one rank."""
+    keep, cu_p, img_p, n = _meta(n_img, cu_seqlens)
+    padded, real = ctypes.c_int64(0), ctypes.c_int64(0)
+    check(_lib.cp_pair_counts(seq_len, img_p, cu_p, n, cp_size, cp_rank, ctypes.byref(padded),
+                              ctypes.byref(real)), "cp_pair_counts")
+    return padded.value, real.value
+
+
+def workspace_size(seq_len: int, n_img=None, cu_seqlens=None, *, cp_size: int, cp_rank: int,
+                   heads: int, kv_heads: int, head_dim: int, dtype: int) -> int:
+    keep, cu_p, img_p, n = _meta(n_img, cu_seqlens)
+    b = ctypes.c_size_t(0)
+    check(_lib.cp_attn_rank_workspace_size(seq_len, img_p, cu_p, n, cp_size, cp_rank, heads, kv_heads,
+                                           head_dim, dtype, ctypes.byref(b)),
+          "cp_attn_rank_workspace_size")
+    return b.value
+
+
+def plan_stats(seq_len: int, n_img=None, cu_seqlens=None, *, cp_size: int, cp_rank: int,
+               heads: int, kv_heads: int, head_dim: int, dtype: int) -> dict:
+    """Work-list diagnostics of one rank (see cp_attn_rank_plan_stats)."""
+    keep, cu_p, img_p, n = _meta(n_img, cu_seqlens)
+    vals = [ctypes.c_int64(0) for _ in range(4)]
+    steps = np.zeros(cp_size, dtype=np.int64)
+    check(_lib.cp_attn_rank_plan_stats(seq_len, img_p, cu_p, n, cp_size, cp_rank, heads, kv_heads,
+                                       head_dim, dtype, *[ctypes.byref(x) for x in vals],
+                                       steps.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))),
+          "cp_attn_rank_plan_stats")
+    return {"tiles": vals[0].value, "entries": vals[1].value, "kv_tiles": vals[2].value,
+            "covered_pairs": vals[3].value, "step_pairs": steps.tolist()}
+
+
+def _dtype_code(t) -> int:
+    import torch
+
+    if t.dtype == torch.bfloat16:
+        return CP_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return CP_DTYPE_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _stream(t) -> int:
+    import torch
+
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+class RankAttention:
+    """Reusable per-rank forward: plans the sizes once and keeps the output
+    and workspace tensors, so repeated calls (benchmarks) allocate nothing."""
+
+    def __init__(self, q, k, v, *, cp_size: int, cp_rank: int, n_img=None, cu_seqlens=None):
+        import torch
+
+        for name, t in (("q", q), ("k", k), ("v", v)):
+            if not t.is_cuda:
+                raise ValueError(f"{name} must be a GPU tensor (the HIP library has no CPU path)")
+            if not t.is_contiguous():
+                raise ValueError(f"{name} must be contiguous (THD layout)")
+        if not (q.dtype == k.dtype == v.dtype):
+            raise TypeError("q, k, v must share one dtype")
+        self.dtype = _dtype_code(q)
+        T, H, D = q.shape
+        Tk, Hkv, Dk = k.shape
+        if tuple(v.shape) != (Tk, Hkv, Dk) or Tk != T or Dk != D:
+            raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+        self.q, self.k, self.v = q, k, v
+        self.T, self.H, self.Hkv, self.D = int(T), int(H), int(Hkv), int(D)
+        self.cp_size, self.cp_rank = int(cp_size), int(cp_rank)
+        self._keep, self._cu_p, self._img_p, self.n_samples = _meta(n_img, cu_seqlens)
+        rows = ctypes.c_int64(0)
+        check(_lib.cp_partition_index(self.T, self._img_p, self._cu_p, self.n_samples, self.cp_size,
+                                      self.cp_rank, None, 0, ctypes.byref(rows), None),
+              "cp_partition_index")
+        self.R = rows.value
+        self.ws_bytes = workspace_size(self.T, self._keep[1], self._keep[0], cp_size=self.cp_size,
+                                       cp_rank=self.cp_rank, heads=self.H, kv_heads=self.Hkv,
+                                       head_dim=self.D, dtype=self.dtype)
+        dev = q.device
+        self.out = torch.empty((self.R, self.H, self.D), dtype=q.dtype, device=dev)
+        self.lse = torch.empty((self.H, self.R), dtype=torch.float32, device=dev)
+        self.workspace = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=dev)
+
+    def __call__(self):
+        st = _lib.cp_attn_rank_fwd(self.q.data_ptr(), self.k.data_ptr(), self.v.data_ptr(), self.dtype,
+                                   self.T, self._img_p, self._cu_p, self.n_samples, self.cp_size,
+                                   self.cp_rank, self.H, self.Hkv, self.D, self.out.data_ptr(),
+                                   self.lse.data_ptr(), self.workspace.data_ptr(), self.ws_bytes,
+                                   _stream(self.q))
+        check(st, "cp_attn_rank_fwd")
+        return self.out, self.lse
+
+
+def rank_fwd(q, k, v, *, cp_size: int, cp_rank: int, n_img=None, cu_seqlens=None):
+    """Per-rank forward attention. Returns (out [R,H,D] in q.dtype, lse fp32 [H,R])."""
+    return RankAttention(q, k, v, cp_size=cp_size, cp_rank=cp_rank, n_img=n_img,
+                         cu_seqlens=cu_seqlens)()
+
+
+def gather_rows(src, index):
+    """dst[i] = src[index[i]] (0 where index is -1); src a GPU tensor [N, ...]."""
+    import torch
+
+    if not src.is_cuda or not src.is_contiguous():
+        raise ValueError("src must be a contiguous GPU tensor")
+    idx = torch.as_tensor(np.asarray(index, dtype=np.int32)).to(src.device)
+    row_elems = int(np.prod(src.shape[1:])) if src.dim() > 1 else 1
+    dst = torch.empty((len(idx),) + tuple(src.shape[1:]), dtype=src.dtype, device=src.device)
+    check(_lib.cp_gather_rows(src.data_ptr(), _dtype_code(src), src.shape[0], row_elems, idx.data_ptr(),
+                              len(idx), dst.data_ptr(), _stream(src)), "cp_gather_rows")
+    return dst
+
+
+def lse_merge(part_out, part_lse, step_mask, out_dtype):
+    """Merge per-step partials: part_out fp32 [S,R,H,D], part_lse fp32 [S,H,R],
+    step_mask uint32-compatible int [R]. Returns (out [R,H,D], lse [H,R])."""
+    import torch
+
+    S, R, H, D = part_out.shape
+    mask = torch.as_tensor(np.asarray(step_mask, dtype=np.uint32).view(np.int32)).to(part_out.device)
+    out = torch.empty((R, H, D), dtype=out_dtype, device=part_out.device)
+    lse = torch.empty((H, R), dtype=torch.float32, device=part_out.device)
+    check(_lib.cp_lse_merge(part_out.data_ptr(), part_lse.data_ptr(), mask.data_ptr(), S, R, H, D,
+                            _dtype_code(out), out.data_ptr(), lse.data_ptr(), _stream(part_out)),
+          "cp_lse_merge")
+    return out, lse

@@ -1,0 +1,285 @@
+// Per-step blockwise causal attention on bf16 matrix cores (gfx950).
+//
+// Work: one workgroup per (row tile, ring step, head group) entry of the
+// host plan. Ring step s of rank r attends the rank's rows to the keys of
+// source rank j = (r - s) mod P (Ring Attention, Liu et al., ICLR 2024);
+// the context-parallel multimodal page (xuesongtap.github.io/2026/03/22/
+// context-parallel-multimodal, sections 1.1 and 4.1) fixes which rows and
+// keys those are. The plan gives each entry its key spans, already clipped
+// to the keys its rows can see, so a key tile is either fully visible
+// (no mask work) or crosses the causal diagonal / a span end (masked);
+// tiles no row can see were never emitted.
+//
+// Per wave: 32 query rows of one head. Scores are computed transposed,
+// S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: each lane then owns one query
+// row (lane % 32) and 16 keys per 32-key block, so the softmax max and sum
+// are in-lane plus one swap with lane ^ 32. The accumulator layout of S^T is
+// directly the B operand layout of O^T = V^T P^T, so probabilities go from
+// registers to the second MFMA without an LDS round trip. V stays in its
+// natural [key][d] layout in LDS; ds_read_b64_tr_b16 produces the V^T
+// operand. K and V tiles of 64 keys are double-buffered in LDS; the next
+// tile's global loads are in flight while the current tile is computed.
+// Several waves of a workgroup share each K/V tile: 4 rows-blocks of one
+// head (MHA) or one rows-block of 2 or 4 heads that read the same KV head
+// (GQA).
+//
+// Output per entry: O_s normalised by its own softmax sum (fp32) and
+// lse_s = max + ln(sum) (fp32), combined across steps by the LSE merge.
+#include "kernels.h"
+
+namespace cpattn {
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Value of the lane 32 positions away combined with our own: the swap puts
+// lanes 0-31 of one copy next to lanes 32-63 of the other.
+__device__ inline float max_with_partner(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float sum_with_partner(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <int D, int NW, int G>
+__global__ __launch_bounds__(NW * 64) void attn_step_bf16_kernel(AttnArgs a) {
+  constexpr int BN = kBlockN;               // keys per tile
+  constexpr int KS = D + 8;                 // K row stride in LDS (bf16): b128 reads conflict-free
+  constexpr int VS = D + 32;                // V row stride: transposed b64 reads conflict-free
+  constexpr int NT = NW * 64;
+  constexpr int PIECES = BN * D / 8;        // 16-byte pieces per K (or V) tile
+  constexpr int PPT = PIECES / NT;          // pieces per thread
+  constexpr int RPIECES = D / 8;            // pieces per key row
+  constexpr int KBUF = BN * KS, VBUF = BN * VS, STAGE = KBUF + VBUF;
+  constexpr int ND = D / 32;                // 32-wide blocks of head_dim
+  constexpr int NQ = D / 16;                // MFMAs per 32x32 score block
+  static_assert(PIECES % NT == 0, "tile pieces must split evenly over threads");
+  static_assert(NW % G == 0, "waves must cover whole heads");
+  __shared__ __attribute__((aligned(16))) __bf16 smem[2 * STAGE];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int hg = blockIdx.x % a.n_hg;
+  const EntryRec ent = a.entries[blockIdx.x / a.n_hg];
+  const TileRec tile = a.tiles[ent.tile];
+  const int h = hg * G + (wave % G);
+  const int rsub = wave / G;
+  const int kvh = (hg * G) / a.group;
+  const int ql = lane & 31, hh = lane >> 5;
+  const int rin = rsub * 32 + ql;
+  const bool row_ok = rin < tile.nrows;
+  const int lrow = tile.local0 + rin;
+  const int grow = tile.g0 + rin;
+  const int wave_lo = tile.g0 + rsub * 32;                 // first row of this wave
+  const int wave_rows = min(32, tile.nrows - rsub * 32);   // <= 0: wave has no rows
+  const int wave_hi = wave_lo + wave_rows - 1;             // last row of this wave
+
+  // Q as the B operand of S^T = K Q^T: lane holds q[row][16*jj + 8*hh + 0..7].
+  bf16x8 qf[NQ];
+  {
+    const __bf16* qp = static_cast<const __bf16*>(a.qr) + (int64_t(lrow) * a.H + h) * D + 8 * hh;
+#pragma unroll
+    for (int jj = 0; jj < NQ; ++jj) {
+      if (row_ok) {
+        qf[jj] = *reinterpret_cast<const bf16x8*>(qp + 16 * jj);
+      } else {
+        s16x8 z = {0, 0, 0, 0, 0, 0, 0, 0};
+        qf[jj] = __builtin_bit_cast(bf16x8, z);
+      }
+    }
+  }
+
+  const __bf16* kg = static_cast<const __bf16*>(a.k);
+  const __bf16* vg = static_cast<const __bf16*>(a.v);
+  const int64_t tok = int64_t(a.Hkv) * D;  // elements between consecutive tokens
+  uint4 kreg[PPT], vreg[PPT];
+
+  auto load_tile = [&](int kt, int k1) {
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+      const int p = tid + i * NT;
+      const int row = p / RPIECES, col = p % RPIECES;
+      const int key = kt + row;
+      if (key < k1) {
+        const int64_t off = int64_t(key) * tok + int64_t(kvh) * D + col * 8;
+        kreg[i] = *reinterpret_cast<const uint4*>(kg + off);
+        vreg[i] = *reinterpret_cast<const uint4*>(vg + off);
+      } else {  // past the span end: zeros (finite, and masked in the scores)
+        kreg[i] = make_uint4(0, 0, 0, 0);
+        vreg[i] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+    __bf16* ks = smem + buf * STAGE;
+    __bf16* vs = ks + KBUF;
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+      const int p = tid + i * NT;
+      const int row = p / RPIECES, col = p % RPIECES;
+      *reinterpret_cast<uint4*>(ks + row * KS + col * 8) = kreg[i];
+      *reinterpret_cast<uint4*>(vs + row * VS + col * 8) = vreg[i];
+    }
+  };
+
+  f32x16 o[ND];
+#pragma unroll
+  for (int db = 0; db < ND; ++db)
+#pragma unroll
+    for (int t = 0; t < 16; ++t) o[db][t] = 0.f;
+  float m = -INFINITY;  // running max of raw scores for this lane's row
+  float l = 0.f;        // running sum over this lane's keys (other half in lane ^ 32)
+  const float c2 = a.scale_log2;
+
+  auto compute = [&](int buf, int kt, int k1) {
+    const __bf16* ks = smem + buf * STAGE;
+    const __bf16* vs = ks + KBUF;
+    f32x16 s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int t = 0; t < 16; ++t) s[kb][t] = 0.f;
+      const __bf16* kr = ks + (32 * kb + ql) * KS + 8 * hh;
+#pragma unroll
+      for (int jj = 0; jj < NQ; ++jj) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kr + 16 * jj);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[jj], s[kb], 0, 0, 0);
+      }
+    }
+    // lane owns row grow; register t of block kb holds key
+    // kt + 32*kb + 8*(t/4) + 4*hh + t%4
+    if (kt + BN > k1 || kt + BN - 1 > wave_lo) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+          const int key = kt + 32 * kb + 8 * (t >> 2) + 4 * hh + (t & 3);
+          if (key >= k1 || key > grow) s[kb][t] = -INFINITY;
+        }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int t = 0; t < 16; ++t) mx = fmaxf(mx, s[kb][t]);
+    mx = max_with_partner(mx);
+    const float m_new = fmaxf(m, mx);
+    const float ms = (m_new == -INFINITY) ? 0.f : m_new * c2;
+    const float alpha = __builtin_amdgcn_exp2f(m * c2 - ms);
+    bf16x8 pb[2][2];
+    float rs = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][t], c2, -ms));
+        rs += p;
+        pb[kb][t >> 3][t & 7] = (__bf16)p;
+      }
+    l = l * alpha + rs;
+    m = m_new;
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+      for (int t = 0; t < 16; ++t) o[db][t] *= alpha;
+    // O^T += V^T P^T. A operand (V^T): lane holds V[key][32*db + lane%32]
+    // for the 8 keys whose probabilities sit in its B operand; built from
+    // two transposed 4-key reads per MFMA.
+    const int trow = (lane & 15) >> 2;                       // key offset inside a 4-key read
+    const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);  // d offset inside a 32-block
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub) {
+          const int key0 = 32 * kb + 16 * sub + 4 * hh + trow;
+          const __bf16* p0 = vs + key0 * VS + 32 * db + tcol;
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0));
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 8 * VS));
+          const s16x8 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, both),
+                                                          pb[kb][sub], o[db], 0, 0, 0);
+        }
+  };
+
+  int sp = ent.span_begin;
+  SpanRec span = a.spans[sp];
+  int kt = span.k0, k1 = span.k1;
+  load_tile(kt, k1);
+  store_tile(0);
+  __syncthreads();
+  int buf = 0;
+  while (true) {
+    int nkt = kt + BN, nk1 = k1, nsp = sp;
+    if (nkt >= k1) {
+      ++nsp;
+      if (nsp < ent.span_end) {
+        const SpanRec ns = a.spans[nsp];
+        nkt = ns.k0;
+        nk1 = ns.k1;
+      }
+    }
+    const bool has_next = nsp < ent.span_end;
+    if (has_next) load_tile(nkt, nk1);
+    if (wave_rows > 0 && kt <= wave_hi) compute(buf, kt, k1);
+    if (has_next) store_tile(buf ^ 1);
+    __syncthreads();
+    if (!has_next) break;
+    kt = nkt;
+    k1 = nk1;
+    sp = nsp;
+    buf ^= 1;
+  }
+
+  const float lt = sum_with_partner(l);
+  if (!row_ok) return;
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  float* po = a.part_o + ((int64_t(ent.step) * a.R + lrow) * a.H + h) * D + 4 * hh;
+#pragma unroll
+  for (int db = 0; db < ND; ++db)
+#pragma unroll
+    for (int tq = 0; tq < 4; ++tq) {
+      const float4 val = make_float4(o[db][4 * tq] * inv, o[db][4 * tq + 1] * inv,
+                                     o[db][4 * tq + 2] * inv, o[db][4 * tq + 3] * inv);
+      *reinterpret_cast<float4*>(po + 32 * db + 8 * tq) = val;
+    }
+  if (hh == 0)
+    a.part_lse[(int64_t(ent.step) * a.H + h) * a.R + lrow] =
+        lt > 0.f ? m * a.scale + logf(lt) : -INFINITY;
+}
+
+template <int D, int G>
+hipError_t launch_g(const AttnArgs& a, int n_entries, hipStream_t stream) {
+  const int64_t blocks = int64_t(n_entries) * a.n_hg;
+  if (blocks >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((attn_step_bf16_kernel<D, kBf16Waves, G>), dim3(uint32_t(blocks)),
+                     dim3(kBf16Waves * 64), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, int heads_per_wg, int n_entries,
+                            hipStream_t stream) {
+  if (n_entries == 0) return hipSuccess;
+  if (head_dim == 128) {
+    if (heads_per_wg == 4) return launch_g<128, 4>(a, n_entries, stream);
+    if (heads_per_wg == 2) return launch_g<128, 2>(a, n_entries, stream);
+    return launch_g<128, 1>(a, n_entries, stream);
+  }
+  if (head_dim == 64) {
+    if (heads_per_wg == 4) return launch_g<64, 4>(a, n_entries, stream);
+    if (heads_per_wg == 2) return launch_g<64, 2>(a, n_entries, stream);
+    return launch_g<64, 1>(a, n_entries, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace cpattn

@@ -1,0 +1,163 @@
+// Device entry points of the C ABI: the per-rank forward and the gather and
+// merge steps on their own. See include/cpattn.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <exception>
+
+#include "cpattn.h"
+#include "kernels.h"
+#include "workspace.h"
+
+using namespace cpattn;
+
+namespace {
+
+// Pinned host staging for the plan upload, one per host thread. The copy of
+// call n must have left the buffer before call n + 1 rewrites it; an event
+// recorded after the copy guards that. Never freed (process lifetime).
+struct Staging {
+  void* host = nullptr;
+  size_t cap = 0;
+  hipEvent_t copied = nullptr;
+  int device = -1;
+  bool pending = false;
+};
+thread_local Staging t_stage;
+
+hipError_t stage_and_upload(const Workspace& w, void* dst, hipStream_t stream) {
+  Staging& s = t_stage;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (s.pending) {
+    e = hipEventSynchronize(s.copied);
+    if (e != hipSuccess) return e;
+    s.pending = false;
+  }
+  if (s.copied != nullptr && s.device != dev) {
+    hipEventDestroy(s.copied);
+    s.copied = nullptr;
+  }
+  if (s.copied == nullptr) {
+    e = hipEventCreateWithFlags(&s.copied, hipEventDisableTiming);
+    if (e != hipSuccess) return e;
+    s.device = dev;
+  }
+  if (s.cap < w.plan_bytes) {
+    if (s.host) hipHostFree(s.host);
+    s.host = nullptr;
+    s.cap = 0;
+    size_t cap = w.plan_bytes < (size_t(1) << 20) ? (size_t(1) << 20) : w.plan_bytes * 2;
+    e = hipHostMalloc(&s.host, cap, hipHostMallocPortable);
+    if (e != hipSuccess) return e;
+    s.cap = cap;
+  }
+  pack_plan(w, static_cast<uint8_t*>(s.host));
+  e = hipMemcpyAsync(dst, s.host, w.plan_bytes, hipMemcpyHostToDevice, stream);
+  if (e != hipSuccess) return e;
+  e = hipEventRecord(s.copied, stream);
+  if (e != hipSuccess) return e;
+  s.pending = true;
+  return hipSuccess;
+}
+
+inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+cp_status cp_attn_rank_fwd(const void* q, const void* k, const void* v, int32_t dtype,
+                           int64_t seq_len, const int32_t* n_img, const int32_t* cu_seqlens,
+                           int32_t n_samples, int32_t cp_size, int32_t cp_rank, int32_t heads,
+                           int32_t kv_heads, int32_t head_dim, void* out, float* lse,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  try {
+    Workspace w;
+    int32_t st = prepare_workspace(seq_len, n_img, cu_seqlens, n_samples, cp_size, cp_rank, heads,
+                                   kv_heads, head_dim, dtype, w);
+    if (st != CP_OK) return st;
+    const int64_t R = w.meta.rows;
+    if (R == 0) return CP_OK;
+    if (!q || !k || !v || !out || !lse || !workspace) return CP_EINVAL;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
+        !aligned(lse, 4) || !aligned(workspace, 256))
+      return CP_EINVAL;
+    if (workspace_bytes < w.total) return CP_ENOSPC;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    const size_t esize = dtype == CP_DTYPE_BF16 ? 2 : 4;
+
+    if (stage_and_upload(w, ws, s) != hipSuccess) return CP_EHIP;
+    const int32_t* index = reinterpret_cast<const int32_t*>(ws + w.off_index);
+    if (launch_gather(q, index, ws + w.off_qr, R, int64_t(heads) * head_dim * esize, s) != hipSuccess)
+      return CP_EHIP;
+
+    AttnArgs a;
+    a.qr = ws + w.off_qr;
+    a.k = k;
+    a.v = v;
+    a.part_o = reinterpret_cast<float*>(ws + w.off_po);
+    a.part_lse = reinterpret_cast<float*>(ws + w.off_pl);
+    a.tiles = reinterpret_cast<const TileRec*>(ws + w.off_tiles);
+    a.entries = reinterpret_cast<const EntryRec*>(ws + w.off_entries);
+    a.spans = reinterpret_cast<const SpanRec*>(ws + w.off_spans);
+    a.R = int32_t(R);
+    a.H = heads;
+    a.Hkv = kv_heads;
+    a.group = heads / kv_heads;
+    a.n_hg = heads / w.shape.heads_per_wg;
+    a.scale = float(1.0 / std::sqrt(double(head_dim)));
+    a.scale_log2 = float(1.4426950408889634 / std::sqrt(double(head_dim)));
+    const int n_entries = int(w.plan.entries.size());
+    hipError_t e = dtype == CP_DTYPE_BF16
+                       ? launch_attn_bf16(a, head_dim, w.shape.heads_per_wg, n_entries, s)
+                       : launch_attn_f32(a, head_dim, n_entries, s);
+    if (e != hipSuccess) return CP_EHIP;
+
+    const uint32_t* mask = reinterpret_cast<const uint32_t*>(ws + w.off_mask);
+    if (launch_lse_merge(a.part_o, a.part_lse, mask, cp_size, R, heads, head_dim, dtype, out, lse, s) !=
+        hipSuccess)
+      return CP_EHIP;
+    return CP_OK;
+  } catch (const std::exception&) {
+    return CP_EINVAL;
+  }
+}
+
+cp_status cp_gather_rows(const void* src, int32_t dtype, int64_t src_rows, int64_t row_elems,
+                         const int32_t* index, int64_t n_rows, void* dst, void* stream) {
+  if (dtype != CP_DTYPE_F32 && dtype != CP_DTYPE_BF16) return CP_EUNSUPPORTED;
+  if (src_rows < 0 || row_elems < 1 || n_rows < 0) return CP_EINVAL;
+  const size_t esize = dtype == CP_DTYPE_BF16 ? 2 : 4;
+  const int64_t row_bytes = row_elems * int64_t(esize);
+  if (row_bytes % 16 != 0) return CP_EUNSUPPORTED;
+  if (n_rows == 0) return CP_OK;
+  if (!src || !index || !dst || !aligned(src, 16) || !aligned(dst, 16)) return CP_EINVAL;
+  if (uint64_t(row_bytes / 16) * uint64_t(n_rows) >= (uint64_t(1) << 32)) return CP_EUNSUPPORTED;
+  return launch_gather(src, index, dst, n_rows, row_bytes, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? CP_OK
+             : CP_EHIP;
+}
+
+cp_status cp_lse_merge(const float* part_out, const float* part_lse, const uint32_t* step_mask,
+                       int32_t n_steps, int64_t n_rows, int32_t heads, int32_t head_dim,
+                       int32_t dtype, void* out, float* lse, void* stream) {
+  if (dtype != CP_DTYPE_F32 && dtype != CP_DTYPE_BF16) return CP_EUNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128) return CP_EUNSUPPORTED;
+  if (n_steps < 1 || n_rows < 0 || heads < 1) return CP_EINVAL;
+  if (n_steps > CP_MAX_CP_SIZE) return CP_EUNSUPPORTED;
+  if (n_rows >= (int64_t(1) << 31)) return CP_EUNSUPPORTED;
+  if (n_rows == 0) return CP_OK;
+  if (!part_out || !part_lse || !step_mask || !out || !lse || !aligned(part_out, 16) ||
+      !aligned(out, 16))
+    return CP_EINVAL;
+  return launch_lse_merge(part_out, part_lse, step_mask, n_steps, n_rows, heads, head_dim, dtype, out, lse,
+                          static_cast<hipStream_t>(stream)) == hipSuccess
+             ? CP_OK
+             : CP_EHIP;
+}
+
+}  // extern "C"

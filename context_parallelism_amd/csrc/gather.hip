@@ -1,0 +1,54 @@
+// Chunk-index gather: the rank-local query rows, dst[i] = src[index[i]]
+// (zero for pad rows, index -1). This is the index_select of the
+// context-parallel multimodal page, section 1.1, done as one HBM-bound
+// copy with 16-byte accesses: consecutive lanes move consecutive 16-byte
+// pieces of a row, so every wavefront reads and writes whole contiguous
+// runs of a row.
+#include "kernels.h"
+
+namespace cpattn {
+
+namespace {
+
+constexpr int kGatherThreads = 256;
+constexpr int kGatherUnroll = 4;  // 16-byte pieces in flight per thread
+
+__global__ __launch_bounds__(kGatherThreads) void gather_rows_kernel(
+    const uint4* __restrict__ src, const int32_t* __restrict__ index, uint4* __restrict__ dst,
+    uint32_t row_vec, uint32_t total_vec) {
+  const uint32_t base = blockIdx.x * (kGatherThreads * kGatherUnroll) + threadIdx.x;
+  uint4 val[kGatherUnroll];
+  uint32_t pos[kGatherUnroll];
+#pragma unroll
+  for (int u = 0; u < kGatherUnroll; ++u) {
+    pos[u] = base + u * kGatherThreads;
+    val[u] = make_uint4(0, 0, 0, 0);
+    if (pos[u] < total_vec) {
+      const uint32_t row = pos[u] / row_vec;
+      const uint32_t col = pos[u] - row * row_vec;
+      const int32_t g = index[row];
+      if (g >= 0) val[u] = src[uint64_t(g) * row_vec + col];
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kGatherUnroll; ++u)
+    if (pos[u] < total_vec) dst[pos[u]] = val[u];
+}
+
+}  // namespace
+
+hipError_t launch_gather(const void* src, const int32_t* index, void* dst, int64_t n_rows,
+                         int64_t row_bytes, hipStream_t stream) {
+  if (n_rows == 0) return hipSuccess;
+  const uint64_t row_vec = uint64_t(row_bytes) / 16;
+  const uint64_t total = row_vec * uint64_t(n_rows);
+  if (row_bytes % 16 != 0 || total >= (uint64_t(1) << 32)) return hipErrorInvalidValue;
+  const uint64_t per_block = kGatherThreads * kGatherUnroll;
+  const uint32_t blocks = uint32_t((total + per_block - 1) / per_block);
+  hipLaunchKernelGGL(gather_rows_kernel, dim3(blocks), dim3(kGatherThreads), 0, stream,
+                     static_cast<const uint4*>(src), index, static_cast<uint4*>(dst),
+                     uint32_t(row_vec), uint32_t(total));
+  return hipGetLastError();
+}
+
+}  // namespace cpattn

@@ -1,0 +1,40 @@
+// Launch interface of the gfx950 kernels (private to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "plan.h"
+
+namespace cpattn {
+
+struct AttnArgs {
+  const void* qr;        // gathered rank-local Q [R, H, D]
+  const void* k;         // [T, Hkv, D]
+  const void* v;         // [T, Hkv, D]
+  float* part_o;         // [P, R, H, D] fp32, normalised per step
+  float* part_lse;       // [P, H, R] fp32, natural log
+  const TileRec* tiles;
+  const EntryRec* entries;
+  const SpanRec* spans;
+  int32_t R, H, Hkv;
+  int32_t n_hg;          // head groups (workgroups per entry)
+  int32_t group;         // heads / kv_heads
+  float scale_log2;      // log2(e) / sqrt(D)
+  float scale;           // 1 / sqrt(D)
+};
+
+hipError_t launch_gather(const void* src, const int32_t* index, void* dst, int64_t n_rows,
+                         int64_t row_bytes, hipStream_t stream);
+
+hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, int heads_per_wg, int n_entries,
+                            hipStream_t stream);
+
+hipError_t launch_attn_f32(const AttnArgs& a, int head_dim, int n_entries, hipStream_t stream);
+
+hipError_t launch_lse_merge(const float* part_o, const float* part_lse, const uint32_t* mask,
+                            int32_t n_steps, int64_t n_rows, int32_t heads, int32_t head_dim, int32_t dtype,
+                            void* out, float* lse, hipStream_t stream);
+
+}  // namespace cpattn

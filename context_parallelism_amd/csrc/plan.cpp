@@ -1,0 +1,188 @@
+// Host planning: see plan.h. Partition and pair counts follow the
+// context-parallel multimodal page (xuesongtap.github.io/2026/03/22/
+// context-parallel-multimodal): section 1.1 (2P chunks, rank r keeps
+// chunks r and 2P-1-r), section 4.1 (image prefix kept whole, only text
+// split), section 5.3 (packed samples split one by one via cu_seqlens).
+#include "plan.h"
+
+#include <algorithm>
+
+#include "cpattn.h"
+
+namespace cpattn {
+
+TileShape tile_shape(int32_t dtype, int32_t group) {
+  if (dtype != CP_DTYPE_BF16) return {kF32RowsPerTile, 1};
+  const int32_t hpw = (group % 4 == 0) ? 4 : (group % 2 == 0) ? 2 : 1;
+  return {32 * kBf16Waves / hpw, hpw};
+}
+
+int32_t build_meta(int64_t seq_len, const int32_t* n_img, const int32_t* cu_seqlens,
+                   int32_t n_samples, int32_t cp_size, int32_t cp_rank, Meta& m) {
+  if (cp_size < 1) return CP_EINVAL;
+  if (cp_size > CP_MAX_CP_SIZE) return CP_EUNSUPPORTED;
+  if (cp_rank < 0 || cp_rank >= cp_size) return CP_EINVAL;
+  if (seq_len < 0 || n_samples < 0) return CP_EINVAL;
+  if (seq_len >= (int64_t(1) << 31)) return CP_EUNSUPPORTED;
+  if (cu_seqlens == nullptr) {
+    if (n_samples != 1 || seq_len < 1) return CP_EINVAL;
+  } else {
+    if (cu_seqlens[0] != 0) return CP_EINVAL;
+    for (int32_t s = 0; s < n_samples; ++s)
+      if (cu_seqlens[s + 1] <= cu_seqlens[s]) return CP_EINVAL;
+    if (int64_t(cu_seqlens[n_samples]) != seq_len) return CP_EINVAL;
+  }
+  m = Meta();
+  m.seq_len = seq_len;
+  m.P = cp_size;
+  m.r = cp_rank;
+  m.samples.resize(n_samples);
+  int64_t local = 0;
+  for (int32_t s = 0; s < n_samples; ++s) {
+    int64_t a = cu_seqlens ? cu_seqlens[s] : 0;
+    int64_t b = cu_seqlens ? cu_seqlens[s + 1] : seq_len;
+    int64_t n = n_img ? n_img[s] : 0;
+    if (n < 0 || n > b - a) return CP_EINVAL;
+    SampleGeom& g = m.samples[s];
+    g.a = a;
+    g.n_img = int32_t(n);
+    g.text = int32_t(b - a - n);
+    g.c = int32_t((int64_t(g.text) + 2 * cp_size - 1) / (2 * cp_size));
+    g.local0 = local;
+    local += n + 2 * int64_t(g.c);
+  }
+  if (local >= (int64_t(1) << 31)) return CP_EUNSUPPORTED;
+  m.rows = local;
+  return CP_OK;
+}
+
+namespace {
+// Real tokens of text chunk k of a sample: offsets [k*c, min((k+1)*c, T)).
+inline int32_t chunk_real(const SampleGeom& g, int32_t k) {
+  int64_t lo = int64_t(k) * g.c;
+  int64_t hi = std::min<int64_t>(lo + g.c, g.text);
+  return hi > lo ? int32_t(hi - lo) : 0;
+}
+// Sum of (n_img + t + 1) for t in [lo, lo + cnt): pairs of cnt text rows.
+inline int64_t text_pairs(const SampleGeom& g, int64_t lo, int64_t cnt) {
+  return cnt * (int64_t(g.n_img) + 1 + lo) + cnt * (cnt - 1) / 2;
+}
+}  // namespace
+
+void fill_index(const Meta& m, int32_t* index, int32_t* cu_rows_local) {
+  const int32_t P = m.P, r = m.r;
+  for (size_t s = 0; s < m.samples.size(); ++s) {
+    const SampleGeom& g = m.samples[s];
+    if (cu_rows_local) cu_rows_local[s] = int32_t(g.local0);
+    if (!index) continue;
+    int32_t* out = index + g.local0;
+    for (int32_t i = 0; i < g.n_img; ++i) *out++ = int32_t(g.a + i);
+    const int32_t ks[2] = {r, 2 * P - 1 - r};
+    for (int32_t k : ks) {
+      for (int32_t u = 0; u < g.c; ++u) {
+        int64_t t = int64_t(k) * g.c + u;
+        *out++ = t < g.text ? int32_t(g.a + g.n_img + t) : -1;
+      }
+    }
+  }
+  if (cu_rows_local) cu_rows_local[m.samples.size()] = int32_t(m.rows);
+}
+
+void pair_counts(const Meta& m, int64_t* padded, int64_t* real) {
+  const int32_t P = m.P, r = m.r;
+  int64_t pp = 0, rr = 0;
+  for (const SampleGeom& g : m.samples) {
+    int64_t img = int64_t(g.n_img) * (g.n_img + 1) / 2;  // image row i sees i + 1 keys
+    pp += img;
+    rr += img;
+    const int32_t ks[2] = {r, 2 * P - 1 - r};
+    for (int32_t k : ks) {
+      int64_t lo = int64_t(k) * g.c;
+      pp += text_pairs(g, lo, g.c);
+      rr += text_pairs(g, lo, chunk_real(g, k));
+    }
+  }
+  if (padded) *padded = pp;
+  if (real) *real = rr;
+}
+
+std::vector<Segment> segments(const Meta& m) {
+  std::vector<Segment> out;
+  const int32_t P = m.P, r = m.r;
+  for (size_t s = 0; s < m.samples.size(); ++s) {
+    const SampleGeom& g = m.samples[s];
+    if (g.n_img > 0) out.push_back({g.local0, g.a, g.n_img, int32_t(s), 0});
+    const int32_t ks[2] = {r, 2 * P - 1 - r};
+    for (int kind = 1; kind <= 2; ++kind) {
+      int32_t k = ks[kind - 1];
+      int32_t len = chunk_real(g, k);
+      if (len == 0) continue;
+      int64_t local0 = g.local0 + g.n_img + int64_t(kind - 1) * g.c;
+      out.push_back({local0, g.a + g.n_img + int64_t(k) * g.c, len, int32_t(s), kind});
+    }
+  }
+  return out;
+}
+
+void step_ranges(const Meta& m, int32_t sample, int32_t step, std::vector<SpanRec>& out) {
+  const SampleGeom& g = m.samples[sample];
+  const int32_t P = m.P;
+  const int32_t j = ((m.r - step) % P + P) % P;  // source rank of this ring step
+  if (step == 0 && g.n_img > 0) out.push_back({int32_t(g.a), int32_t(g.a + g.n_img)});
+  const int32_t ks[2] = {j, 2 * P - 1 - j};
+  for (int32_t k : ks) {
+    int32_t len = chunk_real(g, k);
+    if (len == 0) continue;
+    int64_t k0 = g.a + g.n_img + int64_t(k) * g.c;
+    out.push_back({int32_t(k0), int32_t(k0 + len)});
+  }
+}
+
+void build_plan(const Meta& m, int32_t bm, int32_t bn, Plan& p) {
+  p = Plan();
+  p.bm = bm;
+  p.bn = bn;
+  p.index.resize(size_t(m.rows));
+  p.row_mask.assign(size_t(m.rows), 0u);
+  if (m.rows > 0) fill_index(m, p.index.data(), nullptr);
+  struct Pending { EntryRec e; int64_t cost; };
+  std::vector<Pending> pend;
+  std::vector<SpanRec> ranges;
+  for (const Segment& seg : segments(m)) {
+    for (int32_t off = 0; off < seg.len; off += bm) {
+      TileRec t;
+      t.local0 = int32_t(seg.local0 + off);
+      t.nrows = std::min(bm, seg.len - off);
+      t.g0 = int32_t(seg.g0 + off);
+      t.pad = 0;
+      const int32_t tile_id = int32_t(p.tiles.size());
+      p.tiles.push_back(t);
+      const int32_t g_hi = t.g0 + t.nrows;  // keys >= g_hi are seen by no row of the tile
+      uint32_t mask = 0;
+      for (int32_t s = 0; s < m.P; ++s) {
+        ranges.clear();
+        step_ranges(m, seg.sample, s, ranges);
+        EntryRec e{tile_id, s, int32_t(p.spans.size()), 0};
+        int64_t cost = 0;
+        for (const SpanRec& rg : ranges) {
+          int32_t k1 = std::min(rg.k1, g_hi);
+          if (k1 <= rg.k0) continue;
+          p.spans.push_back({rg.k0, k1});
+          cost += (int64_t(k1) - rg.k0 + bn - 1) / bn;
+        }
+        e.span_end = int32_t(p.spans.size());
+        if (e.span_end == e.span_begin) continue;
+        mask |= 1u << s;
+        pend.push_back({e, cost});
+        p.kv_tiles += cost;
+      }
+      for (int32_t i = 0; i < t.nrows; ++i) p.row_mask[size_t(t.local0 + i)] = mask;
+    }
+  }
+  std::stable_sort(pend.begin(), pend.end(),
+                   [](const Pending& x, const Pending& y) { return x.cost > y.cost; });
+  p.entries.reserve(pend.size());
+  for (const Pending& q : pend) p.entries.push_back(q.e);
+}
+
+}  // namespace cpattn

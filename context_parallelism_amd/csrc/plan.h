@@ -1,0 +1,88 @@
+// Host-side planning for per-rank context-parallel attention: argument
+// checks, the rank partition, exact pair counts and the per-step work list
+// the attention kernel walks. Integer only; no HIP calls.
+#pragma once
+
+#include <cstdint>
+#include <vector>
+
+namespace cpattn {
+
+// One packed sample as seen by one rank.
+struct SampleGeom {
+  int64_t a;        // global id of the sample's first token
+  int32_t n_img;    // image-prefix length
+  int32_t text;     // real text length T
+  int32_t c;        // chunk length ceil(T / 2P)
+  int64_t local0;   // first rank-local row of the sample
+};
+
+// A run of consecutive rank-local rows whose global ids are consecutive
+// real tokens of one sample: the image prefix, or the real part of one of
+// the rank's two text chunks.
+struct Segment {
+  int64_t local0;   // first rank-local row
+  int64_t g0;       // global id of that row
+  int32_t len;      // rows
+  int32_t sample;
+  int32_t kind;     // 0 image, 1 chunk r, 2 chunk 2P-1-r
+};
+
+// Tile shapes of the attention kernels. Each bf16 wave owns 32 query rows
+// of one head and a bf16 workgroup has kBf16Waves waves; K/V stream through
+// LDS kBlockN keys at a time.
+constexpr int kBlockN = 64;
+constexpr int kBf16Waves = 4;
+constexpr int kF32RowsPerTile = 64;
+
+struct TileShape {
+  int32_t rows;          // rows per plan tile (bm)
+  int32_t heads_per_wg;  // query heads sharing one KV head in a workgroup
+};
+
+// bf16 (dtype 1): heads_per_wg = largest of 4, 2, 1 dividing heads/kv_heads,
+// rows = 32 * kBf16Waves / heads_per_wg. fp32: one head, kF32RowsPerTile.
+TileShape tile_shape(int32_t dtype, int32_t group);
+
+struct Meta {
+  int64_t seq_len = 0;
+  int32_t P = 1, r = 0;
+  std::vector<SampleGeom> samples;
+  int64_t rows = 0;  // R
+};
+
+// Checks (seq_len, n_img, cu_seqlens, n_samples, cp_size, cp_rank) and fills
+// `m`. Returns a cp_status value.
+int32_t build_meta(int64_t seq_len, const int32_t* n_img, const int32_t* cu_seqlens,
+                   int32_t n_samples, int32_t cp_size, int32_t cp_rank, Meta& m);
+
+void fill_index(const Meta& m, int32_t* index, int32_t* cu_rows_local);
+void pair_counts(const Meta& m, int64_t* padded, int64_t* real);
+std::vector<Segment> segments(const Meta& m);
+
+// Device-side plan records (plain int32 so the same bytes serve host and GPU).
+struct TileRec { int32_t local0, nrows, g0, pad; };          // a row tile
+struct EntryRec { int32_t tile, step, span_begin, span_end; };  // (tile, step) work
+struct SpanRec { int32_t k0, k1; };                          // global keys [k0, k1)
+
+struct Plan {
+  int32_t bm = 0, bn = 0;
+  std::vector<TileRec> tiles;
+  std::vector<EntryRec> entries;  // launch order: longest first
+  std::vector<SpanRec> spans;
+  std::vector<uint32_t> row_mask;  // per rank-local row: steps with a partial
+  std::vector<int32_t> index;      // per rank-local row: global id or -1
+  int64_t kv_tiles = 0;            // sum over entries of key tiles (one head group)
+};
+
+// Key ranges of ring step s for a rank (source rank j = (r - s) mod P):
+// at s = 0 the sample's image prefix and the rank's own two chunks, at
+// s > 0 chunks j and 2P-1-j; each clipped to real tokens. Appends to out.
+void step_ranges(const Meta& m, int32_t sample, int32_t step, std::vector<SpanRec>& out);
+
+// Row tiles of `bm` rows cut per segment; for each tile and step the key
+// spans it can see (clipped to the tile's last row), entries sorted by
+// descending key-tile count (`bn` keys per tile).
+void build_plan(const Meta& m, int32_t bm, int32_t bn, Plan& p);
+
+}  // namespace cpattn

@@ -1,0 +1,63 @@
+#include "workspace.h"
+
+#include <cstring>
+
+#include "cpattn.h"
+
+namespace cpattn {
+
+namespace {
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+}  // namespace
+
+int32_t prepare_workspace(int64_t seq_len, const int32_t* n_img, const int32_t* cu_seqlens,
+                          int32_t n_samples, int32_t cp_size, int32_t cp_rank, int32_t heads,
+                          int32_t kv_heads, int32_t head_dim, int32_t dtype, Workspace& w) {
+  if (dtype != CP_DTYPE_F32 && dtype != CP_DTYPE_BF16) return CP_EUNSUPPORTED;
+  if (heads < 1 || kv_heads < 1 || heads % kv_heads != 0) return CP_EINVAL;
+  if (head_dim != 64 && head_dim != 128) return CP_EUNSUPPORTED;
+  int32_t st = build_meta(seq_len, n_img, cu_seqlens, n_samples, cp_size, cp_rank, w.meta);
+  if (st != CP_OK) return st;
+  w.heads = heads;
+  w.kv_heads = kv_heads;
+  w.head_dim = head_dim;
+  w.dtype = dtype;
+  w.shape = tile_shape(dtype, heads / kv_heads);
+  build_plan(w.meta, w.shape.rows, kBlockN, w.plan);
+  const size_t R = size_t(w.meta.rows);
+  const size_t esize = dtype == CP_DTYPE_BF16 ? 2 : 4;
+  size_t off = 0;
+  w.off_index = off;
+  off = align256(off + R * sizeof(int32_t));
+  w.off_mask = off;
+  off = align256(off + R * sizeof(uint32_t));
+  w.off_tiles = off;
+  off = align256(off + w.plan.tiles.size() * sizeof(TileRec));
+  w.off_entries = off;
+  off = align256(off + w.plan.entries.size() * sizeof(EntryRec));
+  w.off_spans = off;
+  off = align256(off + w.plan.spans.size() * sizeof(SpanRec));
+  w.plan_bytes = off;
+  w.off_qr = off;
+  off = align256(off + R * size_t(heads) * head_dim * esize);
+  w.off_po = off;
+  off = align256(off + size_t(cp_size) * R * size_t(heads) * head_dim * sizeof(float));
+  w.off_pl = off;
+  off = align256(off + size_t(cp_size) * size_t(heads) * R * sizeof(float));
+  w.total = off;
+  return CP_OK;
+}
+
+void pack_plan(const Workspace& w, uint8_t* dst) {
+  std::memset(dst, 0, w.plan_bytes);
+  const Plan& p = w.plan;
+  if (!p.index.empty()) std::memcpy(dst + w.off_index, p.index.data(), p.index.size() * sizeof(int32_t));
+  if (!p.row_mask.empty())
+    std::memcpy(dst + w.off_mask, p.row_mask.data(), p.row_mask.size() * sizeof(uint32_t));
+  if (!p.tiles.empty()) std::memcpy(dst + w.off_tiles, p.tiles.data(), p.tiles.size() * sizeof(TileRec));
+  if (!p.entries.empty())
+    std::memcpy(dst + w.off_entries, p.entries.data(), p.entries.size() * sizeof(EntryRec));
+  if (!p.spans.empty()) std::memcpy(dst + w.off_spans, p.spans.data(), p.spans.size() * sizeof(SpanRec));
+}
+
+}  // namespace cpattn

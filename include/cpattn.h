@@ -1,0 +1,194 @@
+/*
+ * cpattn.h -- C ABI of the per-rank attention of load-balanced context
+ * parallelism, for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed. The context-parallel multimodal page
+ * (xuesongtap.github.io/2026/03/22/context-parallel-multimodal) describes
+ * how a CP group of size P shares one long causal sequence:
+ *   - section 1.1: the sequence is cut into 2P chunks and rank r keeps
+ *     chunks r and 2P-1-r (head-tail pairing), so every rank gets the same
+ *     causal work;
+ *   - sections 2 and 4.1: an image-token prefix is never split; every rank
+ *     keeps all of it and only the text is cut into chunks;
+ *   - section 5.3: packed samples are delimited by cu_seqlens and are
+ *     balanced sample by sample.
+ * Each rank then attends its rows causally to the key/value blocks of all
+ * P ring steps and combines the per-step partial results by their
+ * log-sum-exp (Ring Attention, Liu et al., ICLR 2024, the page's [2]).
+ * On one GPU every step's K/V block is read in place from HBM.
+ *
+ * Conventions shared by every entry point.
+ *   - Layout "THD": q is [seq_len, heads, head_dim]; k and v are
+ *     [seq_len, kv_heads, head_dim]; all contiguous, head_dim fastest.
+ *   - Rank-local rows: for each sample in cu_seqlens order, the image rows
+ *     (whole prefix), then text chunk r, then text chunk 2P-1-r. A sample's
+ *     text of length T is padded at its end to 2P*c rows, c = ceil(T/2P);
+ *     pad rows carry index -1, output 0 and lse -inf.
+ *   - Mask: causal with an inclusive diagonal over [image, text] inside a
+ *     sample; samples never see each other. Scale 1/sqrt(head_dim); query
+ *     head h reads KV head h / (heads / kv_heads).
+ *   - cu_seqlens: int32[n_samples + 1], 0 = cu[0] < cu[1] < ... <
+ *     cu[n_samples] = seq_len, over real tokens. NULL means one sample
+ *     [0, seq_len) and requires n_samples == 1.
+ *   - n_img: int32[n_samples], image-prefix length of each sample,
+ *     0 <= n_img[s] <= cu[s+1] - cu[s]. NULL means no image prefix.
+ *   - Host pointers are read during the call only; the library keeps no
+ *     pointer and holds no global mutable state (calls on different
+ *     streams may run concurrently).
+ *   - Errors: every argument is checked before anything is written or
+ *     launched; on error nothing is written and a negative status is
+ *     returned. No C++ exception crosses this boundary.
+ */
+#ifndef CPATTN_H
+#define CPATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t cp_status;
+
+enum {
+  CP_OK = 0,
+  CP_EINVAL = -1,       /* malformed argument (sizes, ranks, cu_seqlens, NULL) */
+  CP_ENOSPC = -2,       /* caller buffer (index capacity, workspace) too small */
+  CP_EUNSUPPORTED = -3, /* valid but not supported (dtype, head_dim, sizes)   */
+  CP_EHIP = -4          /* a HIP runtime call failed                          */
+};
+
+enum { CP_DTYPE_F32 = 0, CP_DTYPE_BF16 = 1 };
+
+/* Largest cp_size accepted (per-row step masks are 32-bit). */
+#define CP_MAX_CP_SIZE 32
+
+/*
+ * cp_partition_index -- rows of one CP rank (host only, integer, exact).
+ *
+ * Page section 1.1 (chunks [cp_rank, 2*cp_size-cp_rank-1]), section 4.1
+ * (image prefix kept whole), section 5.3 (per-sample split).
+ *
+ * index: host int32[capacity]; receives the global token id of every
+ *   rank-local row (-1 for pad rows). May be NULL to query the row count.
+ * n_rows: host, receives the number of rank-local rows R.
+ * cu_rows_local: host int32[n_samples + 1] or NULL; receives the sample
+ *   boundaries in rank-local row order.
+ * Returns CP_ENOSPC (writing nothing) if index != NULL and capacity < R.
+ */
+cp_status cp_partition_index(int64_t seq_len, const int32_t *n_img, const int32_t *cu_seqlens,
+                             int32_t n_samples, int32_t cp_size, int32_t cp_rank,
+                             int32_t *index, int64_t capacity, int64_t *n_rows,
+                             int32_t *cu_rows_local);
+
+/*
+ * cp_pair_counts -- unmasked (query, key) pairs per head on one rank
+ * (host only, exact). A row at position p of its sample sees p + 1 keys.
+ * pairs_real sums over real rows; pairs_padded also counts every pad row
+ * as a token at its padded text offset, which head-tail pairing equalises
+ * across ranks exactly (page section 1.1). Either output may be NULL.
+ */
+cp_status cp_pair_counts(int64_t seq_len, const int32_t *n_img, const int32_t *cu_seqlens,
+                         int32_t n_samples, int32_t cp_size, int32_t cp_rank,
+                         int64_t *pairs_padded, int64_t *pairs_real);
+
+/*
+ * cp_attn_rank_workspace_size -- bytes of device workspace that
+ * cp_attn_rank_fwd needs for these arguments (host only). The workspace
+ * holds the uploaded plan, the gathered rank-local Q rows, and the per-step
+ * partial outputs (fp32) and log-sum-exps.
+ */
+cp_status cp_attn_rank_workspace_size(int64_t seq_len, const int32_t *n_img,
+                                      const int32_t *cu_seqlens, int32_t n_samples,
+                                      int32_t cp_size, int32_t cp_rank, int32_t heads,
+                                      int32_t kv_heads, int32_t head_dim, int32_t dtype,
+                                      size_t *bytes);
+
+/*
+ * cp_attn_rank_plan_stats -- diagnostics of the work list cp_attn_rank_fwd
+ * builds for these arguments (host only, integer, exact).
+ *
+ * n_tiles: row tiles; n_entries: (row tile, ring step) work entries;
+ * kv_tiles: key tiles walked per head group, summed over entries;
+ * covered_pairs: (query, key) pairs per head that the entries' key spans
+ *   expose under the causal mask -- equal to pairs_real of cp_pair_counts
+ *   when every visible pair is scheduled exactly once;
+ * step_pairs: host int64[cp_size] or NULL; the same count split by ring
+ *   step (step s reads the keys of source rank (cp_rank - s) mod cp_size).
+ * Any output may be NULL.
+ */
+cp_status cp_attn_rank_plan_stats(int64_t seq_len, const int32_t *n_img, const int32_t *cu_seqlens,
+                                  int32_t n_samples, int32_t cp_size, int32_t cp_rank,
+                                  int32_t heads, int32_t kv_heads, int32_t head_dim, int32_t dtype,
+                                  int64_t *n_tiles, int64_t *n_entries, int64_t *kv_tiles,
+                                  int64_t *covered_pairs, int64_t *step_pairs);
+
+/*
+ * cp_attn_rank_fwd -- forward attention of one CP rank's rows.
+ *
+ * Steps, all enqueued on `stream` (no host synchronisation):
+ *   1. plan on the host (partition, per-step key spans, work list) and
+ *      upload it into the workspace;
+ *   2. gather the rank's query rows from q (page section 1.1, index_select);
+ *   3. for every ring step s = 0..P-1 (source rank j = (r - s) mod P; the
+ *      image prefix and the rank's own chunks at s = 0, chunks j and
+ *      2P-1-j at s > 0), blockwise causal attention of the rank's rows to
+ *      that step's keys, writing per-step partial outputs and lse;
+ *   4. merge the partials of each row by their log-sum-exp.
+ *
+ * q, k, v: device, dtype CP_DTYPE_BF16 or CP_DTYPE_F32, THD layout.
+ * out: device [R, heads, head_dim] in dtype; lse: device fp32 [heads, R],
+ *   natural log. R is the row count from cp_partition_index.
+ * workspace: device, at least cp_attn_rank_workspace_size bytes, 256-byte
+ *   aligned; its contents on entry are ignored.
+ * stream: a hipStream_t (NULL = the null stream).
+ * head_dim must be 64 or 128; heads % kv_heads == 0; cp_size <= 32;
+ * seq_len < 2^31. Results are deterministic: no floating-point atomics,
+ * fixed merge order.
+ */
+cp_status cp_attn_rank_fwd(const void *q, const void *k, const void *v, int32_t dtype,
+                           int64_t seq_len, const int32_t *n_img, const int32_t *cu_seqlens,
+                           int32_t n_samples, int32_t cp_size, int32_t cp_rank, int32_t heads,
+                           int32_t kv_heads, int32_t head_dim, void *out, float *lse,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * cp_gather_rows -- the chunk-index gather alone (page section 1.1,
+ * index_select on the sequence dimension): dst[i, :] = src[index[i], :]
+ * for index[i] >= 0 and 0 for index[i] == -1.
+ *
+ * src: device [src_rows, row_elems]; dst: device [n_rows, row_elems];
+ * index: device int32[n_rows], each -1 or in [0, src_rows) (not checked on
+ * the device: the caller guarantees it). row_elems * element size must be
+ * a multiple of 16 bytes; src, dst 16-byte aligned.
+ */
+cp_status cp_gather_rows(const void *src, int32_t dtype, int64_t src_rows, int64_t row_elems,
+                         const int32_t *index, int64_t n_rows, void *dst, void *stream);
+
+/*
+ * cp_lse_merge -- the log-sum-exp merge alone (Ring Attention's combination
+ * of blockwise partial results).
+ *
+ * part_out: device fp32 [n_steps, n_rows, heads, head_dim], each partial
+ *   already normalised by its own softmax sum; part_lse: device fp32
+ *   [n_steps, heads, n_rows]; step_mask: device uint32[n_rows], bit s set
+ *   when row has a partial from step s (other steps are not read).
+ * For each (row, head): m = max_s lse_s, w_s = exp(lse_s - m),
+ *   out = sum_s w_s * part_s / sum_s w_s, lse = m + ln(sum_s w_s);
+ *   steps are taken in increasing s. A row with mask 0 gets out 0, lse -inf.
+ * out: device [n_rows, heads, head_dim] in dtype; lse: device fp32
+ *   [heads, n_rows]. n_steps <= 32, head_dim 64 or 128.
+ */
+cp_status cp_lse_merge(const float *part_out, const float *part_lse, const uint32_t *step_mask,
+                       int32_t n_steps, int64_t n_rows, int32_t heads, int32_t head_dim,
+                       int32_t dtype, void *out, float *lse, void *stream);
+
+/* Static English text for a status code. */
+const char *cp_status_string(cp_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CPATTN_H */

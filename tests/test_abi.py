@@ -1,0 +1,227 @@
+"""CPU tests of the C ABI: the library loads and exports every declared
+entry point; the host planner matches the oracle bit-exactly; every
+argument error returns its status and writes nothing. No GPU calls."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "cpattn.h")
+
+
+@pytest.fixture(scope="module")
+def cp():
+    import context_parallelism_amd as m
+    return m
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(cp_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_exports_every_declared_symbol(cp):
+    names = declared_functions()
+    assert "cp_attn_rank_fwd" in names and "cp_partition_index" in names
+    lib = ctypes.CDLL(cp.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    bound = {s[0] for s in cp.SIGNATURES}
+    assert set(names) == bound
+
+
+def test_status_strings(cp):
+    for code in (cp.CP_OK, cp.CP_EINVAL, cp.CP_ENOSPC, cp.CP_EUNSUPPORTED, cp.CP_EHIP):
+        assert cp.cp_status_string(code) != "unknown status"
+    assert cp.cp_status_string(12345) == "unknown status"
+
+
+def test_partition_matches_oracle_on_workloads(cp):
+    for w in workloads.WORKLOADS.values():
+        cu = w.cu_seqlens
+        for r in range(w.cp_size):
+            a, acu = cp.partition_index(w.seq_len, w.n_img, cu, cp_size=w.cp_size, cp_rank=r)
+            b, bcu = oracle.partition_index(w.seq_len, w.n_img, cu, w.cp_size, r)
+            assert np.array_equal(a, b) and np.array_equal(acu, bcu)
+            assert cp.pair_counts(w.seq_len, w.n_img, cu, cp_size=w.cp_size, cp_rank=r) == \
+                oracle.pair_counts(w.seq_len, w.n_img, cu, w.cp_size, r)
+
+
+def test_partition_matches_oracle_random(cp):
+    rng = np.random.default_rng(1)
+    for trial in range(300):
+        n = int(rng.integers(1, 6))
+        n_img, cu = workloads.random_meta(rng, n, 40, 200)
+        T = int(cu[-1])
+        P = int(rng.integers(1, 9))
+        r = int(rng.integers(0, P))
+        a, acu = cp.partition_index(T, n_img, cu, cp_size=P, cp_rank=r)
+        b, bcu = oracle.partition_index(T, n_img, cu, P, r)
+        assert np.array_equal(a, b) and np.array_equal(acu, bcu), (trial, n_img, cu, P, r)
+        assert cp.pair_counts(T, n_img, cu, cp_size=P, cp_rank=r) == oracle.pair_counts(T, n_img, cu, P, r)
+
+
+def test_single_sample_null_meta(cp):
+    a, _ = cp.partition_index(1000, cp_size=3, cp_rank=2)
+    b, _ = oracle.partition_index(1000, None, None, 3, 2)
+    assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("dtype", [0, 1])
+def test_schedule_covers_every_visible_pair_once(cp, dtype):
+    # the work list's spans expose exactly the rank's visible pairs, and by
+    # ring step: step 0 holds 2c^2 + c (+ image terms), every other step 2c^2
+    rng = np.random.default_rng(2)
+    for trial in range(60):
+        n = int(rng.integers(1, 4))
+        n_img, cu = workloads.random_meta(rng, n, 70, 400)
+        T = int(cu[-1])
+        P = int(rng.integers(1, 7))
+        r = int(rng.integers(0, P))
+        H, Hkv = [(4, 4), (8, 2), (8, 4), (6, 3)][trial % 4]
+        st = cp.plan_stats(T, n_img, cu, cp_size=P, cp_rank=r, heads=H, kv_heads=Hkv,
+                           head_dim=128, dtype=dtype)
+        assert st["covered_pairs"] == oracle.pair_counts(T, n_img, cu, P, r)[1]
+        assert sum(st["step_pairs"]) == st["covered_pairs"]
+    for w in workloads.WORKLOADS.values():
+        if w.n_samples != 1 or any(w.n_img):
+            continue
+        c = w.seq_len // (2 * w.cp_size)
+        for r in range(w.cp_size):
+            st = cp.plan_stats(w.seq_len, cp_size=w.cp_size, cp_rank=r, heads=w.heads,
+                               kv_heads=w.kv_heads, head_dim=w.head_dim, dtype=dtype)
+            assert st["step_pairs"] == [2 * c * c + c] + [2 * c * c] * (w.cp_size - 1)
+    w = workloads.get(3)
+    n, c = w.n_img[0], w.text_len[0] // (2 * w.cp_size)
+    st = cp.plan_stats(w.seq_len, w.n_img, None, cp_size=w.cp_size, cp_rank=w.rank, heads=w.heads,
+                       kv_heads=w.kv_heads, head_dim=w.head_dim, dtype=1)
+    assert st["step_pairs"][0] == 2 * c * c + c + n * (n + 1) // 2 + 2 * c * n
+    assert st["step_pairs"][1:] == [2 * c * c] * (w.cp_size - 1)
+
+
+def test_workspace_size_grows_with_problem(cp):
+    a = cp.workspace_size(1000, cp_size=2, cp_rank=0, heads=4, kv_heads=4, head_dim=128, dtype=1)
+    b = cp.workspace_size(2000, cp_size=2, cp_rank=0, heads=4, kv_heads=4, head_dim=128, dtype=1)
+    c = cp.workspace_size(1000, cp_size=2, cp_rank=0, heads=4, kv_heads=4, head_dim=128, dtype=0)
+    assert 0 < a < b and a < c and a % 256 == 0
+
+
+# ------------------------------------------------------------------ errors
+
+I32 = ctypes.POINTER(ctypes.c_int32)
+
+
+def arr(x):
+    a = np.ascontiguousarray(np.asarray(x, dtype=np.int32))
+    return a, a.ctypes.data_as(I32)
+
+
+def part(cp, seq_len, n_img, cu, n, P, r, cap=64):
+    """Call cp_partition_index into a canary-filled buffer; returns (status, untouched)."""
+    buf = np.full(cap, 7777, np.int32)
+    rows = ctypes.c_int64(-5)
+    img_a = None if n_img is None else arr(n_img)
+    cu_a = None if cu is None else arr(cu)
+    st = cp.cp_partition_index(seq_len, None if img_a is None else img_a[1],
+                               None if cu_a is None else cu_a[1], n, P, r,
+                               buf.ctypes.data_as(I32), cap, ctypes.byref(rows), None)
+    return st, bool(np.all(buf == 7777)) and rows.value == -5
+
+
+@pytest.mark.parametrize("args,code", [
+    ((10, None, None, 1, 0, 0), "CP_EINVAL"),           # cp_size < 1
+    ((10, None, None, 1, 2, 2), "CP_EINVAL"),           # rank out of range
+    ((10, None, None, 1, 2, -1), "CP_EINVAL"),
+    ((10, None, None, 1, 33, 0), "CP_EUNSUPPORTED"),    # cp_size above 32
+    ((10, None, None, 2, 2, 0), "CP_EINVAL"),           # NULL cu_seqlens needs one sample
+    ((0, None, None, 1, 2, 0), "CP_EINVAL"),            # empty single sample
+    ((10, None, [1, 10], 1, 2, 0), "CP_EINVAL"),        # cu[0] != 0
+    ((10, None, [0, 5, 5, 10], 3, 2, 0), "CP_EINVAL"),  # not strictly increasing
+    ((10, None, [0, 4, 9], 2, 2, 0), "CP_EINVAL"),      # last != seq_len
+    ((10, [11], None, 1, 2, 0), "CP_EINVAL"),           # image longer than sample
+    ((10, [-1], None, 1, 2, 0), "CP_EINVAL"),           # negative image
+    ((2 ** 31, None, None, 1, 2, 0), "CP_EUNSUPPORTED"),  # seq_len >= 2^31
+    ((-1, None, None, 1, 2, 0), "CP_EINVAL"),
+])
+def test_partition_errors_write_nothing(cp, args, code):
+    st, untouched = part(cp, *args)
+    assert st == getattr(cp, code)
+    assert untouched
+
+
+def test_partition_capacity(cp):
+    st, untouched = part(cp, 100, None, None, 1, 1, 0, cap=99)  # one rank: 100 rows
+    assert st == cp.CP_ENOSPC and untouched
+    st, _ = part(cp, 100, None, None, 1, 1, 0, cap=100)
+    assert st == cp.CP_OK
+
+
+def ws_status(cp, heads=4, kv_heads=4, head_dim=128, dtype=1, seq_len=100, P=2, r=0):
+    b = ctypes.c_size_t(12345)
+    st = cp.cp_attn_rank_workspace_size(seq_len, None, None, 1, P, r, heads, kv_heads, head_dim, dtype,
+                                        ctypes.byref(b))
+    return st, b.value
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(heads=6, kv_heads=4), "CP_EINVAL"),
+    (dict(heads=0), "CP_EINVAL"),
+    (dict(kv_heads=0), "CP_EINVAL"),
+    (dict(head_dim=96), "CP_EUNSUPPORTED"),
+    (dict(head_dim=256), "CP_EUNSUPPORTED"),
+    (dict(dtype=2), "CP_EUNSUPPORTED"),
+    (dict(r=5), "CP_EINVAL"),
+])
+def test_workspace_size_errors(cp, kw, code):
+    st, b = ws_status(cp, **kw)
+    assert st == getattr(cp, code) and b == 12345
+
+
+def test_fwd_argument_errors_before_any_device_work(cp):
+    # argument checks run before any HIP call, so these are CPU-safe
+    fake = ctypes.c_void_p(4096)  # never dereferenced: the call must fail first
+    ok_ws = ws_status(cp)[1]
+
+    def fwd(**kw):
+        a = dict(q=fake, k=fake, v=fake, dtype=1, seq_len=100, n_img=None, cu=None, n=1, P=2, r=0,
+                 H=4, Hkv=4, D=128, out=fake, lse=fake, ws=ctypes.c_void_p(1 << 20), wsb=ok_ws)
+        a.update(kw)
+        return cp.cp_attn_rank_fwd(a["q"], a["k"], a["v"], a["dtype"], a["seq_len"], a["n_img"],
+                                   a["cu"], a["n"], a["P"], a["r"], a["H"], a["Hkv"], a["D"], a["out"],
+                                   a["lse"], a["ws"], a["wsb"], None)
+    assert fwd(q=None) == cp.CP_EINVAL
+    assert fwd(out=None) == cp.CP_EINVAL
+    assert fwd(ws=None) == cp.CP_EINVAL
+    assert fwd(ws=ctypes.c_void_p((1 << 20) + 4)) == cp.CP_EINVAL  # workspace alignment
+    assert fwd(q=ctypes.c_void_p(4098)) == cp.CP_EINVAL  # q alignment
+    assert fwd(wsb=ok_ws - 1) == cp.CP_ENOSPC
+    assert fwd(D=80) == cp.CP_EUNSUPPORTED
+    assert fwd(dtype=7) == cp.CP_EUNSUPPORTED
+    assert fwd(H=6) == cp.CP_EINVAL
+    assert fwd(P=0) == cp.CP_EINVAL
+    assert fwd(seq_len=2 ** 31) == cp.CP_EUNSUPPORTED
+
+
+def test_gather_and_merge_argument_errors(cp):
+    fake = ctypes.c_void_p(4096)
+    assert cp.cp_gather_rows(fake, 5, 10, 64, fake, 4, fake, None) == cp.CP_EUNSUPPORTED
+    assert cp.cp_gather_rows(fake, 1, 10, 4, fake, 4, fake, None) == cp.CP_EUNSUPPORTED  # 8-byte rows
+    assert cp.cp_gather_rows(None, 1, 10, 64, fake, 4, fake, None) == cp.CP_EINVAL
+    assert cp.cp_gather_rows(fake, 1, 10, 64, fake, 0, fake, None) == cp.CP_OK  # nothing to do
+    assert cp.cp_lse_merge(fake, fake, fake, 0, 4, 2, 128, 1, fake, fake, None) == cp.CP_EINVAL
+    assert cp.cp_lse_merge(fake, fake, fake, 33, 4, 2, 128, 1, fake, fake, None) == cp.CP_EUNSUPPORTED
+    assert cp.cp_lse_merge(fake, fake, fake, 2, 4, 2, 96, 1, fake, fake, None) == cp.CP_EUNSUPPORTED
+    assert cp.cp_lse_merge(None, fake, fake, 2, 4, 2, 128, 1, fake, fake, None) == cp.CP_EINVAL
+
+
+def test_zero_row_problem(cp):
+    a, cu_rows = cp.partition_index(0, None, np.array([0], np.int32), cp_size=4, cp_rank=1)
+    assert a.size == 0 and list(cu_rows) == [0]
+    assert cp.pair_counts(0, None, np.array([0], np.int32), cp_size=4, cp_rank=1) == (0, 0)
