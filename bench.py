@@ -1,0 +1,202 @@
+"""Benchmark: useful causal attention TFLOP/s of one CP rank's share on one GPU.
+
+Default workload: text L=65536, P=8 (16 chunks of 4096), rank 3, GQA 32/8
+heads, head_dim 128, bf16 Q/K/V ~ N(0,1), batch 1. One step is one call of
+cp_attn_rank_fwd: host plan + upload, Q gather, per-step attention over all
+P ring steps, LSE merge. Inputs are resident in HBM before timing starts.
+
+Prints one JSON line. ``roofline`` covers the dominant kernel (the per-step
+attention): achieved = useful FLOPs per launch / its average duration, timed
+with HIP events recorded by the library on the launch stream.
+``cpu_baseline`` times the fp64 oracle on a bounded sample of the same
+rank's rows on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0
+METRIC = "useful causal attn TFLOP/s per CP-rank share (1 GPU) + % of bf16 MFMA peak"
+PMC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_text64k_r3_pmc.json")
+ATTN_SRC = os.path.join(ROOT, "context_parallelism_amd", "csrc", "attn_bf16.hip")
+
+
+def hip_runtime():
+    """The HIP runtime library already loaded in this process (torch's)."""
+    for line in open("/proc/self/maps"):
+        path = line.split()[-1]
+        if "libamdhip64.so" in path:
+            lib = ctypes.CDLL(path)
+            lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+            lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+            lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            return lib
+    raise RuntimeError("libamdhip64 is not loaded")
+
+
+def traffic_from_profile():
+    """HBM bytes per attention launch from the committed rocprofv3 counters,
+    or None if they were taken on a different version of the kernel."""
+    if not os.path.exists(PMC_FILE):
+        return None
+    doc = json.load(open(PMC_FILE))
+    sha = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
+    if doc.get("attn_bf16_sha256") != sha:
+        return None
+    return doc.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, q, k, v, n_img, cu, target_s: float):
+    """The fp64 oracle, as it stands, on a bounded sample of the rank's rows."""
+    import numpy as np
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    index, _ = oracle.partition_index(w.seq_len, n_img, cu, w.cp_size, w.rank)
+    R = len(index)
+    n = 32
+    while True:
+        rows = np.linspace(0, R - 1, n).astype(np.int64)
+        t0 = time.perf_counter()
+        oracle.rank_attention(q, k, v, n_img, cu, w.cp_size, w.rank, local_rows=rows)
+        dt = time.perf_counter() - t0
+        if dt >= target_s / 3 or n >= R:
+            break
+        n = min(R, int(n * max(2.0, target_s / max(dt, 1e-3))))
+    # a real row at position p of its sample sees p + 1 keys; pads see none
+    ids = index[rows].astype(np.int64)
+    ids = ids[ids >= 0]
+    starts = w.cu_seqlens.astype(np.int64)
+    pairs = int(np.sum(ids - starts[np.searchsorted(starts, ids, side="right") - 1] + 1))
+    flops = 4.0 * w.head_dim * w.heads * pairs
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n} of {R} rank-local rows (evenly spaced), all {w.heads} heads, "
+                      f"{pairs} useful pairs/head, {dt:.1f} s, fp64 numpy"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=4, help="synthetic workload number (1-5)")
+    ap.add_argument("--rank", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one CP rank's share on one GPU; --gpus {args.gpus} is not supported "
+              "(no multi-GPU path is built: see DESIGN.md, 'How the path would shard')", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import context_parallelism_amd as cp
+    import workloads
+
+    w = workloads.get(args.workload)
+    rank = w.rank if args.rank is None else args.rank
+    if rank != w.rank:
+        import dataclasses
+        w = dataclasses.replace(w, ranks=(rank,))
+    dev = torch.device("cuda:0")
+    q, k, v = workloads.make_inputs(w)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    n_img = w.n_img_array if any(w.n_img) else None
+    cu = w.cu_seqlens if w.n_samples > 1 else None
+    ra = cp.RankAttention(qd, kd, vd, cp_size=w.cp_size, cp_rank=rank, n_img=n_img, cu_seqlens=cu)
+    _, pairs = cp.pair_counts(w.seq_len, n_img, cu, cp_size=w.cp_size, cp_rank=rank)
+    useful = 4.0 * w.head_dim * w.heads * pairs
+
+    hip = hip_runtime()
+    K = args.steps
+    events = []
+    for _ in range(K):
+        evs = []
+        for _ in range(5):
+            e = ctypes.c_void_p()
+            assert hip.hipEventCreate(ctypes.byref(e)) == 0
+            evs.append(e.value)
+        events.append(evs)
+
+    for _ in range(args.warmup):
+        ra()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        ra(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    def elapsed(a, b):
+        ms = ctypes.c_float()
+        assert hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b)) == 0
+        return ms.value
+
+    stage = np.array([[elapsed(e[j], e[j + 1]) for j in range(4)] for e in events])  # ms
+    call = np.array([elapsed(e[0], e[4]) for e in events])
+    for evs in events:
+        for e in evs:
+            hip.hipEventDestroy(ctypes.c_void_p(e))
+
+    ms_per_step = wall / K * 1e3
+    value = useful / (wall / K) / 1e12
+    attn_ms = float(stage[:, 2].mean())
+    achieved = useful / (attn_ms * 1e-3) / 1e12
+    R = ra.R
+    esize = 2 if w.dtype == "bf16" else 4
+    gather_bytes = 2 * R * w.heads * w.head_dim * esize
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic: Q/K/V ~ N(0,1) drawn from numpy default_rng(%d), rounded to %s" % (w.seed, w.dtype),
+        "config": {"workload": w.name, "seq_len": w.seq_len, "cp_size": w.cp_size, "cp_rank": rank,
+                   "heads": w.heads, "kv_heads": w.kv_heads, "head_dim": w.head_dim,
+                   "n_img": list(w.n_img), "samples": w.n_samples, "rank_rows": R,
+                   "useful_pairs_per_head": pairs, "useful_flop": useful},
+        "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "stages_ms": {"plan_upload": round(float(stage[:, 0].mean()), 4),
+                      "gather": round(float(stage[:, 1].mean()), 4),
+                      "attention": round(attn_ms, 4),
+                      "merge": round(float(stage[:, 3].mean()), 4),
+                      "call_median": round(float(np.median(call)), 4),
+                      "call_p10": round(float(np.percentile(call, 10)), 4),
+                      "call_p90": round(float(np.percentile(call, 90)), 4)},
+        "gather_GBps": round(gather_bytes / (float(stage[:, 1].mean()) * 1e-3) / 1e9, 1),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic_from_profile(),
+                     "kernel": "attn_step_bf16_kernel (per-step attention, all ring steps, one launch)"},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, q, k, v, n_img, cu, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -20,6 +20,7 @@ from ._lib import (  # noqa: F401
     CpError,
     check,
     cp_attn_rank_fwd,
+    cp_attn_rank_fwd_timed,
     cp_attn_rank_plan_stats,
     cp_attn_rank_workspace_size,
     cp_gather_rows,

@@ -37,6 +37,9 @@ SIGNATURES = [
     ("cp_attn_rank_fwd", c_int32,
      [c_void_p, c_void_p, c_void_p, c_int32, c_int64, _P32, _P32, c_int32, c_int32, c_int32,
       c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+    ("cp_attn_rank_fwd_timed", c_int32,
+     [c_void_p, c_void_p, c_void_p, c_int32, c_int64, _P32, _P32, c_int32, c_int32, c_int32,
+      c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p, POINTER(c_void_p)]),
     ("cp_gather_rows", c_int32, [c_void_p, c_int32, c_int64, c_int64, c_void_p, c_int64, c_void_p, c_void_p]),
     ("cp_lse_merge", c_int32,
      [c_void_p, c_void_p, c_void_p, c_int32, c_int64, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p]),
@@ -94,5 +97,6 @@ cp_pair_counts = _fn("cp_pair_counts")
 cp_attn_rank_workspace_size = _fn("cp_attn_rank_workspace_size")
 cp_attn_rank_plan_stats = _fn("cp_attn_rank_plan_stats")
 cp_attn_rank_fwd = _fn("cp_attn_rank_fwd")
+cp_attn_rank_fwd_timed = _fn("cp_attn_rank_fwd_timed")
 cp_gather_rows = _fn("cp_gather_rows")
 cp_lse_merge = _fn("cp_lse_merge")

@@ -128,13 +128,19 @@ class RankAttention:
         self.lse = torch.empty((self.H, self.R), dtype=torch.float32, device=dev)
         self.workspace = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=dev)
 
-    def __call__(self):
-        st = _lib.cp_attn_rank_fwd(self.q.data_ptr(), self.k.data_ptr(), self.v.data_ptr(), self.dtype,
-                                   self.T, self._img_p, self._cu_p, self.n_samples, self.cp_size,
-                                   self.cp_rank, self.H, self.Hkv, self.D, self.out.data_ptr(),
-                                   self.lse.data_ptr(), self.workspace.data_ptr(), self.ws_bytes,
-                                   _stream(self.q))
-        check(st, "cp_attn_rank_fwd")
+    def __call__(self, events=None):
+        """Run the forward. ``events``: optional sequence of five raw
+        hipEvent_t handles recorded at the stage boundaries
+        (cp_attn_rank_fwd_timed)."""
+        args = (self.q.data_ptr(), self.k.data_ptr(), self.v.data_ptr(), self.dtype, self.T,
+                self._img_p, self._cu_p, self.n_samples, self.cp_size, self.cp_rank, self.H, self.Hkv,
+                self.D, self.out.data_ptr(), self.lse.data_ptr(), self.workspace.data_ptr(),
+                self.ws_bytes, _stream(self.q))
+        if events is None:
+            check(_lib.cp_attn_rank_fwd(*args), "cp_attn_rank_fwd")
+        else:
+            ev = (ctypes.c_void_p * 5)(*[ctypes.c_void_p(int(e)) for e in events])
+            check(_lib.cp_attn_rank_fwd_timed(*args, ev), "cp_attn_rank_fwd_timed")
         return self.out, self.lse
 
 

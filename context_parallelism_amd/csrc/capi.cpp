@@ -65,15 +65,15 @@ hipError_t stage_and_upload(const Workspace& w, void* dst, hipStream_t stream) {
 
 inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-}  // namespace
+inline hipError_t mark(void* const* events, int i, hipStream_t s) {
+  return events ? hipEventRecord(static_cast<hipEvent_t>(events[i]), s) : hipSuccess;
+}
 
-extern "C" {
-
-cp_status cp_attn_rank_fwd(const void* q, const void* k, const void* v, int32_t dtype,
-                           int64_t seq_len, const int32_t* n_img, const int32_t* cu_seqlens,
-                           int32_t n_samples, int32_t cp_size, int32_t cp_rank, int32_t heads,
-                           int32_t kv_heads, int32_t head_dim, void* out, float* lse,
-                           void* workspace, size_t workspace_bytes, void* stream) {
+cp_status rank_fwd(const void* q, const void* k, const void* v, int32_t dtype, int64_t seq_len,
+                   const int32_t* n_img, const int32_t* cu_seqlens, int32_t n_samples,
+                   int32_t cp_size, int32_t cp_rank, int32_t heads, int32_t kv_heads,
+                   int32_t head_dim, void* out, float* lse, void* workspace,
+                   size_t workspace_bytes, void* stream, void* const* events) {
   try {
     Workspace w;
     int32_t st = prepare_workspace(seq_len, n_img, cu_seqlens, n_samples, cp_size, cp_rank, heads,
@@ -90,10 +90,13 @@ cp_status cp_attn_rank_fwd(const void* q, const void* k, const void* v, int32_t 
     uint8_t* ws = static_cast<uint8_t*>(workspace);
     const size_t esize = dtype == CP_DTYPE_BF16 ? 2 : 4;
 
+    if (mark(events, 0, s) != hipSuccess) return CP_EHIP;
     if (stage_and_upload(w, ws, s) != hipSuccess) return CP_EHIP;
+    if (mark(events, 1, s) != hipSuccess) return CP_EHIP;
     const int32_t* index = reinterpret_cast<const int32_t*>(ws + w.off_index);
     if (launch_gather(q, index, ws + w.off_qr, R, int64_t(heads) * head_dim * esize, s) != hipSuccess)
       return CP_EHIP;
+    if (mark(events, 2, s) != hipSuccess) return CP_EHIP;
 
     AttnArgs a;
     a.qr = ws + w.off_qr;
@@ -116,15 +119,40 @@ cp_status cp_attn_rank_fwd(const void* q, const void* k, const void* v, int32_t 
                        ? launch_attn_bf16(a, head_dim, w.shape.heads_per_wg, n_entries, s)
                        : launch_attn_f32(a, head_dim, n_entries, s);
     if (e != hipSuccess) return CP_EHIP;
+    if (mark(events, 3, s) != hipSuccess) return CP_EHIP;
 
     const uint32_t* mask = reinterpret_cast<const uint32_t*>(ws + w.off_mask);
     if (launch_lse_merge(a.part_o, a.part_lse, mask, cp_size, R, heads, head_dim, dtype, out, lse, s) !=
         hipSuccess)
       return CP_EHIP;
+    if (mark(events, 4, s) != hipSuccess) return CP_EHIP;
     return CP_OK;
   } catch (const std::exception&) {
     return CP_EINVAL;
   }
+}
+
+}  // namespace
+
+extern "C" {
+
+cp_status cp_attn_rank_fwd(const void* q, const void* k, const void* v, int32_t dtype,
+                           int64_t seq_len, const int32_t* n_img, const int32_t* cu_seqlens,
+                           int32_t n_samples, int32_t cp_size, int32_t cp_rank, int32_t heads,
+                           int32_t kv_heads, int32_t head_dim, void* out, float* lse,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  return rank_fwd(q, k, v, dtype, seq_len, n_img, cu_seqlens, n_samples, cp_size, cp_rank, heads,
+                  kv_heads, head_dim, out, lse, workspace, workspace_bytes, stream, nullptr);
+}
+
+cp_status cp_attn_rank_fwd_timed(const void* q, const void* k, const void* v, int32_t dtype,
+                                 int64_t seq_len, const int32_t* n_img, const int32_t* cu_seqlens,
+                                 int32_t n_samples, int32_t cp_size, int32_t cp_rank,
+                                 int32_t heads, int32_t kv_heads, int32_t head_dim, void* out,
+                                 float* lse, void* workspace, size_t workspace_bytes,
+                                 void* stream, void* const* events) {
+  return rank_fwd(q, k, v, dtype, seq_len, n_img, cu_seqlens, n_samples, cp_size, cp_rank, heads,
+                  kv_heads, head_dim, out, lse, workspace, workspace_bytes, stream, events);
 }
 
 cp_status cp_gather_rows(const void* src, int32_t dtype, int64_t src_rows, int64_t row_elems,

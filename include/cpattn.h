@@ -154,6 +154,22 @@ cp_status cp_attn_rank_fwd(const void *q, const void *k, const void *v, int32_t 
                            void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * cp_attn_rank_fwd_timed -- cp_attn_rank_fwd that also records five
+ * caller-created hipEvent_t on `stream` at its stage boundaries:
+ * events[0] before the plan upload, [1] after it, [2] after the gather,
+ * [3] after the per-step attention, [4] after the merge. A caller can then
+ * time one stage with hipEventElapsedTime, without a profiler. events may
+ * be NULL (then this is exactly cp_attn_rank_fwd). The library does not
+ * keep the events.
+ */
+cp_status cp_attn_rank_fwd_timed(const void *q, const void *k, const void *v, int32_t dtype,
+                                 int64_t seq_len, const int32_t *n_img, const int32_t *cu_seqlens,
+                                 int32_t n_samples, int32_t cp_size, int32_t cp_rank,
+                                 int32_t heads, int32_t kv_heads, int32_t head_dim, void *out,
+                                 float *lse, void *workspace, size_t workspace_bytes,
+                                 void *stream, void *const *events);
+
+/*
  * cp_gather_rows -- the chunk-index gather alone (page section 1.1,
  * index_select on the sequence dimension): dst[i, :] = src[index[i], :]
  * for index[i] >= 0 and 0 for index[i] == -1.
