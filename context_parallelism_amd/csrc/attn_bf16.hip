@@ -19,12 +19,24 @@
 // natural [key][d] layout in LDS; ds_read_b64_tr_b16 produces the V^T
 // operand. K and V tiles of 64 keys are double-buffered in LDS; the next
 // tile's global loads are in flight while the current tile is computed.
-// Several waves of a workgroup share each K/V tile: 4 rows-blocks of one
-// head (MHA) or one rows-block of 2 or 4 heads that read the same KV head
+// Several waves of a workgroup share each K/V tile: 4 row blocks of one
+// head (MHA) or one row block of 2 or 4 heads that read the same KV head
 // (GQA).
 //
+// Global K/V loads go through a buffer resource whose size ends at the
+// span end: rows past it read as zeros in hardware, so the loads need no
+// branches and their per-lane offsets never change.
+//
+// Online softmax with a lazy reference max: probabilities are
+// exp2((s - m_ref) * log2(e)/sqrt(D)); m_ref moves (and the output and sum
+// are rescaled) only when a row's running max exceeds it by more than
+// kRescaleLog2 in the exp2 domain, so probabilities stay below
+// 2^kRescaleLog2 and most tiles skip the rescale. The output and the sum
+// always share the same m_ref, so the normalised result is unchanged.
+//
 // Output per entry: O_s normalised by its own softmax sum (fp32) and
-// lse_s = max + ln(sum) (fp32), combined across steps by the LSE merge.
+// lse_s = m_ref/sqrt(D) + ln(sum) (fp32), combined across steps by the LSE
+// merge.
 #include "kernels.h"
 
 namespace cpattn {
@@ -35,10 +47,14 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-// Value of the lane 32 positions away combined with our own: the swap puts
-// lanes 0-31 of one copy next to lanes 32-63 of the other.
+constexpr int kBufferWord3 = 0x00020000;  // raw buffer access, gfx9 family
+constexpr float kRescaleLog2 = 8.0f;      // lazy-rescale threshold (exp2 domain)
+
+// Our value combined with that of lane ^ 32: the swap puts lanes 0-31 of
+// one copy next to lanes 32-63 of the other.
 __device__ inline float max_with_partner(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
@@ -48,8 +64,13 @@ __device__ inline float sum_with_partner(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kBufferWord3);
+}
+
 template <int D, int NW, int G>
-__global__ __launch_bounds__(NW * 64) void attn_step_bf16_kernel(AttnArgs a) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_step_bf16_kernel(const AttnArgs a) {
   constexpr int BN = kBlockN;               // keys per tile
   constexpr int KS = D + 8;                 // K row stride in LDS (bf16): b128 reads conflict-free
   constexpr int VS = D + 32;                // V row stride: transposed b64 reads conflict-free
@@ -95,25 +116,29 @@ __global__ __launch_bounds__(NW * 64) void attn_step_bf16_kernel(AttnArgs a) {
     }
   }
 
-  const __bf16* kg = static_cast<const __bf16*>(a.k);
-  const __bf16* vg = static_cast<const __bf16*>(a.v);
-  const int64_t tok = int64_t(a.Hkv) * D;  // elements between consecutive tokens
-  uint4 kreg[PPT], vreg[PPT];
-
+  // K/V tile loads: per-lane byte offsets inside a tile never change; the
+  // tile's base and its valid size go into the buffer resource.
+  const int tok_bytes = a.Hkv * D * 2;  // bytes between consecutive tokens
+  const char* kbase = static_cast<const char*>(a.k) + int64_t(kvh) * D * 2;
+  const char* vbase = static_cast<const char*>(a.v) + int64_t(kvh) * D * 2;
+  int goff[PPT], loff[PPT];
+#pragma unroll
+  for (int i = 0; i < PPT; ++i) {
+    const int p = tid + i * NT;
+    const int row = p / RPIECES, col = p % RPIECES;
+    goff[i] = row * tok_bytes + col * 16;
+    loff[i] = row * KS + col * 8;  // K; V adds row * (VS - KS)
+  }
+  u32x4 kreg[PPT], vreg[PPT];
   auto load_tile = [&](int kt, int k1) {
+    const int valid = min(k1 - kt, BN) * tok_bytes;
+    const int64_t off = int64_t(kt) * tok_bytes;
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase + off, valid);
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase + off, valid);
 #pragma unroll
     for (int i = 0; i < PPT; ++i) {
-      const int p = tid + i * NT;
-      const int row = p / RPIECES, col = p % RPIECES;
-      const int key = kt + row;
-      if (key < k1) {
-        const int64_t off = int64_t(key) * tok + int64_t(kvh) * D + col * 8;
-        kreg[i] = *reinterpret_cast<const uint4*>(kg + off);
-        vreg[i] = *reinterpret_cast<const uint4*>(vg + off);
-      } else {  // past the span end: zeros (finite, and masked in the scores)
-        kreg[i] = make_uint4(0, 0, 0, 0);
-        vreg[i] = make_uint4(0, 0, 0, 0);
-      }
+      kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(kr, goff[i], 0, 0);
+      vreg[i] = __builtin_amdgcn_raw_buffer_load_b128(vr, goff[i], 0, 0);
     }
   };
   auto store_tile = [&](int buf) {
@@ -121,10 +146,9 @@ __global__ __launch_bounds__(NW * 64) void attn_step_bf16_kernel(AttnArgs a) {
     __bf16* vs = ks + KBUF;
 #pragma unroll
     for (int i = 0; i < PPT; ++i) {
-      const int p = tid + i * NT;
-      const int row = p / RPIECES, col = p % RPIECES;
-      *reinterpret_cast<uint4*>(ks + row * KS + col * 8) = kreg[i];
-      *reinterpret_cast<uint4*>(vs + row * VS + col * 8) = vreg[i];
+      const int row = (tid + i * NT) / RPIECES;
+      *reinterpret_cast<u32x4*>(ks + loff[i]) = kreg[i];
+      *reinterpret_cast<u32x4*>(vs + loff[i] + row * (VS - KS)) = vreg[i];
     }
   };
 
@@ -133,9 +157,10 @@ __global__ __launch_bounds__(NW * 64) void attn_step_bf16_kernel(AttnArgs a) {
   for (int db = 0; db < ND; ++db)
 #pragma unroll
     for (int t = 0; t < 16; ++t) o[db][t] = 0.f;
-  float m = -INFINITY;  // running max of raw scores for this lane's row
-  float l = 0.f;        // running sum over this lane's keys (other half in lane ^ 32)
+  float m_ref = -INFINITY;  // reference max (raw score units) for this lane's row
+  float l = 0.f;            // sum over this lane's keys (other half in lane ^ 32)
   const float c2 = a.scale_log2;
+  const float thr = kRescaleLog2 / c2;
 
   auto compute = [&](int buf, int kt, int k1) {
     const __bf16* ks = smem + buf * STAGE;
@@ -169,9 +194,18 @@ __global__ __launch_bounds__(NW * 64) void attn_step_bf16_kernel(AttnArgs a) {
 #pragma unroll
       for (int t = 0; t < 16; ++t) mx = fmaxf(mx, s[kb][t]);
     mx = max_with_partner(mx);
-    const float m_new = fmaxf(m, mx);
-    const float ms = (m_new == -INFINITY) ? 0.f : m_new * c2;
-    const float alpha = __builtin_amdgcn_exp2f(m * c2 - ms);
+    const bool grow_ref = mx > m_ref + thr;  // also true on a row's first visible key
+    if (__builtin_amdgcn_ballot_w64(grow_ref) != 0) {
+      const float m_new = grow_ref ? mx : m_ref;
+      const float alpha = __builtin_amdgcn_exp2f((m_ref - m_new) * c2);  // 0 when m_ref = -inf
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < ND; ++db)
+#pragma unroll
+        for (int t = 0; t < 16; ++t) o[db][t] *= alpha;
+      m_ref = m_new;
+    }
+    const float ms = (m_ref == -INFINITY) ? 0.f : m_ref * c2;
     bf16x8 pb[2][2];
     float rs = 0.f;
 #pragma unroll
@@ -182,16 +216,11 @@ __global__ __launch_bounds__(NW * 64) void attn_step_bf16_kernel(AttnArgs a) {
         rs += p;
         pb[kb][t >> 3][t & 7] = (__bf16)p;
       }
-    l = l * alpha + rs;
-    m = m_new;
-#pragma unroll
-    for (int db = 0; db < ND; ++db)
-#pragma unroll
-      for (int t = 0; t < 16; ++t) o[db][t] *= alpha;
+    l += rs;
     // O^T += V^T P^T. A operand (V^T): lane holds V[key][32*db + lane%32]
     // for the 8 keys whose probabilities sit in its B operand; built from
     // two transposed 4-key reads per MFMA.
-    const int trow = (lane & 15) >> 2;                       // key offset inside a 4-key read
+    const int trow = (lane & 15) >> 2;                         // key offset inside a 4-key read
     const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);  // d offset inside a 32-block
 #pragma unroll
     for (int db = 0; db < ND; ++db)
@@ -252,7 +281,7 @@ __global__ __launch_bounds__(NW * 64) void attn_step_bf16_kernel(AttnArgs a) {
     }
   if (hh == 0)
     a.part_lse[(int64_t(ent.step) * a.H + h) * a.R + lrow] =
-        lt > 0.f ? m * a.scale + logf(lt) : -INFINITY;
+        lt > 0.f ? m_ref * a.scale + logf(lt) : -INFINITY;
 }
 
 template <int D, int G>
