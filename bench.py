@@ -98,6 +98,9 @@ def main():
     ap.add_argument("--rank", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="instead of the attention, run --steps plain device copies of this many MiB "
+                         "(the reference kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one CP rank's share on one GPU; --gpus {args.gpus} is not supported "
@@ -109,6 +112,16 @@ def main():
 
     import context_parallelism_amd as cp
     import workloads
+
+    if args.copy_mib:
+        n = args.copy_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup + args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "launches": args.warmup + args.steps}), flush=True)
+        return
 
     w = workloads.get(args.workload)
     rank = w.rank if args.rank is None else args.rank

@@ -52,6 +52,7 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int kBufferWord3 = 0x00020000;  // raw buffer access, gfx9 family
 constexpr float kRescaleLog2 = 8.0f;      // lazy-rescale threshold (exp2 domain)
+constexpr int kWaitVmcnt0 = 0x0F70;       // s_waitcnt vmcnt(0), expcnt and lgkmcnt untouched
 
 // Our value combined with that of lane ^ 32: the swap puts lanes 0-31 of
 // one copy next to lanes 32-63 of the other.
@@ -284,6 +285,264 @@ void attn_step_bf16_kernel(const AttnArgs a) {
         lt > 0.f ? m_ref * a.scale + logf(lt) : -INFINITY;
 }
 
+// ---------------------------------------------------------------------------
+// head_dim 128: software-pipelined variant.
+//
+// Differences from the kernel above:
+//  * K and V tiles go from HBM straight into LDS (buffer_load ... lds), no
+//    staging registers. One wave instruction fills 1 KiB of LDS (lane l at
+//    byte 16*l), so rows are unpadded (256 B) and bank conflicts are avoided
+//    by XOR-swizzling the 16-byte granules of each row: K granule g of row r
+//    sits at g ^ (r & 15), which spreads the 16 rows read by a b128 access
+//    over all banks; V granule g sits at g ^ 4*(r & 3), which spreads the
+//    4 rows x 4 granules of a transposed read over all banks.
+//  * K runs one tile ahead of V: while the softmax of tile t runs on VALU,
+//    the QK^T MFMAs of tile t+1 are already issued, so matrix and vector
+//    work overlap inside one wave. K is double-buffered and V
+//    triple-buffered, so each tile needs a single barrier.
+template <int G>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_step_bf16_d128_kernel(const AttnArgs a) {
+  constexpr int D = 128, BN = kBlockN, NW = 4;
+  constexpr int TILE = BN * D * 2;           // bytes of one K (or V) tile
+  constexpr int CH = TILE / 1024 / NW;       // LDS-DMA instructions per wave per tensor
+  constexpr int ND = D / 32, NQ = D / 16;
+  static_assert(BN == 64, "tile walk assumes 64-key tiles");
+  __shared__ __attribute__((aligned(1024))) char smem[5 * TILE];  // K0 K1 | V0 V1 V2
+  typedef __attribute__((address_space(3))) void lds_void;
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int hg = blockIdx.x % a.n_hg;
+  const EntryRec ent = a.entries[blockIdx.x / a.n_hg];
+  const TileRec tile = a.tiles[ent.tile];
+  const int h = hg * G + (wave % G);
+  const int rsub = wave / G;
+  const int kvh = (hg * G) / a.group;
+  const int ql = lane & 31, hh = lane >> 5;
+  const int rin = rsub * 32 + ql;
+  const bool row_ok = rin < tile.nrows;
+  const int lrow = tile.local0 + rin;
+  const int grow = tile.g0 + rin;
+  const int wave_lo = tile.g0 + rsub * 32;
+
+  // Key spans of this entry (at most 3: image prefix and two text chunks).
+  int sk0[3] = {0, 0, 0}, sk1[3] = {0, 0, 0}, snt[3] = {0, 0, 0};
+  int n_tiles = 0;
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    if (ent.span_begin + i < ent.span_end) {
+      const SpanRec sp = a.spans[ent.span_begin + i];
+      sk0[i] = sp.k0;
+      sk1[i] = sp.k1;
+      snt[i] = (sp.k1 - sp.k0 + BN - 1) / BN;
+      n_tiles += snt[i];
+    }
+  }
+  auto tile_at = [&](int t, int& kt, int& k1) {
+    if (t < snt[0]) { kt = sk0[0] + t * BN; k1 = sk1[0]; return; }
+    t -= snt[0];
+    if (t < snt[1]) { kt = sk0[1] + t * BN; k1 = sk1[1]; return; }
+    t -= snt[1];
+    kt = sk0[2] + t * BN;
+    k1 = sk1[2];
+  };
+
+  bf16x8 qf[NQ];
+  {
+    const __bf16* qp = static_cast<const __bf16*>(a.qr) + (int64_t(lrow) * a.H + h) * D + 8 * hh;
+#pragma unroll
+    for (int jj = 0; jj < NQ; ++jj) {
+      if (row_ok) {
+        qf[jj] = *reinterpret_cast<const bf16x8*>(qp + 16 * jj);
+      } else {
+        s16x8 z = {0, 0, 0, 0, 0, 0, 0, 0};
+        qf[jj] = __builtin_bit_cast(bf16x8, z);
+      }
+    }
+  }
+
+  // LDS-DMA source offsets: instruction i of this wave fills LDS rows
+  // 4c..4c+3 (c = wave*CH + i); lane l fills physical granule l%16 of row
+  // 4c + l/16, i.e. the logical granule that the row's swizzle maps there.
+  const int tok_bytes = a.Hkv * D * 2;
+  const char* kbase = static_cast<const char*>(a.k) + int64_t(kvh) * D * 2;
+  const char* vbase = static_cast<const char*>(a.v) + int64_t(kvh) * D * 2;
+  int kgo[CH], vgo[CH];
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int row = 4 * (wave * CH + i) + (lane >> 4);
+    const int p = lane & 15;
+    kgo[i] = row * tok_bytes + 16 * (p ^ (row & 15));
+    vgo[i] = row * tok_bytes + 16 * (p ^ (4 * (row & 3)));
+  }
+  auto issue = [&](int t, int kslot, int vslot) {
+    int kt, k1;
+    tile_at(t, kt, k1);
+    const int valid = min(k1 - kt, BN) * tok_bytes;
+    const int64_t off = int64_t(kt) * tok_bytes;
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase + off, valid);
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase + off, valid);
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          kr, (lds_void*)(smem + kslot * TILE + (wave * CH + i) * 1024), 16, kgo[i], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          vr, (lds_void*)(smem + (2 + vslot) * TILE + (wave * CH + i) * 1024), 16, vgo[i], 0, 0, 0);
+    }
+  };
+
+  // K operand reads: row 32*kb + ql, logical granule 2*jj + hh.
+  int kro[NQ];
+#pragma unroll
+  for (int jj = 0; jj < NQ; ++jj) kro[jj] = ql * 256 + 16 * ((2 * jj + hh) ^ (ql & 15));
+  // V transposed reads: rows 32*kb + 16*sub + 8*half + 4*hh + trow,
+  // logical granule 4*db + gsub, byte 8*(lane & 1) inside it.
+  const int trow = (lane & 15) >> 2;
+  const int gsub = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  int vro[ND];
+#pragma unroll
+  for (int db = 0; db < ND; ++db)
+    vro[db] = (4 * hh + trow) * 256 + 16 * (4 * (db ^ trow) + gsub) + 8 * (lane & 1);
+
+  auto qk = [&](int kslot, f32x16 (&s)[2]) {
+    const char* kb0 = smem + kslot * TILE;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int jj = 0; jj < NQ; ++jj) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kb0 + kb * 32 * 256 + kro[jj]);
+        if (jj == 0) {
+          f32x16 z;
+#pragma unroll
+          for (int t = 0; t < 16; ++t) z[t] = 0.f;
+          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[jj], z, 0, 0, 0);
+        } else {
+          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[jj], s[kb], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  f32x16 o[ND];
+#pragma unroll
+  for (int db = 0; db < ND; ++db)
+#pragma unroll
+    for (int t = 0; t < 16; ++t) o[db][t] = 0.f;
+  float m_ref = -INFINITY, l = 0.f;
+  const float c2 = a.scale_log2;
+  const float thr = kRescaleLog2 / c2;
+
+  auto softmax_pv = [&](int t, int vslot, f32x16 (&s)[2]) {
+    int kt, k1;
+    tile_at(t, kt, k1);
+    if (kt + BN > k1 || kt + BN - 1 > wave_lo) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kt + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
+          if (key >= k1 || key > grow) s[kb][r] = -INFINITY;
+        }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    mx = max_with_partner(mx);
+    const bool grow_ref = mx > m_ref + thr;
+    if (__builtin_amdgcn_ballot_w64(grow_ref) != 0) {
+      const float m_new = grow_ref ? mx : m_ref;
+      const float alpha = __builtin_amdgcn_exp2f((m_ref - m_new) * c2);
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < ND; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+      m_ref = m_new;
+    }
+    const float ms = (m_ref == -INFINITY) ? 0.f : m_ref * c2;
+    bf16x8 pb[2][2];
+    float rs = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c2, -ms));
+        rs += p;
+        pb[kb][r >> 3][r & 7] = (__bf16)p;
+      }
+    l += rs;
+    const char* vb0 = smem + (2 + vslot) * TILE;
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub) {
+          const char* p0 = vb0 + vro[db] + (32 * kb + 16 * sub) * 256;
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0));
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 8 * 256));
+          const s16x8 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, both),
+                                                          pb[kb][sub], o[db], 0, 0, 0);
+        }
+  };
+
+  // Pipeline (see the comment above the kernel). Iteration t: wait for
+  // tile t+1's K/V, barrier, start loading tile t+2, issue QK^T of tile t+1,
+  // then softmax and PV of tile t. Unrolled by two so score registers and K
+  // slots alternate at compile time.
+  f32x16 sa[2], sb[2];
+  issue(0, 0, 0);
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  __syncthreads();
+  if (n_tiles > 1) issue(1, 1, 1);
+  qk(0, sa);
+  int vslot = 0;  // V slot of tile t
+  for (int t = 0; t < n_tiles; t += 2) {
+    // even step: scores of t in sa, K of t+1 in slot 1
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    if (t + 2 < n_tiles) issue(t + 2, 0, vslot == 0 ? 2 : vslot - 1);
+    if (t + 1 < n_tiles) qk(1, sb);
+    softmax_pv(t, vslot, sa);
+    vslot = vslot == 2 ? 0 : vslot + 1;
+    if (t + 1 >= n_tiles) break;
+    // odd step: scores of t+1 in sb, K of t+2 in slot 0
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    if (t + 3 < n_tiles) issue(t + 3, 1, vslot == 0 ? 2 : vslot - 1);
+    if (t + 2 < n_tiles) qk(0, sa);
+    softmax_pv(t + 1, vslot, sb);
+    vslot = vslot == 2 ? 0 : vslot + 1;
+  }
+
+  const float lt = sum_with_partner(l);
+  if (!row_ok) return;
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  float* po = a.part_o + ((int64_t(ent.step) * a.R + lrow) * a.H + h) * D + 4 * hh;
+#pragma unroll
+  for (int db = 0; db < ND; ++db)
+#pragma unroll
+    for (int tq = 0; tq < 4; ++tq) {
+      const float4 val = make_float4(o[db][4 * tq] * inv, o[db][4 * tq + 1] * inv,
+                                     o[db][4 * tq + 2] * inv, o[db][4 * tq + 3] * inv);
+      *reinterpret_cast<float4*>(po + 32 * db + 8 * tq) = val;
+    }
+  if (hh == 0)
+    a.part_lse[(int64_t(ent.step) * a.H + h) * a.R + lrow] =
+        lt > 0.f ? m_ref * a.scale + logf(lt) : -INFINITY;
+}
+
+template <int G>
+hipError_t launch_d128(const AttnArgs& a, int n_entries, hipStream_t stream) {
+  const int64_t blocks = int64_t(n_entries) * a.n_hg;
+  if (blocks >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((attn_step_bf16_d128_kernel<G>), dim3(uint32_t(blocks)), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
 template <int D, int G>
 hipError_t launch_g(const AttnArgs& a, int n_entries, hipStream_t stream) {
   const int64_t blocks = int64_t(n_entries) * a.n_hg;
@@ -299,9 +558,9 @@ hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, int heads_per_wg, i
                             hipStream_t stream) {
   if (n_entries == 0) return hipSuccess;
   if (head_dim == 128) {
-    if (heads_per_wg == 4) return launch_g<128, 4>(a, n_entries, stream);
-    if (heads_per_wg == 2) return launch_g<128, 2>(a, n_entries, stream);
-    return launch_g<128, 1>(a, n_entries, stream);
+    if (heads_per_wg == 4) return launch_d128<4>(a, n_entries, stream);
+    if (heads_per_wg == 2) return launch_d128<2>(a, n_entries, stream);
+    return launch_d128<1>(a, n_entries, stream);
   }
   if (head_dim == 64) {
     if (heads_per_wg == 4) return launch_g<64, 4>(a, n_entries, stream);
