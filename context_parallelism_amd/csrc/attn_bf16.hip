@@ -53,6 +53,10 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 constexpr int kBufferWord3 = 0x00020000;  // raw buffer access, gfx9 family
 constexpr float kRescaleLog2 = 8.0f;      // lazy-rescale threshold (exp2 domain)
 constexpr int kWaitVmcnt0 = 0x0F70;       // s_waitcnt vmcnt(0), expcnt and lgkmcnt untouched
+// __builtin_amdgcn_sched_group_barrier instruction classes
+constexpr int kSchedValu = 0x0002;
+constexpr int kSchedMfma = 0x0008;
+constexpr int kSchedDsRead = 0x0100;
 
 // Our value combined with that of lane ^ 32: the swap puts lanes 0-31 of
 // one copy next to lanes 32-63 of the other.
@@ -289,13 +293,23 @@ void attn_step_bf16_kernel(const AttnArgs a) {
 // head_dim 128: software-pipelined variant.
 //
 // Differences from the kernel above:
-//  * K and V tiles go from HBM straight into LDS (buffer_load ... lds), no
-//    staging registers. One wave instruction fills 1 KiB of LDS (lane l at
-//    byte 16*l), so rows are unpadded (256 B) and bank conflicts are avoided
-//    by XOR-swizzling the 16-byte granules of each row: K granule g of row r
-//    sits at g ^ (r & 15), which spreads the 16 rows read by a b128 access
-//    over all banks; V granule g sits at g ^ 4*(r & 3), which spreads the
-//    4 rows x 4 granules of a transposed read over all banks.
+//  * V is read from a V^T copy (vt[g][d][key], made once per call), so the
+//    PV operand needs no transposing read: each lane's 8 keys at one d are
+//    16 contiguous bytes, read with ds_read_b128 like K.
+//  * Lane ql of the QK^T operand reads K row sigma(ql), sigma swapping bits
+//    2 and 3 of the row index. The S^T accumulator register t of lane half
+//    hh then holds key 16*(t/8) + 8*hh + t%8: eight consecutive keys per
+//    MFMA operand, exactly the keys of the lane's contiguous V^T read.
+//  * K and V^T tiles go from HBM straight into LDS (buffer_load ... lds),
+//    no staging registers. One wave instruction fills 1 KiB of LDS (lane l
+//    at byte 16*l), so rows are unpadded and bank conflicts are avoided by
+//    XOR-swizzling 16-byte granules: K granule g of row r sits at
+//    g ^ (r & 15) (16 rows read together land on 16 granule slots); V^T
+//    granule g of row d sits at g ^ ((d >> 1) & 7) (128-byte rows, two per
+//    bank sweep, 16 rows read together land on 16 slots). All LDS read
+//    addresses are per-lane constants plus immediates.
+//  * Key tiles start at multiples of 8 keys so V^T rows load 16-byte
+//    aligned; keys below the span start are masked like those past its end.
 //  * K runs one tile ahead of V: while the softmax of tile t runs on VALU,
 //    the QK^T MFMAs of tile t+1 are already issued, so matrix and vector
 //    work overlap inside one wave. K is double-buffered and V
@@ -304,11 +318,18 @@ template <int G>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_step_bf16_d128_kernel(const AttnArgs a) {
   constexpr int D = 128, BN = kBlockN, NW = 4;
-  constexpr int TILE = BN * D * 2;           // bytes of one K (or V) tile
+  constexpr int TILE = BN * D * 2;           // bytes of one K (or V^T) tile
   constexpr int CH = TILE / 1024 / NW;       // LDS-DMA instructions per wave per tensor
   constexpr int ND = D / 32, NQ = D / 16;
   static_assert(BN == 64, "tile walk assumes 64-key tiles");
-  __shared__ __attribute__((aligned(1024))) char smem[5 * TILE];  // K0 K1 | V0 V1 V2
+  // Separate arrays per buffer, each chosen at compile time in the unrolled
+  // loop, so the compiler can tell an in-flight LDS-DMA target from the
+  // buffers being read and waits only where they alias.
+  __shared__ __attribute__((aligned(1024))) char k0s[TILE];
+  __shared__ __attribute__((aligned(1024))) char k1s[TILE];
+  __shared__ __attribute__((aligned(1024))) char v0s[TILE];
+  __shared__ __attribute__((aligned(1024))) char v1s[TILE];
+  __shared__ __attribute__((aligned(1024))) char v2s[TILE];
   typedef __attribute__((address_space(3))) void lds_void;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -325,7 +346,8 @@ void attn_step_bf16_d128_kernel(const AttnArgs a) {
   const int grow = tile.g0 + rin;
   const int wave_lo = tile.g0 + rsub * 32;
 
-  // Key spans of this entry (at most 3: image prefix and two text chunks).
+  // Key spans (at most 3: image prefix and two text chunks), walked in
+  // 64-key tiles starting at the span start rounded down to 8 keys.
   int sk0[3] = {0, 0, 0}, sk1[3] = {0, 0, 0}, snt[3] = {0, 0, 0};
   int n_tiles = 0;
 #pragma unroll
@@ -334,17 +356,18 @@ void attn_step_bf16_d128_kernel(const AttnArgs a) {
       const SpanRec sp = a.spans[ent.span_begin + i];
       sk0[i] = sp.k0;
       sk1[i] = sp.k1;
-      snt[i] = (sp.k1 - sp.k0 + BN - 1) / BN;
+      snt[i] = (sp.k1 - (sp.k0 & ~7) + BN - 1) / BN;
       n_tiles += snt[i];
     }
   }
-  auto tile_at = [&](int t, int& kt, int& k1) {
-    if (t < snt[0]) { kt = sk0[0] + t * BN; k1 = sk1[0]; return; }
+  auto tile_at = [&](int t, int& kt, int& k0, int& k1) {
+    if (t < snt[0]) { k0 = sk0[0]; k1 = sk1[0]; kt = (k0 & ~7) + t * BN; return; }
     t -= snt[0];
-    if (t < snt[1]) { kt = sk0[1] + t * BN; k1 = sk1[1]; return; }
+    if (t < snt[1]) { k0 = sk0[1]; k1 = sk1[1]; kt = (k0 & ~7) + t * BN; return; }
     t -= snt[1];
-    kt = sk0[2] + t * BN;
+    k0 = sk0[2];
     k1 = sk1[2];
+    kt = (k0 & ~7) + t * BN;
   };
 
   bf16x8 qf[NQ];
@@ -361,51 +384,54 @@ void attn_step_bf16_d128_kernel(const AttnArgs a) {
     }
   }
 
-  // LDS-DMA source offsets: instruction i of this wave fills LDS rows
-  // 4c..4c+3 (c = wave*CH + i); lane l fills physical granule l%16 of row
-  // 4c + l/16, i.e. the logical granule that the row's swizzle maps there.
+  // LDS-DMA source offsets. K: instruction i of this wave fills rows 4c..4c+3
+  // (c = wave*CH + i) of 256 bytes; lane l fills physical granule l%16 of row
+  // 4c + l/16. V^T: rows are 128 bytes (64 keys of one d); instruction i
+  // fills rows 8c..8c+7, lane l physical granule l%8 of row 8c + l/8.
   const int tok_bytes = a.Hkv * D * 2;
+  const int vt_row = a.tpad * 2;
   const char* kbase = static_cast<const char*>(a.k) + int64_t(kvh) * D * 2;
-  const char* vbase = static_cast<const char*>(a.v) + int64_t(kvh) * D * 2;
+  const char* vtbase = static_cast<const char*>(a.vt) + int64_t(kvh) * D * vt_row;
+  const int vt_bytes = D * vt_row;  // one KV head's V^T block
   int kgo[CH], vgo[CH];
 #pragma unroll
   for (int i = 0; i < CH; ++i) {
-    const int row = 4 * (wave * CH + i) + (lane >> 4);
-    const int p = lane & 15;
-    kgo[i] = row * tok_bytes + 16 * (p ^ (row & 15));
-    vgo[i] = row * tok_bytes + 16 * (p ^ (4 * (row & 3)));
+    const int c = wave * CH + i;
+    const int krow = 4 * c + (lane >> 4), kp = lane & 15;
+    kgo[i] = krow * tok_bytes + 16 * (kp ^ (krow & 15));
+    const int d = 8 * c + (lane >> 3), vp = lane & 7;
+    vgo[i] = d * vt_row + 16 * (vp ^ ((d >> 1) & 7));
   }
-  auto issue = [&](int t, int kslot, int vslot) {
-    int kt, k1;
-    tile_at(t, kt, k1);
-    const int valid = min(k1 - kt, BN) * tok_bytes;
-    const int64_t off = int64_t(kt) * tok_bytes;
-    const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase + off, valid);
-    const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase + off, valid);
+  auto issue = [&](int t, char* kdst, char* vdst) {
+    int kt, k0, k1;
+    tile_at(t, kt, k0, k1);
+    const int valid = min(k1 - kt, BN) * tok_bytes;  // K rows past the span end read as 0
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase + int64_t(kt) * tok_bytes, valid);
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(vtbase + int64_t(kt) * 2, vt_bytes - kt * 2);
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          kr, (lds_void*)(smem + kslot * TILE + (wave * CH + i) * 1024), 16, kgo[i], 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          vr, (lds_void*)(smem + (2 + vslot) * TILE + (wave * CH + i) * 1024), 16, vgo[i], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(kdst + (wave * CH + i) * 1024), 16,
+                                               kgo[i], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(vdst + (wave * CH + i) * 1024), 16,
+                                               vgo[i], 0, 0, 0);
     }
   };
 
-  // K operand reads: row 32*kb + ql, logical granule 2*jj + hh.
+  // K operand: lane reads row 32*kb + sigma(ql), logical granule 2*jj + hh.
+  const int srow = (ql & ~12) | ((ql & 4) << 1) | ((ql & 8) >> 1);  // sigma: swap bits 2, 3
   int kro[NQ];
 #pragma unroll
-  for (int jj = 0; jj < NQ; ++jj) kro[jj] = ql * 256 + 16 * ((2 * jj + hh) ^ (ql & 15));
-  // V transposed reads: rows 32*kb + 16*sub + 8*half + 4*hh + trow,
-  // logical granule 4*db + gsub, byte 8*(lane & 1) inside it.
-  const int trow = (lane & 15) >> 2;
-  const int gsub = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-  int vro[ND];
+  for (int jj = 0; jj < NQ; ++jj) kro[jj] = srow * 256 + 16 * ((2 * jj + hh) ^ (srow & 15));
+  // V^T operand: lane reads row d = 32*db + ql, keys 32*kb + 16*sub + 8*hh
+  // .. +7 = logical granule 4*kb + 2*sub + hh.
+  const int vx = (ql >> 1) & 7;
+  int vro[2][2];
 #pragma unroll
-  for (int db = 0; db < ND; ++db)
-    vro[db] = (4 * hh + trow) * 256 + 16 * (4 * (db ^ trow) + gsub) + 8 * (lane & 1);
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) vro[kb][sub] = ql * 128 + 16 * ((4 * kb + 2 * sub + hh) ^ vx);
 
-  auto qk = [&](int kslot, f32x16 (&s)[2]) {
-    const char* kb0 = smem + kslot * TILE;
+  auto qk = [&](const char* kb0, f32x16 (&s)[2]) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -432,16 +458,19 @@ void attn_step_bf16_d128_kernel(const AttnArgs a) {
   const float c2 = a.scale_log2;
   const float thr = kRescaleLog2 / c2;
 
-  auto softmax_pv = [&](int t, int vslot, f32x16 (&s)[2]) {
-    int kt, k1;
-    tile_at(t, kt, k1);
-    if (kt + BN > k1 || kt + BN - 1 > wave_lo) {
+  // Softmax, first half: mask (diagonal and span-edge tiles only), row max,
+  // lazy rescale. Branches live here, before the interleaved region.
+  auto softmax_max = [&](int t, f32x16 (&s)[2]) {
+    int kt, k0, k1;
+    tile_at(t, kt, k0, k1);
+    // register r of block kb holds key kt + 32*kb + 16*(r/8) + 8*hh + r%8
+    if (kt < k0 || kt + BN > k1 || kt + BN - 1 > wave_lo) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = kt + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
-          if (key >= k1 || key > grow) s[kb][r] = -INFINITY;
+          const int key = kt + 32 * kb + 16 * (r >> 3) + 8 * hh + (r & 7);
+          if (key < k0 || key >= k1 || key > grow) s[kb][r] = -INFINITY;
         }
     }
     float mx = -INFINITY;
@@ -461,6 +490,14 @@ void attn_step_bf16_d128_kernel(const AttnArgs a) {
         for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
       m_ref = m_new;
     }
+  };
+
+  // One branch-free scheduling region: QK^T of the next tile (independent
+  // MFMAs) interleaved with the probabilities of this tile (VALU), then PV
+  // of this tile. The group barriers ask the scheduler for that order and
+  // keep each K operand read two MFMAs ahead of its use.
+  auto interleaved = [&](const char* kread, f32x16 (&sn)[2], const char* vb0, f32x16 (&s)[2]) {
+    qk(kread, sn);
     const float ms = (m_ref == -INFINITY) ? 0.f : m_ref * c2;
     bf16x8 pb[2][2];
     float rs = 0.f;
@@ -473,54 +510,66 @@ void attn_step_bf16_d128_kernel(const AttnArgs a) {
         pb[kb][r >> 3][r & 7] = (__bf16)p;
       }
     l += rs;
-    const char* vb0 = smem + (2 + vslot) * TILE;
 #pragma unroll
     for (int db = 0; db < ND; ++db)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub) {
-          const char* p0 = vb0 + vro[db] + (32 * kb + 16 * sub) * 256;
-          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0));
-          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 8 * 256));
-          const s16x8 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, both),
-                                                          pb[kb][sub], o[db], 0, 0, 0);
+          const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vb0 + db * 32 * 128 + vro[kb][sub]);
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[kb][sub], o[db], 0, 0, 0);
         }
+    // requested order: 2 K reads; 16 x {MFMA, K read, 7 VALU}; then PV with
+    // its V^T reads two ahead
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      if (i < 14) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedValu, 7, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      if (i < 14) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+    }
   };
 
-  // Pipeline (see the comment above the kernel). Iteration t: wait for
-  // tile t+1's K/V, barrier, start loading tile t+2, issue QK^T of tile t+1,
-  // then softmax and PV of tile t. Unrolled by two so score registers and K
-  // slots alternate at compile time.
+  // Pipeline (see the comment above the kernel). Step t: wait for tile
+  // t+1's K/V^T, barrier, start loading tile t+2 (K slot t%2, V slot
+  // (t+2)%3), then QK^T of tile t+1 (K slot (t+1)%2) interleaved with the
+  // softmax and PV of tile t (V slot t%3). On the last tile the QK^T reads
+  // a stale K slot and its result is unused. Unrolled by six so every slot
+  // is a compile-time choice and the two score register sets alternate.
   f32x16 sa[2], sb[2];
-  issue(0, 0, 0);
+  auto step = [&](int t, const char* kread, char* kdst, char* vdst, const char* vread,
+                  f32x16 (&sc)[2], f32x16 (&sn)[2]) {
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    if (t + 2 < n_tiles) issue(t + 2, kdst, vdst);
+    softmax_max(t, sc);
+    interleaved(kread, sn, vread, sc);
+    return t + 1 < n_tiles;
+  };
+  issue(0, k0s, v0s);
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   __syncthreads();
-  if (n_tiles > 1) issue(1, 1, 1);
-  qk(0, sa);
-  int vslot = 0;  // V slot of tile t
-  for (int t = 0; t < n_tiles; t += 2) {
-    // even step: scores of t in sa, K of t+1 in slot 1
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    __syncthreads();
-    if (t + 2 < n_tiles) issue(t + 2, 0, vslot == 0 ? 2 : vslot - 1);
-    if (t + 1 < n_tiles) qk(1, sb);
-    softmax_pv(t, vslot, sa);
-    vslot = vslot == 2 ? 0 : vslot + 1;
-    if (t + 1 >= n_tiles) break;
-    // odd step: scores of t+1 in sb, K of t+2 in slot 0
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    __syncthreads();
-    if (t + 3 < n_tiles) issue(t + 3, 1, vslot == 0 ? 2 : vslot - 1);
-    if (t + 2 < n_tiles) qk(0, sa);
-    softmax_pv(t + 1, vslot, sb);
-    vslot = vslot == 2 ? 0 : vslot + 1;
+  if (n_tiles > 1) issue(1, k1s, v1s);
+  qk(k0s, sa);
+  for (int t = 0; t < n_tiles; t += 6) {
+    if (!step(t, k1s, k0s, v2s, v0s, sa, sb)) break;
+    if (!step(t + 1, k0s, k1s, v0s, v1s, sb, sa)) break;
+    if (!step(t + 2, k1s, k0s, v1s, v2s, sa, sb)) break;
+    if (!step(t + 3, k0s, k1s, v2s, v0s, sb, sa)) break;
+    if (!step(t + 4, k1s, k0s, v0s, v1s, sa, sb)) break;
+    if (!step(t + 5, k0s, k1s, v1s, v2s, sb, sa)) break;
   }
 
   const float lt = sum_with_partner(l);
   if (!row_ok) return;
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  // O^T register r of block db holds d = 32*db + 8*(r/4) + 4*hh + r%4
   float* po = a.part_o + ((int64_t(ent.step) * a.R + lrow) * a.H + h) * D + 4 * hh;
 #pragma unroll
   for (int db = 0; db < ND; ++db)

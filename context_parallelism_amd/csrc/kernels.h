@@ -13,6 +13,8 @@ struct AttnArgs {
   const void* qr;        // gathered rank-local Q [R, H, D]
   const void* k;         // [T, Hkv, D]
   const void* v;         // [T, Hkv, D]
+  const void* vt;        // V^T [Hkv, D, tpad] (bf16, head_dim 128 only), zero past T
+  int32_t tpad;          // keys per V^T row
   float* part_o;         // [P, R, H, D] fp32, normalised per step
   float* part_lse;       // [P, H, R] fp32, natural log
   const TileRec* tiles;
@@ -27,6 +29,11 @@ struct AttnArgs {
 
 hipError_t launch_gather(const void* src, const int32_t* index, void* dst, int64_t n_rows,
                          int64_t row_bytes, hipStream_t stream);
+
+// V [T, Hkv, 128] bf16 -> V^T [Hkv, 128, tpad], zeros for keys >= T.
+// tpad: multiple of 64, >= T + 63 (every 64-key window starting below T).
+hipError_t launch_transpose_v(const void* v, void* vt, int32_t T, int32_t Hkv, int32_t tpad,
+                              hipStream_t stream);
 
 hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, int heads_per_wg, int n_entries,
                             hipStream_t stream);

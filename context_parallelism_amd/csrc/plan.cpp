@@ -168,7 +168,8 @@ void build_plan(const Meta& m, int32_t bm, int32_t bn, Plan& p) {
           int32_t k1 = std::min(rg.k1, g_hi);
           if (k1 <= rg.k0) continue;
           p.spans.push_back({rg.k0, k1});
-          cost += (int64_t(k1) - rg.k0 + bn - 1) / bn;
+          // tiles start at multiples of 8 keys (the kernels align them)
+          cost += (int64_t(k1) - (rg.k0 & ~7) + bn - 1) / bn;
         }
         e.span_end = int32_t(p.spans.size());
         if (e.span_end == e.span_begin) continue;

@@ -10,6 +10,8 @@ namespace {
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 }  // namespace
 
+int32_t vt_row_keys(int64_t seq_len) { return int32_t((seq_len + 63 + 63) / 64 * 64); }
+
 int32_t prepare_workspace(int64_t seq_len, const int32_t* n_img, const int32_t* cu_seqlens,
                           int32_t n_samples, int32_t cp_size, int32_t cp_rank, int32_t heads,
                           int32_t kv_heads, int32_t head_dim, int32_t dtype, Workspace& w) {
@@ -40,6 +42,11 @@ int32_t prepare_workspace(int64_t seq_len, const int32_t* n_img, const int32_t* 
   w.plan_bytes = off;
   w.off_qr = off;
   off = align256(off + R * size_t(heads) * head_dim * esize);
+  w.off_vt = off;
+  if (dtype == CP_DTYPE_BF16 && head_dim == 128) {
+    w.tpad = vt_row_keys(seq_len);
+    off = align256(off + size_t(kv_heads) * head_dim * size_t(w.tpad) * 2);
+  }
   w.off_po = off;
   off = align256(off + size_t(cp_size) * R * size_t(heads) * head_dim * sizeof(float));
   w.off_pl = off;

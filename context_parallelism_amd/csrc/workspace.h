@@ -3,6 +3,7 @@
 //   plan   : index int32[R], step mask uint32[R], tiles, entries, spans
 //            (uploaded from the host in one copy);
 //   qr     : gathered rank-local Q rows [R, H, D] in the input dtype;
+//   vt     : V^T [Hkv, D, tpad] (bf16 with head_dim 128 only; else empty);
 //   part_o : per-step partial outputs fp32 [P, R, H, D];
 //   part_l : per-step log-sum-exps fp32 [P, H, R].
 #pragma once
@@ -21,13 +22,18 @@ struct Workspace {
   int32_t heads = 0, kv_heads = 0, head_dim = 0, dtype = 0;
   size_t off_index = 0, off_mask = 0, off_tiles = 0, off_entries = 0, off_spans = 0;
   size_t plan_bytes = 0;
-  size_t off_qr = 0, off_po = 0, off_pl = 0, total = 0;
+  size_t off_qr = 0, off_vt = 0, off_po = 0, off_pl = 0, total = 0;
+  int32_t tpad = 0;  // keys per V^T row (0: no V^T region)
 };
 
 // Checks every argument, builds the plan and the layout. Returns a cp_status.
 int32_t prepare_workspace(int64_t seq_len, const int32_t* n_img, const int32_t* cu_seqlens,
                           int32_t n_samples, int32_t cp_size, int32_t cp_rank, int32_t heads,
                           int32_t kv_heads, int32_t head_dim, int32_t dtype, Workspace& w);
+
+// Keys per V^T row: a multiple of 64 that covers every 64-key window
+// starting below seq_len.
+int32_t vt_row_keys(int64_t seq_len);
 
 // Writes the plan region (w.plan_bytes bytes) into dst.
 void pack_plan(const Workspace& w, uint8_t* dst);

@@ -110,7 +110,7 @@ def test_workspace_size_grows_with_problem(cp):
     a = cp.workspace_size(1000, cp_size=2, cp_rank=0, heads=4, kv_heads=4, head_dim=128, dtype=1)
     b = cp.workspace_size(2000, cp_size=2, cp_rank=0, heads=4, kv_heads=4, head_dim=128, dtype=1)
     c = cp.workspace_size(1000, cp_size=2, cp_rank=0, heads=4, kv_heads=4, head_dim=128, dtype=0)
-    assert 0 < a < b and a < c and a % 256 == 0
+    assert 0 < a < b and 0 < c and a % 256 == 0 and c % 256 == 0
 
 
 # ------------------------------------------------------------------ errors
