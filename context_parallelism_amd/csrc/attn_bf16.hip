@@ -293,9 +293,10 @@ void attn_step_bf16_kernel(const AttnArgs a) {
 // head_dim 128: software-pipelined variant.
 //
 // Differences from the kernel above:
-//  * V is read from a V^T copy (vt[g][d][key], made once per call), so the
-//    PV operand needs no transposing read: each lane's 8 keys at one d are
-//    16 contiguous bytes, read with ds_read_b128 like K.
+//  * V is read from a V^T copy made once per call, blocked by 8 keys
+//    (vt[g][key/8][d][key%8]), so the PV operand needs no transposing
+//    read: each lane's 8 keys at one d are 16 contiguous bytes, read with
+//    ds_read_b128 like K, and a 64-key tile is one contiguous 16 KiB run.
 //  * Lane ql of the QK^T operand reads K row sigma(ql), sigma swapping bits
 //    2 and 3 of the row index. The S^T accumulator register t of lane half
 //    hh then holds key 16*(t/8) + 8*hh + t%8: eight consecutive keys per
@@ -386,13 +387,14 @@ void attn_step_bf16_d128_kernel(const AttnArgs a) {
 
   // LDS-DMA source offsets. K: instruction i of this wave fills rows 4c..4c+3
   // (c = wave*CH + i) of 256 bytes; lane l fills physical granule l%16 of row
-  // 4c + l/16. V^T: rows are 128 bytes (64 keys of one d); instruction i
-  // fills rows 8c..8c+7, lane l physical granule l%8 of row 8c + l/8.
+  // 4c + l/16. V^T in LDS: rows are 128 bytes (64 keys of one d);
+  // instruction i fills rows 8c..8c+7, lane l physical granule l%8 of row
+  // 8c + l/8, reading the 16 bytes of key block l%8 at that d.
   const int tok_bytes = a.Hkv * D * 2;
-  const int vt_row = a.tpad * 2;
   const char* kbase = static_cast<const char*>(a.k) + int64_t(kvh) * D * 2;
-  const char* vtbase = static_cast<const char*>(a.vt) + int64_t(kvh) * D * vt_row;
-  const int vt_bytes = D * vt_row;  // one KV head's V^T block
+  // V^T: 8-key blocks of 128 d-rows (16 bytes each); a tile at kt is the
+  // contiguous 16 KiB starting at key block kt / 8
+  const char* vtbase = static_cast<const char*>(a.vt) + int64_t(kvh) * a.tpad * D * 2;
   int kgo[CH], vgo[CH];
 #pragma unroll
   for (int i = 0; i < CH; ++i) {
@@ -400,14 +402,14 @@ void attn_step_bf16_d128_kernel(const AttnArgs a) {
     const int krow = 4 * c + (lane >> 4), kp = lane & 15;
     kgo[i] = krow * tok_bytes + 16 * (kp ^ (krow & 15));
     const int d = 8 * c + (lane >> 3), vp = lane & 7;
-    vgo[i] = d * vt_row + 16 * (vp ^ ((d >> 1) & 7));
+    vgo[i] = (vp ^ ((d >> 1) & 7)) * (D * 16) + d * 16;
   }
   auto issue = [&](int t, char* kdst, char* vdst) {
     int kt, k0, k1;
     tile_at(t, kt, k0, k1);
     const int valid = min(k1 - kt, BN) * tok_bytes;  // K rows past the span end read as 0
     const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase + int64_t(kt) * tok_bytes, valid);
-    const __amdgpu_buffer_rsrc_t vr = make_rsrc(vtbase + int64_t(kt) * 2, vt_bytes - kt * 2);
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(vtbase + int64_t(kt) * D * 2, (a.tpad - kt) * D * 2);
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(kdst + (wave * CH + i) * 1024), 16,

@@ -37,7 +37,7 @@ hipError_t stage_and_upload(const Workspace& w, void* dst, hipStream_t stream) {
     s.pending = false;
   }
   if (s.copied != nullptr && s.device != dev) {
-    hipEventDestroy(s.copied);
+    (void)hipEventDestroy(s.copied);
     s.copied = nullptr;
   }
   if (s.copied == nullptr) {
@@ -46,7 +46,7 @@ hipError_t stage_and_upload(const Workspace& w, void* dst, hipStream_t stream) {
     s.device = dev;
   }
   if (s.cap < w.plan_bytes) {
-    if (s.host) hipHostFree(s.host);
+    if (s.host) (void)hipHostFree(s.host);
     s.host = nullptr;
     s.cap = 0;
     size_t cap = w.plan_bytes < (size_t(1) << 20) ? (size_t(1) << 20) : w.plan_bytes * 2;

@@ -11,10 +11,11 @@
 
 namespace cpattn {
 
-TileShape tile_shape(int32_t dtype, int32_t group) {
+TileShape tile_shape(int32_t dtype, int32_t group, int32_t head_dim) {
   if (dtype != CP_DTYPE_BF16) return {kF32RowsPerTile, 1};
   const int32_t hpw = (group % 4 == 0) ? 4 : (group % 2 == 0) ? 2 : 1;
-  return {32 * kBf16Waves / hpw, hpw};
+  const int32_t waves = head_dim == 128 ? kBf16WavesD128 : kBf16Waves;
+  return {32 * waves / hpw, hpw};
 }
 
 int32_t build_meta(int64_t seq_len, const int32_t* n_img, const int32_t* cu_seqlens,

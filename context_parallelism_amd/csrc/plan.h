@@ -29,10 +29,12 @@ struct Segment {
 };
 
 // Tile shapes of the attention kernels. Each bf16 wave owns 32 query rows
-// of one head and a bf16 workgroup has kBf16Waves waves; K/V stream through
-// LDS kBlockN keys at a time.
+// of one head; a bf16 workgroup has kBf16Waves (head_dim 64) or
+// kBf16WavesD128 (head_dim 128) waves; K/V stream through LDS kBlockN keys
+// at a time.
 constexpr int kBlockN = 64;
 constexpr int kBf16Waves = 4;
+constexpr int kBf16WavesD128 = 4;
 constexpr int kF32RowsPerTile = 64;
 
 struct TileShape {
@@ -41,8 +43,8 @@ struct TileShape {
 };
 
 // bf16 (dtype 1): heads_per_wg = largest of 4, 2, 1 dividing heads/kv_heads,
-// rows = 32 * kBf16Waves / heads_per_wg. fp32: one head, kF32RowsPerTile.
-TileShape tile_shape(int32_t dtype, int32_t group);
+// rows = 32 * waves / heads_per_wg. fp32: one head, kF32RowsPerTile.
+TileShape tile_shape(int32_t dtype, int32_t group, int32_t head_dim);
 
 struct Meta {
   int64_t seq_len = 0;

@@ -2,10 +2,13 @@
 //
 // The attention kernel contracts P against V over keys. A matrix-core
 // operand needs its reduction index (here: keys) contiguous in each lane, so
-// the kernel reads V^T: vt[g][d][key], keys fastest, each (g, d) row padded
-// to tpad keys with zeros past seq_len. One workgroup moves a 64-key x 128-d
-// block of one KV head: it reads 64 rows of 256 contiguous bytes, turns the
-// block around in LDS and writes 128 rows of 128 contiguous bytes.
+// the kernel reads V^T. Layout, per KV head g: blocks of 8 keys, each block
+// holding all 128 d-rows of its 8 keys: vt[g][key / 8][d][key % 8], padded
+// to tpad keys with zeros past seq_len. Any 64-key window starting at a
+// multiple of 8 keys is then one contiguous 16 KiB run, which the attention
+// kernel copies into LDS with long sequential reads. One workgroup moves a
+// 64-key x 128-d block of one KV head: it reads 64 rows of 256 contiguous
+// bytes, turns the block around in LDS and writes 16 KiB contiguously.
 // HBM-bound; runs once per call, before the attention kernel.
 #include "kernels.h"
 
@@ -39,11 +42,12 @@ __global__ __launch_bounds__(256) void transpose_v_kernel(const unsigned short* 
     dst[3] = val.w;
   }
   __syncthreads();
-  // 128 rows (d) x 8 pieces of 8 keys
+  // 8 key groups x 128 d-rows of 8 keys; consecutive lanes take
+  // consecutive d, so each wavefront writes 1 KiB contiguously
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int q = tid + 256 * i;
-    const int d = q >> 3, kc = q & 7;
+    const int d = q & (kD - 1), kc = q >> 7;
     unsigned w[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -51,7 +55,7 @@ __global__ __launch_bounds__(256) void transpose_v_kernel(const unsigned short* 
       const unsigned hi = tile[(8 * kc + 2 * e + 1) * kStride + d];
       w[e] = lo | (hi << 16);
     }
-    *reinterpret_cast<uint4*>(vt + (int64_t(g) * kD + d) * tpad + t0 + 8 * kc) =
+    *reinterpret_cast<uint4*>(vt + ((int64_t(g) * (tpad / 8) + t0 / 8 + kc) * kD + d) * 8) =
         make_uint4(w[0], w[1], w[2], w[3]);
   }
 }

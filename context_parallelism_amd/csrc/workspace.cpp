@@ -24,7 +24,7 @@ int32_t prepare_workspace(int64_t seq_len, const int32_t* n_img, const int32_t* 
   w.kv_heads = kv_heads;
   w.head_dim = head_dim;
   w.dtype = dtype;
-  w.shape = tile_shape(dtype, heads / kv_heads);
+  w.shape = tile_shape(dtype, heads / kv_heads, head_dim);
   build_plan(w.meta, w.shape.rows, kBlockN, w.plan);
   const size_t R = size_t(w.meta.rows);
   const size_t esize = dtype == CP_DTYPE_BF16 ? 2 : 4;
