@@ -142,7 +142,7 @@ def main():
     events = []
     for _ in range(K):
         evs = []
-        for _ in range(5):
+        for _ in range(6):
             e = ctypes.c_void_p()
             assert hip.hipEventCreate(ctypes.byref(e)) == 0
             evs.append(e.value)
@@ -162,15 +162,15 @@ def main():
         assert hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b)) == 0
         return ms.value
 
-    stage = np.array([[elapsed(e[j], e[j + 1]) for j in range(4)] for e in events])  # ms
-    call = np.array([elapsed(e[0], e[4]) for e in events])
+    stage = np.array([[elapsed(e[j], e[j + 1]) for j in range(5)] for e in events])  # ms
+    call = np.array([elapsed(e[0], e[5]) for e in events])
     for evs in events:
         for e in evs:
             hip.hipEventDestroy(ctypes.c_void_p(e))
 
     ms_per_step = wall / K * 1e3
     value = useful / (wall / K) / 1e12
-    attn_ms = float(stage[:, 2].mean())
+    attn_ms = float(stage[:, 3].mean())
     achieved = useful / (attn_ms * 1e-3) / 1e12
     R = ra.R
     esize = 2 if w.dtype == "bf16" else 4
@@ -195,8 +195,9 @@ def main():
         "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "stages_ms": {"plan_upload": round(float(stage[:, 0].mean()), 4),
                       "gather": round(float(stage[:, 1].mean()), 4),
+                      "v_relayout": round(float(stage[:, 2].mean()), 4),
                       "attention": round(attn_ms, 4),
-                      "merge": round(float(stage[:, 3].mean()), 4),
+                      "merge": round(float(stage[:, 4].mean()), 4),
                       "call_median": round(float(np.median(call)), 4),
                       "call_p10": round(float(np.percentile(call, 10)), 4),
                       "call_p90": round(float(np.percentile(call, 90)), 4)},
@@ -204,7 +205,8 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic_from_profile(),
-                     "kernel": "attn_step_bf16_kernel (per-step attention, all ring steps, one launch)"},
+                     "kernel": ("attn_step_bf16_d128_kernel" if w.head_dim == 128 else "attn_step_bf16_kernel")
+                               + " (per-step attention, all ring steps, one launch)"},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, q, k, v, n_img, cu, args.cpu_seconds)

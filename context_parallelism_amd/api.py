@@ -129,7 +129,7 @@ class RankAttention:
         self.workspace = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=dev)
 
     def __call__(self, events=None):
-        """Run the forward. ``events``: optional sequence of five raw
+        """Run the forward. ``events``: optional sequence of six raw
         hipEvent_t handles recorded at the stage boundaries
         (cp_attn_rank_fwd_timed)."""
         args = (self.q.data_ptr(), self.k.data_ptr(), self.v.data_ptr(), self.dtype, self.T,
@@ -139,7 +139,9 @@ class RankAttention:
         if events is None:
             check(_lib.cp_attn_rank_fwd(*args), "cp_attn_rank_fwd")
         else:
-            ev = (ctypes.c_void_p * 5)(*[ctypes.c_void_p(int(e)) for e in events])
+            if len(events) != 6:
+                raise ValueError("cp_attn_rank_fwd_timed records exactly six events")
+            ev = (ctypes.c_void_p * 6)(*[ctypes.c_void_p(int(e)) for e in events])
             check(_lib.cp_attn_rank_fwd_timed(*args, ev), "cp_attn_rank_fwd_timed")
         return self.out, self.lse
 

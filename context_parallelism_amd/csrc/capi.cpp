@@ -106,6 +106,7 @@ cp_status rank_fwd(const void* q, const void* k, const void* v, int32_t dtype, i
         return CP_EHIP;
       a.vt = ws + w.off_vt;
     }
+    if (mark(events, 3, s) != hipSuccess) return CP_EHIP;
     a.qr = ws + w.off_qr;
     a.k = k;
     a.v = v;
@@ -126,13 +127,13 @@ cp_status rank_fwd(const void* q, const void* k, const void* v, int32_t dtype, i
                        ? launch_attn_bf16(a, head_dim, w.shape.heads_per_wg, n_entries, s)
                        : launch_attn_f32(a, head_dim, n_entries, s);
     if (e != hipSuccess) return CP_EHIP;
-    if (mark(events, 3, s) != hipSuccess) return CP_EHIP;
+    if (mark(events, 4, s) != hipSuccess) return CP_EHIP;
 
     const uint32_t* mask = reinterpret_cast<const uint32_t*>(ws + w.off_mask);
     if (launch_lse_merge(a.part_o, a.part_lse, mask, cp_size, R, heads, head_dim, dtype, out, lse, s) !=
         hipSuccess)
       return CP_EHIP;
-    if (mark(events, 4, s) != hipSuccess) return CP_EHIP;
+    if (mark(events, 5, s) != hipSuccess) return CP_EHIP;
     return CP_OK;
   } catch (const std::exception&) {
     return CP_EINVAL;

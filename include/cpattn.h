@@ -154,10 +154,11 @@ cp_status cp_attn_rank_fwd(const void *q, const void *k, const void *v, int32_t 
                            void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * cp_attn_rank_fwd_timed -- cp_attn_rank_fwd that also records five
+ * cp_attn_rank_fwd_timed -- cp_attn_rank_fwd that also records six
  * caller-created hipEvent_t on `stream` at its stage boundaries:
  * events[0] before the plan upload, [1] after it, [2] after the gather,
- * [3] after the per-step attention, [4] after the merge. A caller can then
+ * [3] after the V relayout (bf16, head_dim 128; otherwise right after [2]),
+ * [4] after the per-step attention, [5] after the merge. A caller can then
  * time one stage with hipEventElapsedTime, without a profiler. events may
  * be NULL (then this is exactly cp_attn_rank_fwd). The library does not
  * keep the events.
