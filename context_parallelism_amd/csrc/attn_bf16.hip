@@ -52,10 +52,11 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int kBufferWord3 = 0x00020000;  // raw buffer access, gfx9 family
 constexpr float kRescaleLog2 = 8.0f;      // lazy-rescale threshold (exp2 domain)
+constexpr int kLdsAhead = 6;             // LDS operand reads issued ahead of their MFMA
 constexpr int kWaitVmcnt0 = 0x0F70;       // s_waitcnt vmcnt(0), expcnt and lgkmcnt untouched
 // __builtin_amdgcn_sched_group_barrier instruction classes
-constexpr int kSchedValu = 0x0002;
 constexpr int kSchedMfma = 0x0008;
+constexpr int kSchedVmemRead = 0x0020;
 constexpr int kSchedDsRead = 0x0100;
 
 // Our value combined with that of lane ^ 32: the swap puts lanes 0-31 of
@@ -290,7 +291,13 @@ void attn_step_bf16_kernel(const AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// head_dim 128: software-pipelined variant.
+// head_dim 128: ping-pong variant.
+//
+// Work: one workgroup of 8 waves per (row tile, ring step, head group)
+// entry. Waves w and w+4 share a SIMD; waves 0-3 form group 0 and waves
+// 4-7 group 1. Each wave owns 32 query rows of one head; with G query heads
+// per KV head (G = 4, 2, 1) a group covers 4/G row blocks of G heads, so the
+// workgroup's 8 waves share every K/V tile.
 //
 // Differences from the kernel above:
 //  * V is read from a V^T copy made once per call, blocked by 8 keys
@@ -298,8 +305,8 @@ void attn_step_bf16_kernel(const AttnArgs a) {
 //    read: each lane's 8 keys at one d are 16 contiguous bytes, read with
 //    ds_read_b128 like K, and a 64-key tile is one contiguous 16 KiB run.
 //  * Lane ql of the QK^T operand reads K row sigma(ql), sigma swapping bits
-//    2 and 3 of the row index. The S^T accumulator register t of lane half
-//    hh then holds key 16*(t/8) + 8*hh + t%8: eight consecutive keys per
+//    2 and 3 of the row index. The S^T accumulator register r of lane half
+//    hh then holds key 16*(r/8) + 8*hh + r%8: eight consecutive keys per
 //    MFMA operand, exactly the keys of the lane's contiguous V^T read.
 //  * K and V^T tiles go from HBM straight into LDS (buffer_load ... lds),
 //    no staging registers. One wave instruction fills 1 KiB of LDS (lane l
@@ -311,34 +318,47 @@ void attn_step_bf16_kernel(const AttnArgs a) {
 //    addresses are per-lane constants plus immediates.
 //  * Key tiles start at multiples of 8 keys so V^T rows load 16-byte
 //    aligned; keys below the span start are masked like those past its end.
-//  * K runs one tile ahead of V: while the softmax of tile t runs on VALU,
-//    the QK^T MFMAs of tile t+1 are already issued, so matrix and vector
-//    work overlap inside one wave. K is double-buffered and V
-//    triple-buffered, so each tile needs a single barrier.
+//  * Ping-pong: each wave alternates a softmax phase (VALU: exp, sum,
+//    convert) and a matrix phase (MFMA: PV of tile t, QK^T of tile t+1).
+//    Group 1 runs one phase behind group 0 and every phase ends at a
+//    workgroup barrier, so on each SIMD one wave keeps the matrix core busy
+//    while its partner does the vector work.
+//  * Matrix phases read each MFMA operand from LDS kLdsAhead MFMAs ahead,
+//    which hides LDS latency under load; group 0 spreads the next tile's
+//    LDS-DMA loads over its matrix phase, one every four MFMAs, so the
+//    memory queue never stalls the matrix work.
+//  * Masks of diagonal and span-edge tiles are built as a 64-bit lane mask
+//    and applied with bitfield selects, keeping scalar registers free.
+// Scalar walk over an entry's 64-key tiles: up to three key spans, each
+// walked from its start rounded down to 8 keys. Holds the current tile
+// start kt and its span's [k0, k1).
+struct TileCursor {
+  int kt, k0, k1, span;
+};
+
 template <int G>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_step_bf16_d128_kernel(const AttnArgs a) {
-  constexpr int D = 128, BN = kBlockN, NW = 4;
+  constexpr int D = 128, BN = kBlockN;
   constexpr int TILE = BN * D * 2;           // bytes of one K (or V^T) tile
-  constexpr int CH = TILE / 1024 / NW;       // LDS-DMA instructions per wave per tensor
+  constexpr int CH = TILE / 1024 / 4;        // LDS-DMA instructions per loading wave per tensor
   constexpr int ND = D / 32, NQ = D / 16;
+  constexpr int RB = 4 / G;                  // row blocks per wave group
   static_assert(BN == 64, "tile walk assumes 64-key tiles");
-  // Separate arrays per buffer, each chosen at compile time in the unrolled
-  // loop, so the compiler can tell an in-flight LDS-DMA target from the
-  // buffers being read and waits only where they alias.
   __shared__ __attribute__((aligned(1024))) char k0s[TILE];
   __shared__ __attribute__((aligned(1024))) char k1s[TILE];
   __shared__ __attribute__((aligned(1024))) char v0s[TILE];
   __shared__ __attribute__((aligned(1024))) char v1s[TILE];
-  __shared__ __attribute__((aligned(1024))) char v2s[TILE];
   typedef __attribute__((address_space(3))) void lds_void;
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
+  const int grp = wave >> 2, wg = wave & 3;  // waves w and w+4 share a SIMD
   const int hg = blockIdx.x % a.n_hg;
   const EntryRec ent = a.entries[blockIdx.x / a.n_hg];
   const TileRec tile = a.tiles[ent.tile];
-  const int h = hg * G + (wave % G);
-  const int rsub = wave / G;
+  const int h = hg * G + (wg % G);
+  const int rsub = grp * RB + wg / G;
   const int kvh = (hg * G) / a.group;
   const int ql = lane & 31, hh = lane >> 5;
   const int rin = rsub * 32 + ql;
@@ -346,29 +366,30 @@ void attn_step_bf16_d128_kernel(const AttnArgs a) {
   const int lrow = tile.local0 + rin;
   const int grow = tile.g0 + rin;
   const int wave_lo = tile.g0 + rsub * 32;
+  const int n_spans = ent.span_end - ent.span_begin;
+  const SpanRec* spans = a.spans + ent.span_begin;
+  // output addresses (per lane), formed now so the arguments they come
+  // from need not stay live through the main loop
+  float* const po = a.part_o + ((int64_t(ent.step) * a.R + lrow) * a.H + h) * D + 4 * hh;
+  float* const pl = a.part_lse + (int64_t(ent.step) * a.H + h) * a.R + lrow;
+  const float lse_scale = a.scale;
 
-  // Key spans (at most 3: image prefix and two text chunks), walked in
-  // 64-key tiles starting at the span start rounded down to 8 keys.
-  int sk0[3] = {0, 0, 0}, sk1[3] = {0, 0, 0}, snt[3] = {0, 0, 0};
   int n_tiles = 0;
-#pragma unroll
-  for (int i = 0; i < 3; ++i) {
-    if (ent.span_begin + i < ent.span_end) {
-      const SpanRec sp = a.spans[ent.span_begin + i];
-      sk0[i] = sp.k0;
-      sk1[i] = sp.k1;
-      snt[i] = (sp.k1 - (sp.k0 & ~7) + BN - 1) / BN;
-      n_tiles += snt[i];
+  for (int i = 0; i < n_spans; ++i) n_tiles += (spans[i].k1 - (spans[i].k0 & ~7) + BN - 1) / BN;
+  auto start = [&](TileCursor& c) {
+    c.span = 0;
+    c.k0 = spans[0].k0;
+    c.k1 = spans[0].k1;
+    c.kt = c.k0 & ~7;
+  };
+  auto advance = [&](TileCursor& c) {
+    c.kt += BN;
+    if (c.kt >= c.k1 && c.span + 1 < n_spans) {
+      ++c.span;
+      c.k0 = spans[c.span].k0;
+      c.k1 = spans[c.span].k1;
+      c.kt = c.k0 & ~7;
     }
-  }
-  auto tile_at = [&](int t, int& kt, int& k0, int& k1) {
-    if (t < snt[0]) { k0 = sk0[0]; k1 = sk1[0]; kt = (k0 & ~7) + t * BN; return; }
-    t -= snt[0];
-    if (t < snt[1]) { k0 = sk0[1]; k1 = sk1[1]; kt = (k0 & ~7) + t * BN; return; }
-    t -= snt[1];
-    k0 = sk0[2];
-    k1 = sk1[2];
-    kt = (k0 & ~7) + t * BN;
   };
 
   bf16x8 qf[NQ];
@@ -385,47 +406,42 @@ void attn_step_bf16_d128_kernel(const AttnArgs a) {
     }
   }
 
-  // LDS-DMA source offsets. K: instruction i of this wave fills rows 4c..4c+3
-  // (c = wave*CH + i) of 256 bytes; lane l fills physical granule l%16 of row
-  // 4c + l/16. V^T in LDS: rows are 128 bytes (64 keys of one d);
-  // instruction i fills rows 8c..8c+7, lane l physical granule l%8 of row
-  // 8c + l/8, reading the 16 bytes of key block l%8 at that d.
+  // Loads are issued by the four waves of group 0 only (they are in their
+  // matrix phase when loads start). Wave wg fills 1-KiB pieces wg*CH..+CH-1.
   const int tok_bytes = a.Hkv * D * 2;
-  const char* kbase = static_cast<const char*>(a.k) + int64_t(kvh) * D * 2;
+    const char* kbase = static_cast<const char*>(a.k) + int64_t(kvh) * D * 2;
   // V^T: 8-key blocks of 128 d-rows (16 bytes each); a tile at kt is the
   // contiguous 16 KiB starting at key block kt / 8
   const char* vtbase = static_cast<const char*>(a.vt) + int64_t(kvh) * a.tpad * D * 2;
   int kgo[CH], vgo[CH];
 #pragma unroll
   for (int i = 0; i < CH; ++i) {
-    const int c = wave * CH + i;
+    const int c = wg * CH + i;
     const int krow = 4 * c + (lane >> 4), kp = lane & 15;
     kgo[i] = krow * tok_bytes + 16 * (kp ^ (krow & 15));
     const int d = 8 * c + (lane >> 3), vp = lane & 7;
     vgo[i] = (vp ^ ((d >> 1) & 7)) * (D * 16) + d * 16;
   }
-  auto issue = [&](int t, char* kdst, char* vdst) {
-    int kt, k0, k1;
-    tile_at(t, kt, k0, k1);
-    const int valid = min(k1 - kt, BN) * tok_bytes;  // K rows past the span end read as 0
-    const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase + int64_t(kt) * tok_bytes, valid);
-    const __amdgpu_buffer_rsrc_t vr = make_rsrc(vtbase + int64_t(kt) * D * 2, (a.tpad - kt) * D * 2);
+  auto issue_k = [&](const TileCursor& c, char* dst) {
+    const int valid = min(c.k1 - c.kt, BN) * tok_bytes;
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(kbase + int64_t(c.kt) * tok_bytes, valid);
 #pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(kdst + (wave * CH + i) * 1024), 16,
+    for (int i = 0; i < CH; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + (wg * CH + i) * 1024), 16,
                                                kgo[i], 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(vdst + (wave * CH + i) * 1024), 16,
+  };
+  auto issue_v = [&](const TileCursor& c, char* dst) {
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(vtbase + int64_t(c.kt) * D * 2, (a.tpad - c.kt) * D * 2);
+#pragma unroll
+    for (int i = 0; i < CH; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + (wg * CH + i) * 1024), 16,
                                                vgo[i], 0, 0, 0);
-    }
   };
 
-  // K operand: lane reads row 32*kb + sigma(ql), logical granule 2*jj + hh.
-  const int srow = (ql & ~12) | ((ql & 4) << 1) | ((ql & 8) >> 1);  // sigma: swap bits 2, 3
+  const int srow = (ql & ~12) | ((ql & 4) << 1) | ((ql & 8) >> 1);
   int kro[NQ];
 #pragma unroll
   for (int jj = 0; jj < NQ; ++jj) kro[jj] = srow * 256 + 16 * ((2 * jj + hh) ^ (srow & 15));
-  // V^T operand: lane reads row d = 32*db + ql, keys 32*kb + 16*sub + 8*hh
-  // .. +7 = logical granule 4*kb + 2*sub + hh.
   const int vx = (ql >> 1) & 7;
   int vro[2][2];
 #pragma unroll
@@ -433,7 +449,17 @@ void attn_step_bf16_d128_kernel(const AttnArgs a) {
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) vro[kb][sub] = ql * 128 + 16 * ((4 * kb + 2 * sub + hh) ^ vx);
 
-  auto qk = [&](const char* kb0, f32x16 (&s)[2]) {
+  f32x16 sc[2];     // scores of the tile whose softmax is next
+  bf16x8 pb[2][2];  // probabilities of the tile whose PV is next
+  f32x16 o[ND];
+#pragma unroll
+  for (int db = 0; db < ND; ++db)
+#pragma unroll
+    for (int t = 0; t < 16; ++t) o[db][t] = 0.f;
+  float m_ref = -INFINITY, l = 0.f;
+  const float c2 = a.scale_log2;
+
+  auto qk = [&](const char* kb0) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -443,75 +469,14 @@ void attn_step_bf16_d128_kernel(const AttnArgs a) {
           f32x16 z;
 #pragma unroll
           for (int t = 0; t < 16; ++t) z[t] = 0.f;
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[jj], z, 0, 0, 0);
+          sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[jj], z, 0, 0, 0);
         } else {
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[jj], s[kb], 0, 0, 0);
+          sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[jj], sc[kb], 0, 0, 0);
         }
       }
     }
   };
-
-  f32x16 o[ND];
-#pragma unroll
-  for (int db = 0; db < ND; ++db)
-#pragma unroll
-    for (int t = 0; t < 16; ++t) o[db][t] = 0.f;
-  float m_ref = -INFINITY, l = 0.f;
-  const float c2 = a.scale_log2;
-  const float thr = kRescaleLog2 / c2;
-
-  // Softmax, first half: mask (diagonal and span-edge tiles only), row max,
-  // lazy rescale. Branches live here, before the interleaved region.
-  auto softmax_max = [&](int t, f32x16 (&s)[2]) {
-    int kt, k0, k1;
-    tile_at(t, kt, k0, k1);
-    // register r of block kb holds key kt + 32*kb + 16*(r/8) + 8*hh + r%8
-    if (kt < k0 || kt + BN > k1 || kt + BN - 1 > wave_lo) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kt + 32 * kb + 16 * (r >> 3) + 8 * hh + (r & 7);
-          if (key < k0 || key >= k1 || key > grow) s[kb][r] = -INFINITY;
-        }
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = max_with_partner(mx);
-    const bool grow_ref = mx > m_ref + thr;
-    if (__builtin_amdgcn_ballot_w64(grow_ref) != 0) {
-      const float m_new = grow_ref ? mx : m_ref;
-      const float alpha = __builtin_amdgcn_exp2f((m_ref - m_new) * c2);
-      l *= alpha;
-#pragma unroll
-      for (int db = 0; db < ND; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-      m_ref = m_new;
-    }
-  };
-
-  // One branch-free scheduling region: QK^T of the next tile (independent
-  // MFMAs) interleaved with the probabilities of this tile (VALU), then PV
-  // of this tile. The group barriers ask the scheduler for that order and
-  // keep each K operand read two MFMAs ahead of its use.
-  auto interleaved = [&](const char* kread, f32x16 (&sn)[2], const char* vb0, f32x16 (&s)[2]) {
-    qk(kread, sn);
-    const float ms = (m_ref == -INFINITY) ? 0.f : m_ref * c2;
-    bf16x8 pb[2][2];
-    float rs = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c2, -ms));
-        rs += p;
-        pb[kb][r >> 3][r & 7] = (__bf16)p;
-      }
-    l += rs;
+  auto pv = [&](const char* vb0) {
 #pragma unroll
     for (int db = 0; db < ND; ++db)
 #pragma unroll
@@ -521,58 +486,233 @@ void attn_step_bf16_d128_kernel(const AttnArgs a) {
           const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vb0 + db * 32 * 128 + vro[kb][sub]);
           o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[kb][sub], o[db], 0, 0, 0);
         }
-    // requested order: 2 K reads; 16 x {MFMA, K read, 7 VALU}; then PV with
-    // its V^T reads two ahead
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+  };
+  // Register fences: an empty asm that "reads and writes" the values forces
+  // the work producing them to stay before it (barriers order memory only,
+  // so arithmetic could otherwise drift into the next phase).
+  auto fence_p = [&]() {
+    asm volatile("" : "+v"(pb[0][0]), "+v"(pb[0][1]), "+v"(pb[1][0]), "+v"(pb[1][1]), "+v"(l), "+v"(m_ref));
+  };
+  auto fence_s = [&]() {
+    asm volatile("" : "+v"(sc[0]), "+v"(sc[1]));
+    asm volatile("" : "+v"(o[0]), "+v"(o[1]), "+v"(o[2]), "+v"(o[3]));
+  };
+  // Softmax phase. Probabilities are exp2((s - m_ref) * c2): any reference
+  // works while the values stay finite, since the output and the sum share
+  // it. The common path computes them against the current reference; only
+  // if a row's partial sum exceeds 2^64 (or the row has no reference yet)
+  // does the slow path compute the row max, move the reference there,
+  // rescale the output and the sum, and recompute.
+  auto probs = [&](float& rs) {
+    const float ms = (m_ref == -INFINITY) ? 0.f : m_ref * c2;
+    rs = 0.f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-      if (i < 14) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedValu, 7, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-      if (i < 14) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][r], c2, -ms));
+        rs += p;
+        pb[kb][r >> 3][r & 7] = (__bf16)p;
+      }
+  };
+  auto softmax = [&](const TileCursor& c) {
+    if (c.kt < c.k0 || c.kt + BN > c.k1 || c.kt + BN - 1 > wave_lo) {
+      // Keys of this lane sit at offsets 32kb + 16(r>>3) + (r&7) from
+      // kt + 8hh; the visible ones form the range [lo, hi). Build that range
+      // as a 64-bit lane mask and select with bitfield ops, so no per-key
+      // compare results occupy scalar registers.
+      const int base = c.kt + 8 * hh;
+      const int lo = min(max(c.k0 - base, 0), 64);
+      const int hi = min(max(min(c.k1, grow + 1) - base, 0), 64);
+      const uint64_t below_hi = hi >= 64 ? ~0ull : (1ull << hi) - 1;
+      const uint64_t below_lo = lo >= 64 ? ~0ull : (1ull << lo) - 1;
+      const uint64_t vis = below_hi & ~below_lo;
+      const int w0 = int(uint32_t(vis)), w1 = int(uint32_t(vis >> 32));
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = __builtin_amdgcn_sbfe(kb ? w1 : w0, 16 * (r >> 3) + (r & 7), 1);
+          float y;
+          asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(y) : "v"(m), "v"(sc[kb][r]), "v"(-INFINITY));
+          sc[kb][r] = y;
+        }
     }
+    float rs;
+    probs(rs);
+    const bool redo = (m_ref == -INFINITY) || !(rs <= 0x1p64f);  // also catches NaN
+    if (__builtin_amdgcn_ballot_w64(redo) != 0) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
+      mx = max_with_partner(mx);
+      const float m_new = fmaxf(m_ref, mx);
+      const float alpha = __builtin_amdgcn_exp2f((m_ref - m_new) * c2);  // 0 if m_ref = -inf
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < ND; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+      m_ref = m_new;
+      probs(rs);
+    }
+    l += rs;
   };
 
-  // Pipeline (see the comment above the kernel). Step t: wait for tile
-  // t+1's K/V^T, barrier, start loading tile t+2 (K slot t%2, V slot
-  // (t+2)%3), then QK^T of tile t+1 (K slot (t+1)%2) interleaved with the
-  // softmax and PV of tile t (V slot t%3). On the last tile the QK^T reads
-  // a stale K slot and its result is unused. Unrolled by six so every slot
-  // is a compile-time choice and the two score register sets alternate.
-  f32x16 sa[2], sb[2];
-  auto step = [&](int t, const char* kread, char* kdst, char* vdst, const char* vread,
-                  f32x16 (&sc)[2], f32x16 (&sn)[2]) {
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    __syncthreads();
-    if (t + 2 < n_tiles) issue(t + 2, kdst, vdst);
-    softmax_max(t, sc);
-    interleaved(kread, sn, vread, sc);
-    return t + 1 < n_tiles;
+  // Ping-pong schedule. Each wave runs QK(0), then per tile t a softmax
+  // phase S(t) and a matrix phase M(t) = PV(t) + QK(t+1). Group 1 runs one
+  // phase behind group 0, so on every SIMD one wave is in a matrix phase
+  // while its partner is in a softmax phase; phases end at a workgroup
+  // barrier. Loads: group j = {K(j+1), V(j)} (slot j%2) is issued by group 0
+  // at the start of phase 2j (its matrix phase; j >= 1, groups -1 and 0 in
+  // the prologue), waited for by group 0 at the end of phase 2j+1, and read
+  // in phases 2j+2 and 2j+3.
+  // Ping-pong schedule. Each wave runs QK(0), then per tile t a softmax
+  // phase S(t) and a matrix phase M(t) = PV(t) + QK(t+1). Group 1 runs one
+  // phase behind group 0, so on every SIMD one wave is in a matrix phase
+  // while its partner is in a softmax phase; phases end at a workgroup
+  // barrier. Load group j = {K(j+1), V(j)} lives in LDS slot j%2. Group 0
+  // issues group j inside its matrix phase M(j-1) (phase 2j), spread
+  // between the MFMAs, waits for it at the end of its softmax phase S(j)
+  // (phase 2j+1), and both groups read it in M(j) (phases 2j+2, 2j+3).
+  // The two groups run separate copies of the loop, so neither carries a
+  // branch on its group inside a phase.
+  TileCursor cs, ck, cv;   // softmax tile; K and V tiles of the last load group
+  start(cs);
+  start(ck);
+  start(cv);
+  // Buffer resources of a load group; past the last tile they cover no
+  // bytes (the loads then write zeros into a slot nobody reads again).
+  // (readfirstlane: the values are wave-uniform; this keeps them scalar)
+  auto krsrc = [&](const TileCursor& c) {
+    const int kt = __builtin_amdgcn_readfirstlane(c.kt);
+    const int valid = __builtin_amdgcn_readfirstlane(max(min(c.k1 - kt, BN), 0) * tok_bytes);
+    return make_rsrc(kbase + int64_t(kt) * tok_bytes, valid);
   };
-  issue(0, k0s, v0s);
-  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-  __syncthreads();
-  if (n_tiles > 1) issue(1, k1s, v1s);
-  qk(k0s, sa);
-  for (int t = 0; t < n_tiles; t += 6) {
-    if (!step(t, k1s, k0s, v2s, v0s, sa, sb)) break;
-    if (!step(t + 1, k0s, k1s, v0s, v1s, sb, sa)) break;
-    if (!step(t + 2, k1s, k0s, v1s, v2s, sa, sb)) break;
-    if (!step(t + 3, k0s, k1s, v2s, v0s, sb, sa)) break;
-    if (!step(t + 4, k1s, k0s, v0s, v1s, sa, sb)) break;
-    if (!step(t + 5, k0s, k1s, v1s, v2s, sb, sa)) break;
+  auto vrsrc = [&](const TileCursor& c) {
+    const int kt = __builtin_amdgcn_readfirstlane(c.kt);
+    const int valid = __builtin_amdgcn_readfirstlane(max(a.tpad - kt, 0) * D * 2);
+    return make_rsrc(vtbase + int64_t(kt) * D * 2, valid);
+  };
+  auto sync = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto load_group = [&](__amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr, char* kdst, char* vdst) {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(kdst + (wg * CH + i) * 1024), 16,
+                                               kgo[i], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(vdst + (wg * CH + i) * 1024), 16,
+                                               vgo[i], 0, 0, 0);
+    }
+  };
+  // Matrix phase: PV of tile t and QK^T of tile t+1, 32 MFMAs each fed by
+  // one 1-KiB LDS read issued kLdsAhead MFMAs ahead. With loads, one
+  // LDS-DMA instruction goes out every four MFMAs, so the memory queue never
+  // holds up the matrix work. On the last tile the QK^T reads a stale K
+  // slot; those scores are never used.
+  auto matrix = [&](const char* vb, const char* kb, bool loads, char* kdst, char* vdst) {
+    __builtin_amdgcn_s_setprio(1);  // favour this wave's MFMA issue
+    pv(vb);
+    qk(kb);
+    if (loads) {
+      load_group(krsrc(ck), vrsrc(cv), kdst, vdst);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kLdsAhead, 0);
+      int d = kLdsAhead;
+#pragma unroll
+      for (int i = 0; i < 2 * CH; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
+#pragma unroll
+        for (int q = 0; q < 32 / (2 * CH); ++q) {
+          __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+          if (d < 32) {
+            __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+            ++d;
+          }
+        }
+      }
+    } else {
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kLdsAhead, 0);
+#pragma unroll
+      for (int i = 0; i < 32 - kLdsAhead; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, kLdsAhead, 0);
+    }
+    fence_s();
+    __builtin_amdgcn_s_setprio(0);
+  };
+
+  if (grp == 0) {
+    // prologue: K(0) into the slot of group -1 (k1s), group 0 into slot 0
+    load_group(krsrc(ck), vrsrc(cv), k1s, v0s);  // V(0) and, harmlessly, K(0) twice
+    advance(ck);
+    {
+      const __amdgpu_buffer_rsrc_t kr = krsrc(ck);
+#pragma unroll
+      for (int i = 0; i < CH; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(k0s + (wg * CH + i) * 1024), 16,
+                                                 kgo[i], 0, 0, 0);
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    sync();
+    qk(k1s);  // phase 0
+    fence_s();
+    sync();
+    for (int t = 0; t < n_tiles; t += 2) {
+      // phase 2t+1: S(t); prepare load group t+1
+      advance(ck);
+      advance(cv);
+      softmax(cs);
+      advance(cs);
+      fence_p();
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // group t has landed
+      sync();
+      matrix(v0s, k0s, true, k1s, v1s);  // phase 2t+2: M(t), loads group t+1
+      sync();
+      if (t + 1 >= n_tiles) break;
+      advance(ck);
+      advance(cv);
+      softmax(cs);
+      advance(cs);
+      fence_p();
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      sync();
+      matrix(v1s, k1s, true, k0s, v0s);
+      sync();
+    }
+    sync();  // group 1's last matrix phase
+  } else {
+    sync();  // prologue loads
+    sync();  // phase 0
+    qk(k1s);  // phase 1
+    fence_s();
+    sync();
+    for (int t = 0; t < n_tiles; t += 2) {
+      softmax(cs);
+      advance(cs);
+      fence_p();
+      sync();
+      matrix(v0s, k0s, false, nullptr, nullptr);
+      sync();
+      if (t + 1 >= n_tiles) break;
+      softmax(cs);
+      advance(cs);
+      fence_p();
+      sync();
+      matrix(v1s, k1s, false, nullptr, nullptr);
+      sync();
+    }
   }
 
   const float lt = sum_with_partner(l);
   if (!row_ok) return;
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
-  // O^T register r of block db holds d = 32*db + 8*(r/4) + 4*hh + r%4
-  float* po = a.part_o + ((int64_t(ent.step) * a.R + lrow) * a.H + h) * D + 4 * hh;
 #pragma unroll
   for (int db = 0; db < ND; ++db)
 #pragma unroll
@@ -581,16 +721,14 @@ void attn_step_bf16_d128_kernel(const AttnArgs a) {
                                      o[db][4 * tq + 2] * inv, o[db][4 * tq + 3] * inv);
       *reinterpret_cast<float4*>(po + 32 * db + 8 * tq) = val;
     }
-  if (hh == 0)
-    a.part_lse[(int64_t(ent.step) * a.H + h) * a.R + lrow] =
-        lt > 0.f ? m_ref * a.scale + logf(lt) : -INFINITY;
+  if (hh == 0) *pl = lt > 0.f ? m_ref * lse_scale + logf(lt) : -INFINITY;
 }
 
 template <int G>
 hipError_t launch_d128(const AttnArgs& a, int n_entries, hipStream_t stream) {
   const int64_t blocks = int64_t(n_entries) * a.n_hg;
   if (blocks >= (int64_t(1) << 31)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((attn_step_bf16_d128_kernel<G>), dim3(uint32_t(blocks)), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((attn_step_bf16_d128_kernel<G>), dim3(uint32_t(blocks)), dim3(512), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -34,7 +34,7 @@ struct Segment {
 // at a time.
 constexpr int kBlockN = 64;
 constexpr int kBf16Waves = 4;
-constexpr int kBf16WavesD128 = 4;
+constexpr int kBf16WavesD128 = 8;  // two ping-pong groups of four
 constexpr int kF32RowsPerTile = 64;
 
 struct TileShape {
