@@ -338,13 +338,14 @@ struct TileCursor {
 
 template <int G>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void attn_step_bf16_d128_kernel(const AttnArgs a) {
+void attn_rank_bf16_d128_kernel(const AttnArgs a) {
   constexpr int D = 128, BN = kBlockN;
   constexpr int TILE = BN * D * 2;           // bytes of one K (or V^T) tile
   constexpr int CH = TILE / 1024 / 4;        // LDS-DMA instructions per loading wave per tensor
   constexpr int ND = D / 32, NQ = D / 16;
   constexpr int RB = 4 / G;                  // row blocks per wave group
   static_assert(BN == 64, "tile walk assumes 64-key tiles");
+  static_assert(kUnitWaves == 8 && kUnitSlotFloats == (ND * 16 + 1) * 64, "partial slot layout");
   __shared__ __attribute__((aligned(1024))) char k0s[TILE];
   __shared__ __attribute__((aligned(1024))) char k1s[TILE];
   __shared__ __attribute__((aligned(1024))) char v0s[TILE];
@@ -355,8 +356,10 @@ void attn_step_bf16_d128_kernel(const AttnArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   const int grp = wave >> 2, wg = wave & 3;  // waves w and w+4 share a SIMD
   const int hg = blockIdx.x % a.n_hg;
-  const EntryRec ent = a.entries[blockIdx.x / a.n_hg];
-  const TileRec tile = a.tiles[ent.tile];
+  const UnitRec unit = a.units[blockIdx.x / a.n_hg];
+  const TileRec tile = a.tiles[unit.tile];
+  const EntryRec* const steps = a.tile_entries + unit.e0;
+  const int n_steps = unit.e1 - unit.e0;
   const int h = hg * G + (wg % G);
   const int rsub = grp * RB + wg / G;
   const int kvh = (hg * G) / a.group;
@@ -366,16 +369,21 @@ void attn_step_bf16_d128_kernel(const AttnArgs a) {
   const int lrow = tile.local0 + rin;
   const int grow = tile.g0 + rin;
   const int wave_lo = tile.g0 + rsub * 32;
-  const int n_spans = ent.span_end - ent.span_begin;
-  const SpanRec* spans = a.spans + ent.span_begin;
-  // output addresses (per lane), formed now so the arguments they come
-  // from need not stay live through the main loop
-  float* const po = a.part_o + ((int64_t(ent.step) * a.R + lrow) * a.H + h) * D + 4 * hh;
-  float* const pl = a.part_lse + (int64_t(ent.step) * a.H + h) * a.R + lrow;
-  const float lse_scale = a.scale;
+  // The unit's key spans: every step's spans, contiguous and in step order.
+  const SpanRec* spans = a.spans + steps[0].span_begin;
+  const int n_spans = steps[n_steps - 1].span_end - steps[0].span_begin;
+  // This wave's per-step partial slots (step i at i * kUnitWaves slots).
+  float* const part = a.part_o + (int64_t(blockIdx.x) * a.max_steps * kUnitWaves + wave) *
+                                     int64_t(kUnitSlotFloats) + lane;
 
+  auto span_tiles = [&](int i) { return (spans[i].k1 - (spans[i].k0 & ~7) + BN - 1) / BN; };
+  auto step_tiles = [&](int st) {
+    int n = 0;
+    for (int i = steps[st].span_begin; i < steps[st].span_end; ++i) n += span_tiles(i - steps[0].span_begin);
+    return n;
+  };
   int n_tiles = 0;
-  for (int i = 0; i < n_spans; ++i) n_tiles += (spans[i].k1 - (spans[i].k0 & ~7) + BN - 1) / BN;
+  for (int i = 0; i < n_spans; ++i) n_tiles += span_tiles(i);
   auto start = [&](TileCursor& c) {
     c.span = 0;
     c.k0 = spans[0].k0;
@@ -406,10 +414,10 @@ void attn_step_bf16_d128_kernel(const AttnArgs a) {
     }
   }
 
-  // Loads are issued by the four waves of group 0 only (they are in their
-  // matrix phase when loads start). Wave wg fills 1-KiB pieces wg*CH..+CH-1.
+  // K/V loads are issued by the four waves of group 0 only, in their matrix
+  // phases. Wave wg fills 1-KiB pieces wg*CH..+CH-1 of each tile.
   const int tok_bytes = a.Hkv * D * 2;
-    const char* kbase = static_cast<const char*>(a.k) + int64_t(kvh) * D * 2;
+  const char* kbase = static_cast<const char*>(a.k) + int64_t(kvh) * D * 2;
   // V^T: 8-key blocks of 128 d-rows (16 bytes each); a tile at kt is the
   // contiguous 16 KiB starting at key block kt / 8
   const char* vtbase = static_cast<const char*>(a.vt) + int64_t(kvh) * a.tpad * D * 2;
@@ -422,21 +430,6 @@ void attn_step_bf16_d128_kernel(const AttnArgs a) {
     const int d = 8 * c + (lane >> 3), vp = lane & 7;
     vgo[i] = (vp ^ ((d >> 1) & 7)) * (D * 16) + d * 16;
   }
-  auto issue_k = [&](const TileCursor& c, char* dst) {
-    const int valid = min(c.k1 - c.kt, BN) * tok_bytes;
-    const __amdgpu_buffer_rsrc_t r = make_rsrc(kbase + int64_t(c.kt) * tok_bytes, valid);
-#pragma unroll
-    for (int i = 0; i < CH; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + (wg * CH + i) * 1024), 16,
-                                               kgo[i], 0, 0, 0);
-  };
-  auto issue_v = [&](const TileCursor& c, char* dst) {
-    const __amdgpu_buffer_rsrc_t r = make_rsrc(vtbase + int64_t(c.kt) * D * 2, (a.tpad - c.kt) * D * 2);
-#pragma unroll
-    for (int i = 0; i < CH; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + (wg * CH + i) * 1024), 16,
-                                               vgo[i], 0, 0, 0);
-  };
 
   const int srow = (ql & ~12) | ((ql & 4) << 1) | ((ql & 8) >> 1);
   int kro[NQ];
@@ -451,7 +444,7 @@ void attn_step_bf16_d128_kernel(const AttnArgs a) {
 
   f32x16 sc[2];     // scores of the tile whose softmax is next
   bf16x8 pb[2][2];  // probabilities of the tile whose PV is next
-  f32x16 o[ND];
+  f32x16 o[ND];     // output of the current ring step, not yet normalised
 #pragma unroll
   for (int db = 0; db < ND; ++db)
 #pragma unroll
@@ -515,7 +508,35 @@ void attn_step_bf16_d128_kernel(const AttnArgs a) {
         pb[kb][r >> 3][r & 7] = (__bf16)p;
       }
   };
+  // Ring-step boundaries: the step that owns softmax tile ts, and the tile
+  // where the next step starts.
+  int ts = 0, cur_step = 0, step_end = step_tiles(0);
+  // Close the current step: its partial (output normalised by its own sum,
+  // and lse = m_ref/sqrt(D) + ln(sum)) goes to this wave's slot for the
+  // step, and the running state restarts for the next step.
+  auto end_step = [&]() {
+    const float lt = sum_with_partner(l);
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    float* const slot = part + int64_t(cur_step) * kUnitWaves * kUnitSlotFloats;
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        slot[(db * 16 + r) * 64] = o[db][r] * inv;
+        o[db][r] = 0.f;
+      }
+    slot[ND * 16 * 64] = lt > 0.f ? m_ref * a.scale + logf(lt) : -INFINITY;
+    l = 0.f;
+    m_ref = -INFINITY;
+  };
   auto softmax = [&](const TileCursor& c) {
+    // The previous matrix phase finished the last PV of a step: close it.
+    if (ts == step_end) {
+      end_step();
+      ++cur_step;
+      step_end += step_tiles(cur_step);
+    }
+    ++ts;
     if (c.kt < c.k0 || c.kt + BN > c.k1 || c.kt + BN - 1 > wave_lo) {
       // Keys of this lane sit at offsets 32kb + 16(r>>3) + (r&7) from
       // kt + 8hh; the visible ones form the range [lo, hi). Build that range
@@ -565,20 +586,13 @@ void attn_step_bf16_d128_kernel(const AttnArgs a) {
   // phase S(t) and a matrix phase M(t) = PV(t) + QK(t+1). Group 1 runs one
   // phase behind group 0, so on every SIMD one wave is in a matrix phase
   // while its partner is in a softmax phase; phases end at a workgroup
-  // barrier. Loads: group j = {K(j+1), V(j)} (slot j%2) is issued by group 0
-  // at the start of phase 2j (its matrix phase; j >= 1, groups -1 and 0 in
-  // the prologue), waited for by group 0 at the end of phase 2j+1, and read
-  // in phases 2j+2 and 2j+3.
-  // Ping-pong schedule. Each wave runs QK(0), then per tile t a softmax
-  // phase S(t) and a matrix phase M(t) = PV(t) + QK(t+1). Group 1 runs one
-  // phase behind group 0, so on every SIMD one wave is in a matrix phase
-  // while its partner is in a softmax phase; phases end at a workgroup
   // barrier. Load group j = {K(j+1), V(j)} lives in LDS slot j%2. Group 0
   // issues group j inside its matrix phase M(j-1) (phase 2j), spread
   // between the MFMAs, waits for it at the end of its softmax phase S(j)
   // (phase 2j+1), and both groups read it in M(j) (phases 2j+2, 2j+3).
   // The two groups run separate copies of the loop, so neither carries a
-  // branch on its group inside a phase.
+  // branch on its group inside a phase. Tiles run through all ring steps of
+  // the unit without a break; a step boundary only closes the step's partial.
   TileCursor cs, ck, cv;   // softmax tile; K and V tiles of the last load group
   start(cs);
   start(ck);
@@ -710,25 +724,54 @@ void attn_step_bf16_d128_kernel(const AttnArgs a) {
     }
   }
 
+  // LSE merge of the unit's ring steps (Ring Attention's combination of
+  // blockwise results): the last step is still in registers, the others
+  // are in this wave's slots. m = max over steps of lse_s; w_s =
+  // exp(lse_s - m); out = sum_s w_s O_s / sum_s w_s; lse = m + ln sum_s w_s.
   const float lt = sum_with_partner(l);
+  const float lse_last = lt > 0.f ? m_ref * a.scale + logf(lt) : -INFINITY;
+  float m = lse_last;
+  for (int st = 0; st < n_steps - 1; ++st)
+    m = fmaxf(m, part[int64_t(st) * kUnitWaves * kUnitSlotFloats + ND * 16 * 64]);
+  const float w_last = m == -INFINITY ? 0.f : __expf(lse_last - m);
+  float den = w_last;
+  {
+    const float c = lt > 0.f ? w_last / lt : 0.f;
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[db][r] *= c;
+  }
+  for (int st = 0; st < n_steps - 1; ++st) {
+    const float* slot = part + int64_t(st) * kUnitWaves * kUnitSlotFloats;
+    const float ls = slot[ND * 16 * 64];
+    const float w = m == -INFINITY ? 0.f : __expf(ls - m);
+    den += w;
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[db][r] = __builtin_fmaf(w, slot[(db * 16 + r) * 64], o[db][r]);
+  }
   if (!row_ok) return;
-  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  const float inv = den > 0.f ? 1.f / den : 0.f;
+  __bf16* const po = static_cast<__bf16*>(a.out) + (int64_t(lrow) * a.H + h) * D + 4 * hh;
 #pragma unroll
   for (int db = 0; db < ND; ++db)
 #pragma unroll
     for (int tq = 0; tq < 4; ++tq) {
-      const float4 val = make_float4(o[db][4 * tq] * inv, o[db][4 * tq + 1] * inv,
-                                     o[db][4 * tq + 2] * inv, o[db][4 * tq + 3] * inv);
-      *reinterpret_cast<float4*>(po + 32 * db + 8 * tq) = val;
+      typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+      const bf16x4 val = {(__bf16)(o[db][4 * tq] * inv), (__bf16)(o[db][4 * tq + 1] * inv),
+                          (__bf16)(o[db][4 * tq + 2] * inv), (__bf16)(o[db][4 * tq + 3] * inv)};
+      *reinterpret_cast<bf16x4*>(po + 32 * db + 8 * tq) = val;
     }
-  if (hh == 0) *pl = lt > 0.f ? m_ref * lse_scale + logf(lt) : -INFINITY;
+  if (hh == 0) a.lse[int64_t(h) * a.R + lrow] = den > 0.f ? m + logf(den) : -INFINITY;
 }
 
 template <int G>
-hipError_t launch_d128(const AttnArgs& a, int n_entries, hipStream_t stream) {
-  const int64_t blocks = int64_t(n_entries) * a.n_hg;
+hipError_t launch_units(const AttnArgs& a, int n_units, hipStream_t stream) {
+  const int64_t blocks = int64_t(n_units) * a.n_hg;
   if (blocks >= (int64_t(1) << 31)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((attn_step_bf16_d128_kernel<G>), dim3(uint32_t(blocks)), dim3(512), 0, stream, a);
+  hipLaunchKernelGGL((attn_rank_bf16_d128_kernel<G>), dim3(uint32_t(blocks)), dim3(512), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -746,17 +789,20 @@ hipError_t launch_g(const AttnArgs& a, int n_entries, hipStream_t stream) {
 hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, int heads_per_wg, int n_entries,
                             hipStream_t stream) {
   if (n_entries == 0) return hipSuccess;
-  if (head_dim == 128) {
-    if (heads_per_wg == 4) return launch_d128<4>(a, n_entries, stream);
-    if (heads_per_wg == 2) return launch_d128<2>(a, n_entries, stream);
-    return launch_d128<1>(a, n_entries, stream);
-  }
   if (head_dim == 64) {
     if (heads_per_wg == 4) return launch_g<64, 4>(a, n_entries, stream);
     if (heads_per_wg == 2) return launch_g<64, 2>(a, n_entries, stream);
     return launch_g<64, 1>(a, n_entries, stream);
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_attn_bf16_units(const AttnArgs& a, int heads_per_wg, int n_units,
+                                  hipStream_t stream) {
+  if (n_units == 0) return hipSuccess;
+  if (heads_per_wg == 4) return launch_units<4>(a, n_units, stream);
+  if (heads_per_wg == 2) return launch_units<2>(a, n_units, stream);
+  return launch_units<1>(a, n_units, stream);
 }
 
 }  // namespace cpattn

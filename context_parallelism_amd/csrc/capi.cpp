@@ -115,6 +115,11 @@ cp_status rank_fwd(const void* q, const void* k, const void* v, int32_t dtype, i
     a.tiles = reinterpret_cast<const TileRec*>(ws + w.off_tiles);
     a.entries = reinterpret_cast<const EntryRec*>(ws + w.off_entries);
     a.spans = reinterpret_cast<const SpanRec*>(ws + w.off_spans);
+    a.tile_entries = reinterpret_cast<const EntryRec*>(ws + w.off_tile_entries);
+    a.units = reinterpret_cast<const UnitRec*>(ws + w.off_units);
+    a.out = out;
+    a.lse = lse;
+    a.max_steps = cp_size;
     a.R = int32_t(R);
     a.H = heads;
     a.Hkv = kv_heads;
@@ -123,6 +128,17 @@ cp_status rank_fwd(const void* q, const void* k, const void* v, int32_t dtype, i
     a.scale = float(1.0 / std::sqrt(double(head_dim)));
     a.scale_log2 = float(1.4426950408889634 / std::sqrt(double(head_dim)));
     const int n_entries = int(w.plan.entries.size());
+    if (w.unit_kernel) {
+      // all ring steps of a row tile in one workgroup, merged in the kernel
+      if (launch_attn_bf16_units(a, w.shape.heads_per_wg, int(w.plan.units.size()), s) != hipSuccess)
+        return CP_EHIP;
+      if (w.plan.pad_rows > 0 &&
+          launch_fill_pad_rows(index, R, heads, head_dim, dtype, out, lse, s) != hipSuccess)
+        return CP_EHIP;
+      if (mark(events, 4, s) != hipSuccess) return CP_EHIP;
+      if (mark(events, 5, s) != hipSuccess) return CP_EHIP;
+      return CP_OK;
+    }
     hipError_t e = dtype == CP_DTYPE_BF16
                        ? launch_attn_bf16(a, head_dim, w.shape.heads_per_wg, n_entries, s)
                        : launch_attn_f32(a, head_dim, n_entries, s);

@@ -35,7 +35,37 @@ __global__ __launch_bounds__(kGatherThreads) void gather_rows_kernel(
     if (pos[u] < total_vec) dst[pos[u]] = val[u];
 }
 
+// Pad rows (index -1) of the outputs: zero output row, lse -inf. One thread
+// per (row, 16-byte piece of a row); piece 0 also writes the row's lse.
+__global__ __launch_bounds__(kGatherThreads) void fill_pad_rows_kernel(
+    const int32_t* __restrict__ index, uint4* __restrict__ out, float* __restrict__ lse,
+    uint32_t row_vec, uint32_t n_rows, uint32_t heads) {
+  const uint32_t i = blockIdx.x * kGatherThreads + threadIdx.x;
+  if (i >= row_vec * n_rows) return;
+  const uint32_t row = i / row_vec, piece = i % row_vec;
+  if (index[row] >= 0) return;
+  out[i] = make_uint4(0, 0, 0, 0);
+  if (piece < heads) lse[uint64_t(piece) * n_rows + row] = -INFINITY;
+}
+
 }  // namespace
+
+hipError_t launch_fill_pad_rows(const int32_t* index, int64_t n_rows, int32_t heads,
+                                int32_t head_dim, int32_t dtype, void* out, float* lse,
+                                hipStream_t stream) {
+  if (n_rows == 0) return hipSuccess;
+  const int64_t row_bytes = int64_t(heads) * head_dim * (dtype == 1 ? 2 : 4);
+  const uint64_t row_vec = uint64_t(row_bytes) / 16;
+  const uint64_t total = row_vec * uint64_t(n_rows);
+  // piece h < heads writes head h's lse: needs at least `heads` pieces per row
+  if (row_bytes % 16 != 0 || row_vec < uint64_t(heads) || total >= (uint64_t(1) << 32))
+    return hipErrorInvalidValue;
+  const uint32_t blocks = uint32_t((total + kGatherThreads - 1) / kGatherThreads);
+  hipLaunchKernelGGL(fill_pad_rows_kernel, dim3(blocks), dim3(kGatherThreads), 0, stream, index,
+                     static_cast<uint4*>(out), lse, uint32_t(row_vec), uint32_t(n_rows),
+                     uint32_t(heads));
+  return hipGetLastError();
+}
 
 hipError_t launch_gather(const void* src, const int32_t* index, void* dst, int64_t n_rows,
                          int64_t row_bytes, hipStream_t stream) {

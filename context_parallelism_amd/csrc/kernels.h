@@ -20,6 +20,11 @@ struct AttnArgs {
   const TileRec* tiles;
   const EntryRec* entries;
   const SpanRec* spans;
+  const EntryRec* tile_entries;  // entries in (tile, step) order (unit kernel)
+  const UnitRec* units;          // unit kernel work list
+  void* out;                     // [R, H, D] in the input dtype (unit kernel)
+  float* lse;                    // [H, R] fp32 (unit kernel)
+  int32_t max_steps;             // P: per-step partial slots per workgroup (unit kernel)
   int32_t R, H, Hkv;
   int32_t n_hg;          // head groups (workgroups per entry)
   int32_t group;         // heads / kv_heads
@@ -37,6 +42,17 @@ hipError_t launch_transpose_v(const void* v, void* vt, int32_t T, int32_t Hkv, i
 
 hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, int heads_per_wg, int n_entries,
                             hipStream_t stream);
+
+// bf16, head_dim 128: one workgroup per (unit, head group), all ring steps
+// of the unit's row tile, per-step partials merged in the kernel; writes
+// a.out and a.lse for the unit's rows.
+hipError_t launch_attn_bf16_units(const AttnArgs& a, int heads_per_wg, int n_units,
+                                  hipStream_t stream);
+
+// out[i] = 0 and lse[:, i] = -inf for every rank-local row i with index -1.
+hipError_t launch_fill_pad_rows(const int32_t* index, int64_t n_rows, int32_t heads,
+                                int32_t head_dim, int32_t dtype, void* out, float* lse,
+                                hipStream_t stream);
 
 hipError_t launch_attn_f32(const AttnArgs& a, int head_dim, int n_entries, hipStream_t stream);
 

@@ -181,10 +181,27 @@ void build_plan(const Meta& m, int32_t bm, int32_t bn, Plan& p) {
       for (int32_t i = 0; i < t.nrows; ++i) p.row_mask[size_t(t.local0 + i)] = mask;
     }
   }
+  // units: every tile's entries in step order (pend is in (tile, step) order)
+  struct PendingUnit { UnitRec u; int64_t cost; };
+  std::vector<PendingUnit> units;
+  p.tile_entries.reserve(pend.size());
+  for (size_t i = 0; i < pend.size(); ++i) {
+    const int32_t e = int32_t(p.tile_entries.size());
+    if (units.empty() || units.back().u.tile != pend[i].e.tile)
+      units.push_back({UnitRec{pend[i].e.tile, e, e, 0}, 0});
+    p.tile_entries.push_back(pend[i].e);
+    units.back().u.e1 = e + 1;
+    units.back().cost += pend[i].cost;
+  }
+  std::stable_sort(units.begin(), units.end(),
+                   [](const PendingUnit& x, const PendingUnit& y) { return x.cost > y.cost; });
+  p.units.reserve(units.size());
+  for (const PendingUnit& u : units) p.units.push_back(u.u);
   std::stable_sort(pend.begin(), pend.end(),
                    [](const Pending& x, const Pending& y) { return x.cost > y.cost; });
   p.entries.reserve(pend.size());
   for (const Pending& q : pend) p.entries.push_back(q.e);
+  for (int32_t g : p.index) p.pad_rows += g < 0;
 }
 
 }  // namespace cpattn

@@ -36,6 +36,11 @@ constexpr int kBlockN = 64;
 constexpr int kBf16Waves = 4;
 constexpr int kBf16WavesD128 = 8;  // two ping-pong groups of four
 constexpr int kF32RowsPerTile = 64;
+// Unit kernel (bf16, head_dim 128): waves per workgroup, and floats of one
+// wave's per-step partial slot (64 output registers and the log-sum-exp,
+// each for 64 lanes).
+constexpr int kUnitWaves = kBf16WavesD128;
+constexpr int kUnitSlotFloats = 65 * 64;
 
 struct TileShape {
   int32_t rows;          // rows per plan tile (bm)
@@ -66,11 +71,17 @@ std::vector<Segment> segments(const Meta& m);
 struct TileRec { int32_t local0, nrows, g0, pad; };          // a row tile
 struct EntryRec { int32_t tile, step, span_begin, span_end; };  // (tile, step) work
 struct SpanRec { int32_t k0, k1; };                          // global keys [k0, k1)
+// All ring steps of one row tile: tile_entries[e0, e1), in step order; their
+// key spans are contiguous in the span list.
+struct UnitRec { int32_t tile, e0, e1, pad; };
 
 struct Plan {
   int32_t bm = 0, bn = 0;
   std::vector<TileRec> tiles;
   std::vector<EntryRec> entries;  // launch order: longest first
+  std::vector<EntryRec> tile_entries;  // the same entries in (tile, step) order
+  std::vector<UnitRec> units;          // one per row tile, launch order: longest first
+  int64_t pad_rows = 0;                // rank-local rows with index -1
   std::vector<SpanRec> spans;
   std::vector<uint32_t> row_mask;  // per rank-local row: steps with a partial
   std::vector<int32_t> index;      // per rank-local row: global id or -1

@@ -39,6 +39,10 @@ int32_t prepare_workspace(int64_t seq_len, const int32_t* n_img, const int32_t* 
   off = align256(off + w.plan.entries.size() * sizeof(EntryRec));
   w.off_spans = off;
   off = align256(off + w.plan.spans.size() * sizeof(SpanRec));
+  w.off_tile_entries = off;
+  off = align256(off + w.plan.tile_entries.size() * sizeof(EntryRec));
+  w.off_units = off;
+  off = align256(off + w.plan.units.size() * sizeof(UnitRec));
   w.plan_bytes = off;
   w.off_qr = off;
   off = align256(off + R * size_t(heads) * head_dim * esize);
@@ -47,10 +51,18 @@ int32_t prepare_workspace(int64_t seq_len, const int32_t* n_img, const int32_t* 
     w.tpad = vt_row_keys(seq_len);
     off = align256(off + size_t(kv_heads) * head_dim * size_t(w.tpad) * 2);
   }
+  w.unit_kernel = dtype == CP_DTYPE_BF16 && head_dim == 128;
   w.off_po = off;
-  off = align256(off + size_t(cp_size) * R * size_t(heads) * head_dim * sizeof(float));
-  w.off_pl = off;
-  off = align256(off + size_t(cp_size) * size_t(heads) * R * sizeof(float));
+  if (w.unit_kernel) {
+    const size_t n_hg = size_t(heads / w.shape.heads_per_wg);
+    off = align256(off + w.plan.units.size() * n_hg * size_t(cp_size) * kUnitWaves *
+                             kUnitSlotFloats * sizeof(float));
+    w.off_pl = off;
+  } else {
+    off = align256(off + size_t(cp_size) * R * size_t(heads) * head_dim * sizeof(float));
+    w.off_pl = off;
+    off = align256(off + size_t(cp_size) * size_t(heads) * R * sizeof(float));
+  }
   w.total = off;
   return CP_OK;
 }
@@ -65,6 +77,9 @@ void pack_plan(const Workspace& w, uint8_t* dst) {
   if (!p.entries.empty())
     std::memcpy(dst + w.off_entries, p.entries.data(), p.entries.size() * sizeof(EntryRec));
   if (!p.spans.empty()) std::memcpy(dst + w.off_spans, p.spans.data(), p.spans.size() * sizeof(SpanRec));
+  if (!p.tile_entries.empty())
+    std::memcpy(dst + w.off_tile_entries, p.tile_entries.data(), p.tile_entries.size() * sizeof(EntryRec));
+  if (!p.units.empty()) std::memcpy(dst + w.off_units, p.units.data(), p.units.size() * sizeof(UnitRec));
 }
 
 }  // namespace cpattn

@@ -1,11 +1,13 @@
 // Workspace layout of cp_attn_rank_fwd (host only, no HIP). The device
 // workspace holds, each region 256-byte aligned:
-//   plan   : index int32[R], step mask uint32[R], tiles, entries, spans
-//            (uploaded from the host in one copy);
+//   plan   : index int32[R], step mask uint32[R], tiles, entries, spans,
+//            step-ordered entries, units (uploaded from the host in one copy);
 //   qr     : gathered rank-local Q rows [R, H, D] in the input dtype;
-//   vt     : V^T [Hkv, D, tpad] (bf16 with head_dim 128 only; else empty);
-//   part_o : per-step partial outputs fp32 [P, R, H, D];
-//   part_l : per-step log-sum-exps fp32 [P, H, R].
+//   vt     : V^T blocked by 8 keys (bf16 with head_dim 128 only; else empty);
+//   part_o : per-step partial outputs, fp32. Per-step kernels: [P, R, H, D].
+//            Unit kernel (bf16, head_dim 128): one slot per (workgroup, step,
+//            wave) of kUnitSlotFloats, in the wave's own register order;
+//   part_l : per-step log-sum-exps fp32 [P, H, R] (per-step kernels only).
 #pragma once
 
 #include <cstddef>
@@ -21,6 +23,8 @@ struct Workspace {
   TileShape shape{0, 0};
   int32_t heads = 0, kv_heads = 0, head_dim = 0, dtype = 0;
   size_t off_index = 0, off_mask = 0, off_tiles = 0, off_entries = 0, off_spans = 0;
+  size_t off_tile_entries = 0, off_units = 0;
+  bool unit_kernel = false;  // bf16 head_dim 128: units with the in-kernel merge
   size_t plan_bytes = 0;
   size_t off_qr = 0, off_vt = 0, off_po = 0, off_pl = 0, total = 0;
   int32_t tpad = 0;  // keys per V^T row (0: no V^T region)
