@@ -610,9 +610,16 @@ void attn_rank_bf16_d128_kernel(const AttnArgs a) {
     const int valid = __builtin_amdgcn_readfirstlane(max(a.tpad - kt, 0) * D * 2);
     return make_rsrc(vtbase + int64_t(kt) * D * 2, valid);
   };
+  // Phase barrier: a bare s_barrier. __syncthreads() would add a release
+  // fence, i.e. wait for every outstanding memory operation of the wave --
+  // including the LDS-DMA loads group 0 has just issued for a later tile.
+  // LDS ordering is explicit here instead: a slot's DMA is waited for
+  // (vmcnt) by its issuing waves before the barrier that publishes it, and
+  // every LDS read completes inside its phase (its MFMA consumes it). The
+  // "memory" clobber keeps the compiler from moving memory accesses across.
   auto sync = [&]() {
     __builtin_amdgcn_sched_barrier(0);
-    __syncthreads();
+    asm volatile("s_barrier" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
   };
   auto load_group = [&](__amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr, char* kdst, char* vdst) {
