@@ -97,7 +97,8 @@ def main():
     ap.add_argument("--workload", type=int, default=4, help="synthetic workload number (1-5)")
     ap.add_argument("--rank", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=36.0,
+                    help="CPU-baseline budget; the oracle sample grows until it takes a third of this")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="instead of the attention, run --steps plain device copies of this many MiB "
                          "(the reference kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")

@@ -96,8 +96,9 @@ cp_status cp_pair_counts(int64_t seq_len, const int32_t *n_img, const int32_t *c
 /*
  * cp_attn_rank_workspace_size -- bytes of device workspace that
  * cp_attn_rank_fwd needs for these arguments (host only). The workspace
- * holds the uploaded plan, the gathered rank-local Q rows, and the per-step
- * partial outputs (fp32) and log-sum-exps.
+ * holds the uploaded plan, the gathered rank-local Q rows, the V^T copy
+ * (bf16, head_dim 128), and the per-step partial outputs (fp32) and
+ * log-sum-exps.
  */
 cp_status cp_attn_rank_workspace_size(int64_t seq_len, const int32_t *n_img,
                                       const int32_t *cu_seqlens, int32_t n_samples,
@@ -134,8 +135,15 @@ cp_status cp_attn_rank_plan_stats(int64_t seq_len, const int32_t *n_img, const i
  *   3. for every ring step s = 0..P-1 (source rank j = (r - s) mod P; the
  *      image prefix and the rank's own chunks at s = 0, chunks j and
  *      2P-1-j at s > 0), blockwise causal attention of the rank's rows to
- *      that step's keys, writing per-step partial outputs and lse;
- *   4. merge the partials of each row by their log-sum-exp.
+ *      that step's keys, each step giving a partial output normalised by
+ *      its own softmax sum, and that sum's log-sum-exp;
+ *   4. merge the partials of each row by their log-sum-exp (Ring
+ *      Attention's combination of blockwise results).
+ * With bf16 and head_dim 128, steps 3 and 4 run in one kernel: a workgroup
+ * takes all ring steps of a row tile in order, keeps each step's partial in
+ * its own workspace slot and merges them before it writes out and lse.
+ * Other dtypes and head_dim 64 write partials for all rows and merge them
+ * in a separate pass (cp_lse_merge's kernel).
  *
  * q, k, v: device, dtype CP_DTYPE_BF16 or CP_DTYPE_F32, THD layout.
  * out: device [R, heads, head_dim] in dtype; lse: device fp32 [heads, R],
