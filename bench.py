@@ -56,7 +56,7 @@ def traffic_from_profile():
     return doc.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, q, k, v, n_img, cu, target_s: float):
+def cpu_baseline(w, q, k, v, n_img, cu, target_s: float, split: str = "head_tail"):
     """The fp64 oracle, as it stands, on a bounded sample of the rank's rows."""
     import numpy as np
 
@@ -67,13 +67,13 @@ def cpu_baseline(w, q, k, v, n_img, cu, target_s: float):
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     except Exception:  # pragma: no cover
         threads = 1
-    index, _ = oracle.partition_index(w.seq_len, n_img, cu, w.cp_size, w.rank)
+    index, _ = oracle.partition_index(w.seq_len, n_img, cu, w.cp_size, w.rank, split)
     R = len(index)
     n = 32
     while True:
         rows = np.linspace(0, R - 1, n).astype(np.int64)
         t0 = time.perf_counter()
-        oracle.rank_attention(q, k, v, n_img, cu, w.cp_size, w.rank, local_rows=rows)
+        oracle.rank_attention(q, k, v, n_img, cu, w.cp_size, w.rank, local_rows=rows, split=split)
         dt = time.perf_counter() - t0
         if dt >= target_s / 3 or n >= R:
             break
@@ -89,6 +89,78 @@ def cpu_baseline(w, q, k, v, n_img, cu, target_s: float):
                       f"{pairs} useful pairs/head, {dt:.1f} s, fp64 numpy"}
 
 
+def timed_calls(ra, hip, steps, warmup):
+    """Median per-call and attention-stage times (ms) of `steps` calls, HIP events."""
+    import numpy as np
+    import torch
+
+    evs = []
+    for _ in range(steps):
+        row = []
+        for _ in range(6):
+            e = ctypes.c_void_p()
+            assert hip.hipEventCreate(ctypes.byref(e)) == 0
+            row.append(e.value)
+        evs.append(row)
+    for _ in range(warmup):
+        ra()
+    torch.cuda.synchronize()
+    for i in range(steps):
+        ra(evs[i])
+    torch.cuda.synchronize()
+
+    def el(a, b):
+        ms = ctypes.c_float()
+        assert hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b)) == 0
+        return ms.value
+    call = np.median([el(e[0], e[5]) for e in evs])
+    attn = np.median([el(e[3], e[4]) for e in evs])
+    for row in evs:
+        for e in row:
+            hip.hipEventDestroy(ctypes.c_void_p(e))
+    return float(call), float(attn)
+
+
+def compare_splits(w, args):
+    """Every rank share of one workload under head-tail pairing and under the
+    plain contiguous split, same kernels. The CP step waits for its slowest
+    rank, so the figure of merit is the maximum over ranks."""
+    import torch
+
+    import context_parallelism_amd as cp
+    import workloads
+
+    dev = torch.device("cuda:0")
+    q, k, v = workloads.make_inputs(w)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    n_img = w.n_img_array if any(w.n_img) else None
+    cu = w.cu_seqlens if w.n_samples > 1 else None
+    hip = hip_runtime()
+    res = {}
+    for split in ("head_tail", "contiguous"):
+        rows = []
+        for r in range(w.cp_size):
+            ra = cp.RankAttention(qd, kd, vd, cp_size=w.cp_size, cp_rank=r, n_img=n_img, cu_seqlens=cu,
+                                  split=split)
+            _, pairs = cp.pair_counts(w.seq_len, n_img, cu, cp_size=w.cp_size, cp_rank=r, split=split)
+            call, attn = timed_calls(ra, hip, args.steps, args.warmup)
+            rows.append({"rank": r, "pairs_per_head": pairs, "call_ms": round(call, 4),
+                         "attention_ms": round(attn, 4)})
+            del ra
+            print(f"{split} rank {r}: {pairs} pairs/head, call {call:.4f} ms", file=sys.stderr, flush=True)
+        calls = [x["call_ms"] for x in rows]
+        res[split] = {"ranks": rows, "max_call_ms": max(calls), "mean_call_ms": round(sum(calls) / len(calls), 4),
+                      "max_over_mean": round(max(calls) / (sum(calls) / len(calls)), 4)}
+    useful = 4.0 * w.head_dim * w.heads * sum(x["pairs_per_head"] for x in res["head_tail"]["ranks"])
+    line = {"mode": "compare_splits", "workload": w.name, "cp_size": w.cp_size, "steps": args.steps,
+            "warmup": args.warmup, "splits": res,
+            "job_step_ms": {s: res[s]["max_call_ms"] for s in res},
+            "job_useful_TFLOPs_per_gpu": {s: round(useful / w.cp_size / (res[s]["max_call_ms"] * 1e-3) / 1e12, 2)
+                                          for s in res},
+            "head_tail_speedup": round(res["contiguous"]["max_call_ms"] / res["head_tail"]["max_call_ms"], 4)}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -99,6 +171,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=36.0,
                     help="CPU-baseline budget; the oracle sample grows until it takes a third of this")
+    ap.add_argument("--split", choices=["head_tail", "contiguous"], default="head_tail",
+                    help="text split over the CP group (contiguous: the plain P-way split)")
+    ap.add_argument("--compare-splits", action="store_true",
+                    help="instead of the headline line: time every rank share under both splits "
+                         "and print one JSON line with the per-rank times (the CP step waits for "
+                         "the slowest rank)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="instead of the attention, run --steps plain device copies of this many MiB "
                          "(the reference kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -125,6 +203,9 @@ def main():
         return
 
     w = workloads.get(args.workload)
+    if args.compare_splits:
+        compare_splits(w, args)
+        return
     rank = w.rank if args.rank is None else args.rank
     if rank != w.rank:
         import dataclasses
@@ -134,8 +215,9 @@ def main():
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
     n_img = w.n_img_array if any(w.n_img) else None
     cu = w.cu_seqlens if w.n_samples > 1 else None
-    ra = cp.RankAttention(qd, kd, vd, cp_size=w.cp_size, cp_rank=rank, n_img=n_img, cu_seqlens=cu)
-    _, pairs = cp.pair_counts(w.seq_len, n_img, cu, cp_size=w.cp_size, cp_rank=rank)
+    ra = cp.RankAttention(qd, kd, vd, cp_size=w.cp_size, cp_rank=rank, n_img=n_img, cu_seqlens=cu,
+                          split=args.split)
+    _, pairs = cp.pair_counts(w.seq_len, n_img, cu, cp_size=w.cp_size, cp_rank=rank, split=args.split)
     useful = 4.0 * w.head_dim * w.heads * pairs
 
     hip = hip_runtime()
@@ -190,6 +272,7 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic: Q/K/V ~ N(0,1) drawn from numpy default_rng(%d), rounded to %s" % (w.seed, w.dtype),
         "config": {"workload": w.name, "seq_len": w.seq_len, "cp_size": w.cp_size, "cp_rank": rank,
+                   "split": args.split,
                    "heads": w.heads, "kv_heads": w.kv_heads, "head_dim": w.head_dim,
                    "n_img": list(w.n_img), "samples": w.n_samples, "rank_rows": R,
                    "useful_pairs_per_head": pairs, "useful_flop": useful},
@@ -210,7 +293,7 @@ def main():
                                },
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, q, k, v, n_img, cu, args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(w, q, k, v, n_img, cu, args.cpu_seconds, args.split)
     print(json.dumps(line), flush=True)
 
 

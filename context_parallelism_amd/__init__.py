@@ -15,22 +15,30 @@ from ._lib import (  # noqa: F401
     CP_EUNSUPPORTED,
     CP_MAX_CP_SIZE,
     CP_OK,
+    CP_SPLIT_CONTIGUOUS,
+    CP_SPLIT_HEAD_TAIL,
     LIB_PATH,
     SIGNATURES,
     CpError,
     check,
     cp_attn_rank_fwd,
+    cp_attn_rank_fwd_ex,
     cp_attn_rank_fwd_timed,
     cp_attn_rank_plan_stats,
+    cp_attn_rank_plan_stats_ex,
     cp_attn_rank_workspace_size,
+    cp_attn_rank_workspace_size_ex,
     cp_gather_rows,
     cp_lse_merge,
     cp_pair_counts,
+    cp_pair_counts_ex,
     cp_partition_index,
+    cp_partition_index_ex,
     cp_status_string,
     load,
 )
 from .api import (  # noqa: F401
+    SPLITS,
     RankAttention,
     gather_rows,
     lse_merge,

@@ -20,6 +20,8 @@ CP_EHIP = -4
 CP_DTYPE_F32 = 0
 CP_DTYPE_BF16 = 1
 CP_MAX_CP_SIZE = 32
+CP_SPLIT_HEAD_TAIL = 0
+CP_SPLIT_CONTIGUOUS = 1
 
 # (name, restype, argtypes) for every entry point declared in include/cpattn.h
 _P32 = POINTER(c_int32)
@@ -43,6 +45,18 @@ SIGNATURES = [
     ("cp_gather_rows", c_int32, [c_void_p, c_int32, c_int64, c_int64, c_void_p, c_int64, c_void_p, c_void_p]),
     ("cp_lse_merge", c_int32,
      [c_void_p, c_void_p, c_void_p, c_int32, c_int64, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p]),
+    ("cp_partition_index_ex", c_int32,
+     [c_int64, _P32, _P32, c_int32, c_int32, c_int32, c_int32, _P32, c_int64, _P64, _P32]),
+    ("cp_pair_counts_ex", c_int32, [c_int64, _P32, _P32, c_int32, c_int32, c_int32, c_int32, _P64, _P64]),
+    ("cp_attn_rank_workspace_size_ex", c_int32,
+     [c_int64, _P32, _P32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32,
+      POINTER(c_size_t)]),
+    ("cp_attn_rank_plan_stats_ex", c_int32,
+     [c_int64, _P32, _P32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32,
+      _P64, _P64, _P64, _P64, _P64]),
+    ("cp_attn_rank_fwd_ex", c_int32,
+     [c_void_p, c_void_p, c_void_p, c_int32, c_int64, _P32, _P32, c_int32, c_int32, c_int32, c_int32,
+      c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p, POINTER(c_void_p)]),
     ("cp_status_string", c_char_p, [c_int32]),
 ]
 
@@ -100,3 +114,8 @@ cp_attn_rank_fwd = _fn("cp_attn_rank_fwd")
 cp_attn_rank_fwd_timed = _fn("cp_attn_rank_fwd_timed")
 cp_gather_rows = _fn("cp_gather_rows")
 cp_lse_merge = _fn("cp_lse_merge")
+cp_partition_index_ex = _fn("cp_partition_index_ex")
+cp_pair_counts_ex = _fn("cp_pair_counts_ex")
+cp_attn_rank_workspace_size_ex = _fn("cp_attn_rank_workspace_size_ex")
+cp_attn_rank_plan_stats_ex = _fn("cp_attn_rank_plan_stats_ex")
+cp_attn_rank_fwd_ex = _fn("cp_attn_rank_fwd_ex")

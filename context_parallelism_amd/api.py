@@ -12,9 +12,16 @@ from typing import Optional, Sequence, Tuple
 import numpy as np
 
 from . import _lib
-from ._lib import CP_DTYPE_BF16, CP_DTYPE_F32, check
+from ._lib import CP_DTYPE_BF16, CP_DTYPE_F32, CP_SPLIT_CONTIGUOUS, CP_SPLIT_HEAD_TAIL, check
 
 _I32P = ctypes.POINTER(ctypes.c_int32)
+SPLITS = {"head_tail": CP_SPLIT_HEAD_TAIL, "contiguous": CP_SPLIT_CONTIGUOUS}
+
+
+def _split_code(split) -> int:
+    if split not in SPLITS:
+        raise ValueError(f"split must be one of {sorted(SPLITS)}, not {split!r}")
+    return SPLITS[split]
 
 
 def _meta(n_img, cu_seqlens):
@@ -27,51 +34,54 @@ def _meta(n_img, cu_seqlens):
     return (cu, img), cu_p, img_p, n_samples
 
 
-def partition_index(seq_len: int, n_img=None, cu_seqlens=None, *, cp_size: int, cp_rank: int
-                    ) -> Tuple[np.ndarray, np.ndarray]:
+def partition_index(seq_len: int, n_img=None, cu_seqlens=None, *, cp_size: int, cp_rank: int,
+                    split: str = "head_tail") -> Tuple[np.ndarray, np.ndarray]:
     """(index int32[R], cu_rows int32[n_samples+1]) of one CP rank."""
     keep, cu_p, img_p, n = _meta(n_img, cu_seqlens)
+    sp = _split_code(split)
     rows = ctypes.c_int64(0)
-    check(_lib.cp_partition_index(seq_len, img_p, cu_p, n, cp_size, cp_rank, None, 0,
-                                  ctypes.byref(rows), None), "cp_partition_index")
+    check(_lib.cp_partition_index_ex(seq_len, img_p, cu_p, n, cp_size, cp_rank, sp, None, 0,
+                                     ctypes.byref(rows), None), "cp_partition_index_ex")
     index = np.zeros(rows.value, dtype=np.int32)
     cu_rows = np.zeros(n + 1, dtype=np.int32)
-    check(_lib.cp_partition_index(seq_len, img_p, cu_p, n, cp_size, cp_rank,
-                                  index.ctypes.data_as(_I32P), rows.value, ctypes.byref(rows),
-                                  cu_rows.ctypes.data_as(_I32P)), "cp_partition_index")
+    check(_lib.cp_partition_index_ex(seq_len, img_p, cu_p, n, cp_size, cp_rank, sp,
+                                     index.ctypes.data_as(_I32P), rows.value, ctypes.byref(rows),
+                                     cu_rows.ctypes.data_as(_I32P)), "cp_partition_index_ex")
     return index, cu_rows
 
 
-def pair_counts(seq_len: int, n_img=None, cu_seqlens=None, *, cp_size: int, cp_rank: int
-                ) -> Tuple[int, int]:
+def pair_counts(seq_len: int, n_img=None, cu_seqlens=None, *, cp_size: int, cp_rank: int,
+                split: str = "head_tail") -> Tuple[int, int]:
     """(padded, real) unmasked pairs per head on one rank."""
     keep, cu_p, img_p, n = _meta(n_img, cu_seqlens)
     padded, real = ctypes.c_int64(0), ctypes.c_int64(0)
-    check(_lib.cp_pair_counts(seq_len, img_p, cu_p, n, cp_size, cp_rank, ctypes.byref(padded),
-                              ctypes.byref(real)), "cp_pair_counts")
+    check(_lib.cp_pair_counts_ex(seq_len, img_p, cu_p, n, cp_size, cp_rank, _split_code(split),
+                                 ctypes.byref(padded), ctypes.byref(real)), "cp_pair_counts_ex")
     return padded.value, real.value
 
 
 def workspace_size(seq_len: int, n_img=None, cu_seqlens=None, *, cp_size: int, cp_rank: int,
-                   heads: int, kv_heads: int, head_dim: int, dtype: int) -> int:
+                   heads: int, kv_heads: int, head_dim: int, dtype: int, split: str = "head_tail") -> int:
     keep, cu_p, img_p, n = _meta(n_img, cu_seqlens)
     b = ctypes.c_size_t(0)
-    check(_lib.cp_attn_rank_workspace_size(seq_len, img_p, cu_p, n, cp_size, cp_rank, heads, kv_heads,
-                                           head_dim, dtype, ctypes.byref(b)),
-          "cp_attn_rank_workspace_size")
+    check(_lib.cp_attn_rank_workspace_size_ex(seq_len, img_p, cu_p, n, cp_size, cp_rank,
+                                              _split_code(split), heads, kv_heads, head_dim, dtype,
+                                              ctypes.byref(b)),
+          "cp_attn_rank_workspace_size_ex")
     return b.value
 
 
 def plan_stats(seq_len: int, n_img=None, cu_seqlens=None, *, cp_size: int, cp_rank: int,
-               heads: int, kv_heads: int, head_dim: int, dtype: int) -> dict:
+               heads: int, kv_heads: int, head_dim: int, dtype: int, split: str = "head_tail") -> dict:
     """Work-list diagnostics of one rank (see cp_attn_rank_plan_stats)."""
     keep, cu_p, img_p, n = _meta(n_img, cu_seqlens)
     vals = [ctypes.c_int64(0) for _ in range(4)]
     steps = np.zeros(cp_size, dtype=np.int64)
-    check(_lib.cp_attn_rank_plan_stats(seq_len, img_p, cu_p, n, cp_size, cp_rank, heads, kv_heads,
-                                       head_dim, dtype, *[ctypes.byref(x) for x in vals],
-                                       steps.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))),
-          "cp_attn_rank_plan_stats")
+    check(_lib.cp_attn_rank_plan_stats_ex(seq_len, img_p, cu_p, n, cp_size, cp_rank, _split_code(split),
+                                          heads, kv_heads, head_dim, dtype,
+                                          *[ctypes.byref(x) for x in vals],
+                                          steps.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))),
+          "cp_attn_rank_plan_stats_ex")
     return {"tiles": vals[0].value, "entries": vals[1].value, "kv_tiles": vals[2].value,
             "covered_pairs": vals[3].value, "step_pairs": steps.tolist()}
 
@@ -96,7 +106,8 @@ class RankAttention:
     """Reusable per-rank forward: plans the sizes once and keeps the output
     and workspace tensors, so repeated calls (benchmarks) allocate nothing."""
 
-    def __init__(self, q, k, v, *, cp_size: int, cp_rank: int, n_img=None, cu_seqlens=None):
+    def __init__(self, q, k, v, *, cp_size: int, cp_rank: int, n_img=None, cu_seqlens=None,
+                 split: str = "head_tail"):
         import torch
 
         for name, t in (("q", q), ("k", k), ("v", v)):
@@ -114,15 +125,16 @@ class RankAttention:
         self.q, self.k, self.v = q, k, v
         self.T, self.H, self.Hkv, self.D = int(T), int(H), int(Hkv), int(D)
         self.cp_size, self.cp_rank = int(cp_size), int(cp_rank)
+        self.split = _split_code(split)
         self._keep, self._cu_p, self._img_p, self.n_samples = _meta(n_img, cu_seqlens)
         rows = ctypes.c_int64(0)
-        check(_lib.cp_partition_index(self.T, self._img_p, self._cu_p, self.n_samples, self.cp_size,
-                                      self.cp_rank, None, 0, ctypes.byref(rows), None),
-              "cp_partition_index")
+        check(_lib.cp_partition_index_ex(self.T, self._img_p, self._cu_p, self.n_samples, self.cp_size,
+                                         self.cp_rank, self.split, None, 0, ctypes.byref(rows), None),
+              "cp_partition_index_ex")
         self.R = rows.value
         self.ws_bytes = workspace_size(self.T, self._keep[1], self._keep[0], cp_size=self.cp_size,
                                        cp_rank=self.cp_rank, heads=self.H, kv_heads=self.Hkv,
-                                       head_dim=self.D, dtype=self.dtype)
+                                       head_dim=self.D, dtype=self.dtype, split=split)
         dev = q.device
         self.out = torch.empty((self.R, self.H, self.D), dtype=q.dtype, device=dev)
         self.lse = torch.empty((self.H, self.R), dtype=torch.float32, device=dev)
@@ -132,24 +144,24 @@ class RankAttention:
         """Run the forward. ``events``: optional sequence of six raw
         hipEvent_t handles recorded at the stage boundaries
         (cp_attn_rank_fwd_timed)."""
-        args = (self.q.data_ptr(), self.k.data_ptr(), self.v.data_ptr(), self.dtype, self.T,
-                self._img_p, self._cu_p, self.n_samples, self.cp_size, self.cp_rank, self.H, self.Hkv,
-                self.D, self.out.data_ptr(), self.lse.data_ptr(), self.workspace.data_ptr(),
-                self.ws_bytes, _stream(self.q))
-        if events is None:
-            check(_lib.cp_attn_rank_fwd(*args), "cp_attn_rank_fwd")
-        else:
+        ev = None
+        if events is not None:
             if len(events) != 6:
-                raise ValueError("cp_attn_rank_fwd_timed records exactly six events")
+                raise ValueError("cp_attn_rank_fwd_ex records exactly six events")
             ev = (ctypes.c_void_p * 6)(*[ctypes.c_void_p(int(e)) for e in events])
-            check(_lib.cp_attn_rank_fwd_timed(*args, ev), "cp_attn_rank_fwd_timed")
+        check(_lib.cp_attn_rank_fwd_ex(self.q.data_ptr(), self.k.data_ptr(), self.v.data_ptr(), self.dtype,
+                                       self.T, self._img_p, self._cu_p, self.n_samples, self.cp_size,
+                                       self.cp_rank, self.split, self.H, self.Hkv, self.D,
+                                       self.out.data_ptr(), self.lse.data_ptr(), self.workspace.data_ptr(),
+                                       self.ws_bytes, _stream(self.q), ev), "cp_attn_rank_fwd_ex")
         return self.out, self.lse
 
 
-def rank_fwd(q, k, v, *, cp_size: int, cp_rank: int, n_img=None, cu_seqlens=None):
+def rank_fwd(q, k, v, *, cp_size: int, cp_rank: int, n_img=None, cu_seqlens=None,
+             split: str = "head_tail"):
     """Per-rank forward attention. Returns (out [R,H,D] in q.dtype, lse fp32 [H,R])."""
     return RankAttention(q, k, v, cp_size=cp_size, cp_rank=cp_rank, n_img=n_img,
-                         cu_seqlens=cu_seqlens)()
+                         cu_seqlens=cu_seqlens, split=split)()
 
 
 def gather_rows(src, index):

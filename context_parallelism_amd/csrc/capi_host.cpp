@@ -12,12 +12,13 @@ using namespace cpattn;
 
 extern "C" {
 
-cp_status cp_partition_index(int64_t seq_len, const int32_t* n_img, const int32_t* cu_seqlens,
-                             int32_t n_samples, int32_t cp_size, int32_t cp_rank, int32_t* index,
-                             int64_t capacity, int64_t* n_rows, int32_t* cu_rows_local) {
+cp_status cp_partition_index_ex(int64_t seq_len, const int32_t* n_img, const int32_t* cu_seqlens,
+                                int32_t n_samples, int32_t cp_size, int32_t cp_rank, int32_t split,
+                                int32_t* index, int64_t capacity, int64_t* n_rows,
+                                int32_t* cu_rows_local) {
   try {
     Meta m;
-    int32_t st = build_meta(seq_len, n_img, cu_seqlens, n_samples, cp_size, cp_rank, m);
+    int32_t st = build_meta(seq_len, n_img, cu_seqlens, n_samples, cp_size, cp_rank, m, split);
     if (st != CP_OK) return st;
     if (index != nullptr && capacity < m.rows) return CP_ENOSPC;
     if (n_rows) *n_rows = m.rows;
@@ -28,12 +29,12 @@ cp_status cp_partition_index(int64_t seq_len, const int32_t* n_img, const int32_
   }
 }
 
-cp_status cp_pair_counts(int64_t seq_len, const int32_t* n_img, const int32_t* cu_seqlens,
-                         int32_t n_samples, int32_t cp_size, int32_t cp_rank, int64_t* pairs_padded,
-                         int64_t* pairs_real) {
+cp_status cp_pair_counts_ex(int64_t seq_len, const int32_t* n_img, const int32_t* cu_seqlens,
+                            int32_t n_samples, int32_t cp_size, int32_t cp_rank, int32_t split,
+                            int64_t* pairs_padded, int64_t* pairs_real) {
   try {
     Meta m;
-    int32_t st = build_meta(seq_len, n_img, cu_seqlens, n_samples, cp_size, cp_rank, m);
+    int32_t st = build_meta(seq_len, n_img, cu_seqlens, n_samples, cp_size, cp_rank, m, split);
     if (st != CP_OK) return st;
     pair_counts(m, pairs_padded, pairs_real);
     return CP_OK;
@@ -42,16 +43,16 @@ cp_status cp_pair_counts(int64_t seq_len, const int32_t* n_img, const int32_t* c
   }
 }
 
-cp_status cp_attn_rank_workspace_size(int64_t seq_len, const int32_t* n_img,
-                                      const int32_t* cu_seqlens, int32_t n_samples,
-                                      int32_t cp_size, int32_t cp_rank, int32_t heads,
-                                      int32_t kv_heads, int32_t head_dim, int32_t dtype,
-                                      size_t* bytes) {
+cp_status cp_attn_rank_workspace_size_ex(int64_t seq_len, const int32_t* n_img,
+                                         const int32_t* cu_seqlens, int32_t n_samples,
+                                         int32_t cp_size, int32_t cp_rank, int32_t split,
+                                         int32_t heads, int32_t kv_heads, int32_t head_dim,
+                                         int32_t dtype, size_t* bytes) {
   if (bytes == nullptr) return CP_EINVAL;
   try {
     Workspace w;
     int32_t st = prepare_workspace(seq_len, n_img, cu_seqlens, n_samples, cp_size, cp_rank, heads,
-                                   kv_heads, head_dim, dtype, w);
+                                   kv_heads, head_dim, dtype, w, split);
     if (st != CP_OK) return st;
     *bytes = w.total;
     return CP_OK;
@@ -60,15 +61,16 @@ cp_status cp_attn_rank_workspace_size(int64_t seq_len, const int32_t* n_img,
   }
 }
 
-cp_status cp_attn_rank_plan_stats(int64_t seq_len, const int32_t* n_img, const int32_t* cu_seqlens,
-                                  int32_t n_samples, int32_t cp_size, int32_t cp_rank,
-                                  int32_t heads, int32_t kv_heads, int32_t head_dim, int32_t dtype,
-                                  int64_t* n_tiles, int64_t* n_entries, int64_t* kv_tiles,
-                                  int64_t* covered_pairs, int64_t* step_pairs) {
+cp_status cp_attn_rank_plan_stats_ex(int64_t seq_len, const int32_t* n_img,
+                                     const int32_t* cu_seqlens, int32_t n_samples, int32_t cp_size,
+                                     int32_t cp_rank, int32_t split, int32_t heads,
+                                     int32_t kv_heads, int32_t head_dim, int32_t dtype,
+                                     int64_t* n_tiles, int64_t* n_entries, int64_t* kv_tiles,
+                                     int64_t* covered_pairs, int64_t* step_pairs) {
   try {
     Workspace w;
     int32_t st = prepare_workspace(seq_len, n_img, cu_seqlens, n_samples, cp_size, cp_rank, heads,
-                                   kv_heads, head_dim, dtype, w);
+                                   kv_heads, head_dim, dtype, w, split);
     if (st != CP_OK) return st;
     const Plan& p = w.plan;
     std::vector<int64_t> per_step(size_t(cp_size), 0);
@@ -97,6 +99,39 @@ cp_status cp_attn_rank_plan_stats(int64_t seq_len, const int32_t* n_img, const i
   } catch (const std::exception&) {
     return CP_EINVAL;
   }
+}
+
+cp_status cp_partition_index(int64_t seq_len, const int32_t* n_img, const int32_t* cu_seqlens,
+                             int32_t n_samples, int32_t cp_size, int32_t cp_rank, int32_t* index,
+                             int64_t capacity, int64_t* n_rows, int32_t* cu_rows_local) {
+  return cp_partition_index_ex(seq_len, n_img, cu_seqlens, n_samples, cp_size, cp_rank,
+                               CP_SPLIT_HEAD_TAIL, index, capacity, n_rows, cu_rows_local);
+}
+
+cp_status cp_pair_counts(int64_t seq_len, const int32_t* n_img, const int32_t* cu_seqlens,
+                         int32_t n_samples, int32_t cp_size, int32_t cp_rank, int64_t* pairs_padded,
+                         int64_t* pairs_real) {
+  return cp_pair_counts_ex(seq_len, n_img, cu_seqlens, n_samples, cp_size, cp_rank,
+                           CP_SPLIT_HEAD_TAIL, pairs_padded, pairs_real);
+}
+
+cp_status cp_attn_rank_workspace_size(int64_t seq_len, const int32_t* n_img,
+                                      const int32_t* cu_seqlens, int32_t n_samples,
+                                      int32_t cp_size, int32_t cp_rank, int32_t heads,
+                                      int32_t kv_heads, int32_t head_dim, int32_t dtype,
+                                      size_t* bytes) {
+  return cp_attn_rank_workspace_size_ex(seq_len, n_img, cu_seqlens, n_samples, cp_size, cp_rank,
+                                        CP_SPLIT_HEAD_TAIL, heads, kv_heads, head_dim, dtype, bytes);
+}
+
+cp_status cp_attn_rank_plan_stats(int64_t seq_len, const int32_t* n_img, const int32_t* cu_seqlens,
+                                  int32_t n_samples, int32_t cp_size, int32_t cp_rank,
+                                  int32_t heads, int32_t kv_heads, int32_t head_dim, int32_t dtype,
+                                  int64_t* n_tiles, int64_t* n_entries, int64_t* kv_tiles,
+                                  int64_t* covered_pairs, int64_t* step_pairs) {
+  return cp_attn_rank_plan_stats_ex(seq_len, n_img, cu_seqlens, n_samples, cp_size, cp_rank,
+                                    CP_SPLIT_HEAD_TAIL, heads, kv_heads, head_dim, dtype, n_tiles,
+                                    n_entries, kv_tiles, covered_pairs, step_pairs);
 }
 
 const char* cp_status_string(cp_status s) {

@@ -19,7 +19,8 @@ TileShape tile_shape(int32_t dtype, int32_t group, int32_t head_dim) {
 }
 
 int32_t build_meta(int64_t seq_len, const int32_t* n_img, const int32_t* cu_seqlens,
-                   int32_t n_samples, int32_t cp_size, int32_t cp_rank, Meta& m) {
+                   int32_t n_samples, int32_t cp_size, int32_t cp_rank, Meta& m, int32_t split) {
+  if (split != 0 && split != 1) return CP_EUNSUPPORTED;
   if (cp_size < 1) return CP_EINVAL;
   if (cp_size > CP_MAX_CP_SIZE) return CP_EUNSUPPORTED;
   if (cp_rank < 0 || cp_rank >= cp_size) return CP_EINVAL;
@@ -34,6 +35,7 @@ int32_t build_meta(int64_t seq_len, const int32_t* n_img, const int32_t* cu_seql
     if (int64_t(cu_seqlens[n_samples]) != seq_len) return CP_EINVAL;
   }
   m = Meta();
+  m.split = split;
   m.seq_len = seq_len;
   m.P = cp_size;
   m.r = cp_rank;
@@ -78,7 +80,8 @@ void fill_index(const Meta& m, int32_t* index, int32_t* cu_rows_local) {
     if (!index) continue;
     int32_t* out = index + g.local0;
     for (int32_t i = 0; i < g.n_img; ++i) *out++ = int32_t(g.a + i);
-    const int32_t ks[2] = {r, 2 * P - 1 - r};
+    int32_t ks[2];
+    owned_chunks(m, r, ks);
     for (int32_t k : ks) {
       for (int32_t u = 0; u < g.c; ++u) {
         int64_t t = int64_t(k) * g.c + u;
@@ -96,7 +99,8 @@ void pair_counts(const Meta& m, int64_t* padded, int64_t* real) {
     int64_t img = int64_t(g.n_img) * (g.n_img + 1) / 2;  // image row i sees i + 1 keys
     pp += img;
     rr += img;
-    const int32_t ks[2] = {r, 2 * P - 1 - r};
+    int32_t ks[2];
+    owned_chunks(m, r, ks);
     for (int32_t k : ks) {
       int64_t lo = int64_t(k) * g.c;
       pp += text_pairs(g, lo, g.c);
@@ -113,7 +117,8 @@ std::vector<Segment> segments(const Meta& m) {
   for (size_t s = 0; s < m.samples.size(); ++s) {
     const SampleGeom& g = m.samples[s];
     if (g.n_img > 0) out.push_back({g.local0, g.a, g.n_img, int32_t(s), 0});
-    const int32_t ks[2] = {r, 2 * P - 1 - r};
+    int32_t ks[2];
+    owned_chunks(m, r, ks);
     for (int kind = 1; kind <= 2; ++kind) {
       int32_t k = ks[kind - 1];
       int32_t len = chunk_real(g, k);
@@ -130,7 +135,8 @@ void step_ranges(const Meta& m, int32_t sample, int32_t step, std::vector<SpanRe
   const int32_t P = m.P;
   const int32_t j = ((m.r - step) % P + P) % P;  // source rank of this ring step
   if (step == 0 && g.n_img > 0) out.push_back({int32_t(g.a), int32_t(g.a + g.n_img)});
-  const int32_t ks[2] = {j, 2 * P - 1 - j};
+  int32_t ks[2];
+  owned_chunks(m, j, ks);
   for (int32_t k : ks) {
     int32_t len = chunk_real(g, k);
     if (len == 0) continue;

@@ -25,7 +25,7 @@ struct Segment {
   int64_t g0;       // global id of that row
   int32_t len;      // rows
   int32_t sample;
-  int32_t kind;     // 0 image, 1 chunk r, 2 chunk 2P-1-r
+  int32_t kind;     // 0 image, 1 first owned chunk, 2 second owned chunk
 };
 
 // Tile shapes of the attention kernels. Each bf16 wave owns 32 query rows
@@ -54,6 +54,7 @@ TileShape tile_shape(int32_t dtype, int32_t group, int32_t head_dim);
 struct Meta {
   int64_t seq_len = 0;
   int32_t P = 1, r = 0;
+  int32_t split = 0;  // CP_SPLIT_HEAD_TAIL or CP_SPLIT_CONTIGUOUS
   std::vector<SampleGeom> samples;
   int64_t rows = 0;  // R
 };
@@ -61,7 +62,20 @@ struct Meta {
 // Checks (seq_len, n_img, cu_seqlens, n_samples, cp_size, cp_rank) and fills
 // `m`. Returns a cp_status value.
 int32_t build_meta(int64_t seq_len, const int32_t* n_img, const int32_t* cu_seqlens,
-                   int32_t n_samples, int32_t cp_size, int32_t cp_rank, Meta& m);
+                   int32_t n_samples, int32_t cp_size, int32_t cp_rank, Meta& m,
+                   int32_t split = 0);
+
+// The two text chunks (of 2P) that rank `rank` holds, in local order:
+// head-tail pairing {rank, 2P-1-rank}; contiguous split {2rank, 2rank+1}.
+inline void owned_chunks(const Meta& m, int32_t rank, int32_t ks[2]) {
+  if (m.split == 1) {
+    ks[0] = 2 * rank;
+    ks[1] = 2 * rank + 1;
+  } else {
+    ks[0] = rank;
+    ks[1] = 2 * m.P - 1 - rank;
+  }
+}
 
 void fill_index(const Meta& m, int32_t* index, int32_t* cu_rows_local);
 void pair_counts(const Meta& m, int64_t* padded, int64_t* real);

@@ -14,11 +14,12 @@ int32_t vt_row_keys(int64_t seq_len) { return int32_t((seq_len + 63 + 63) / 64 *
 
 int32_t prepare_workspace(int64_t seq_len, const int32_t* n_img, const int32_t* cu_seqlens,
                           int32_t n_samples, int32_t cp_size, int32_t cp_rank, int32_t heads,
-                          int32_t kv_heads, int32_t head_dim, int32_t dtype, Workspace& w) {
+                          int32_t kv_heads, int32_t head_dim, int32_t dtype, Workspace& w,
+                          int32_t split) {
   if (dtype != CP_DTYPE_F32 && dtype != CP_DTYPE_BF16) return CP_EUNSUPPORTED;
   if (heads < 1 || kv_heads < 1 || heads % kv_heads != 0) return CP_EINVAL;
   if (head_dim != 64 && head_dim != 128) return CP_EUNSUPPORTED;
-  int32_t st = build_meta(seq_len, n_img, cu_seqlens, n_samples, cp_size, cp_rank, w.meta);
+  int32_t st = build_meta(seq_len, n_img, cu_seqlens, n_samples, cp_size, cp_rank, w.meta, split);
   if (st != CP_OK) return st;
   w.heads = heads;
   w.kv_heads = kv_heads;

@@ -33,7 +33,8 @@ struct Workspace {
 // Checks every argument, builds the plan and the layout. Returns a cp_status.
 int32_t prepare_workspace(int64_t seq_len, const int32_t* n_img, const int32_t* cu_seqlens,
                           int32_t n_samples, int32_t cp_size, int32_t cp_rank, int32_t heads,
-                          int32_t kv_heads, int32_t head_dim, int32_t dtype, Workspace& w);
+                          int32_t kv_heads, int32_t head_dim, int32_t dtype, Workspace& w,
+                          int32_t split = 0);
 
 // Keys per V^T row: a multiple of 64 that covers every 64-key window
 // starting below seq_len.

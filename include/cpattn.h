@@ -65,6 +65,18 @@ enum { CP_DTYPE_F32 = 0, CP_DTYPE_BF16 = 1 };
 #define CP_MAX_CP_SIZE 32
 
 /*
+ * How the text of a sample is split over the CP group (the *_ex entry
+ * points). Both view the padded text as 2P chunks of c = ceil(T/2P).
+ *   CP_SPLIT_HEAD_TAIL: rank r holds chunks r and 2P-1-r (the context-
+ *     parallel multimodal page, section 1.1: equal causal work per rank).
+ *   CP_SPLIT_CONTIGUOUS: rank r holds chunks 2r and 2r+1, i.e. the r-th
+ *     contiguous P-th of the text -- the plain split that section 1.1
+ *     describes as unbalanced under a causal mask (later ranks do more).
+ * The entry points without the suffix use CP_SPLIT_HEAD_TAIL.
+ */
+enum { CP_SPLIT_HEAD_TAIL = 0, CP_SPLIT_CONTIGUOUS = 1 };
+
+/*
  * cp_partition_index -- rows of one CP rank (host only, integer, exact).
  *
  * Page section 1.1 (chunks [cp_rank, 2*cp_size-cp_rank-1]), section 4.1
@@ -210,6 +222,39 @@ cp_status cp_lse_merge(const float *part_out, const float *part_lse, const uint3
                        int32_t dtype, void *out, float *lse, void *stream);
 
 /* Static English text for a status code. */
+/*
+ * The same operations with an explicit split (CP_SPLIT_*). An unknown
+ * split returns CP_EUNSUPPORTED and writes nothing. Everything else --
+ * arguments, layouts, errors -- is as for the entry point without the
+ * suffix; cp_attn_rank_fwd_ex also takes the optional six events of
+ * cp_attn_rank_fwd_timed (NULL: none). A workspace sized for one split is
+ * not valid for the other.
+ */
+cp_status cp_partition_index_ex(int64_t seq_len, const int32_t *n_img, const int32_t *cu_seqlens,
+                                int32_t n_samples, int32_t cp_size, int32_t cp_rank, int32_t split,
+                                int32_t *index, int64_t capacity, int64_t *n_rows,
+                                int32_t *cu_rows_local);
+cp_status cp_pair_counts_ex(int64_t seq_len, const int32_t *n_img, const int32_t *cu_seqlens,
+                            int32_t n_samples, int32_t cp_size, int32_t cp_rank, int32_t split,
+                            int64_t *pairs_padded, int64_t *pairs_real);
+cp_status cp_attn_rank_workspace_size_ex(int64_t seq_len, const int32_t *n_img,
+                                         const int32_t *cu_seqlens, int32_t n_samples,
+                                         int32_t cp_size, int32_t cp_rank, int32_t split,
+                                         int32_t heads, int32_t kv_heads, int32_t head_dim,
+                                         int32_t dtype, size_t *bytes);
+cp_status cp_attn_rank_plan_stats_ex(int64_t seq_len, const int32_t *n_img,
+                                     const int32_t *cu_seqlens, int32_t n_samples, int32_t cp_size,
+                                     int32_t cp_rank, int32_t split, int32_t heads,
+                                     int32_t kv_heads, int32_t head_dim, int32_t dtype,
+                                     int64_t *n_tiles, int64_t *n_entries, int64_t *kv_tiles,
+                                     int64_t *covered_pairs, int64_t *step_pairs);
+cp_status cp_attn_rank_fwd_ex(const void *q, const void *k, const void *v, int32_t dtype,
+                              int64_t seq_len, const int32_t *n_img, const int32_t *cu_seqlens,
+                              int32_t n_samples, int32_t cp_size, int32_t cp_rank, int32_t split,
+                              int32_t heads, int32_t kv_heads, int32_t head_dim, void *out,
+                              float *lse, void *workspace, size_t workspace_bytes, void *stream,
+                              void *const *events);
+
 const char *cp_status_string(cp_status s);
 
 #ifdef __cplusplus

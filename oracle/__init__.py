@@ -33,6 +33,7 @@ them only against this oracle.
 """
 from .cp_oracle import (  # noqa: F401
     chunk_len,
+    owned_chunks,
     partition_index,
     pair_counts,
     attend,

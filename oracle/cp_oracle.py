@@ -12,6 +12,7 @@ import numpy as np
 
 __all__ = [
     "chunk_len",
+    "owned_chunks",
     "partition_index",
     "pair_counts",
     "attend",
@@ -50,8 +51,25 @@ def chunk_len(text_len: int, cp_size: int) -> int:
     return -(-int(text_len) // (2 * int(cp_size)))
 
 
-def partition_index(seq_len: int, n_img, cu_seqlens, cp_size: int, cp_rank: int
-                    ) -> Tuple[np.ndarray, np.ndarray]:
+def owned_chunks(cp_size: int, cp_rank: int, split: str = "head_tail") -> np.ndarray:
+    """The two of the 2P text chunks a rank holds, in its local order.
+
+    Context-parallel multimodal page, §1.1: head-tail pairing gives rank r
+    chunks [r, 2P - r - 1]. The page contrasts it with the plain split into
+    P contiguous pieces, which loads the later ranks more under a causal
+    mask; on the same 2P chunks that split gives rank r chunks [2r, 2r + 1]
+    ("contiguous").
+    """
+    P, r = int(cp_size), int(cp_rank)
+    if split == "head_tail":
+        return np.array([r, 2 * P - r - 1])
+    if split == "contiguous":
+        return np.array([2 * r, 2 * r + 1])
+    raise ValueError(f"unknown split {split!r}")
+
+
+def partition_index(seq_len: int, n_img, cu_seqlens, cp_size: int, cp_rank: int,
+                    split: str = "head_tail") -> Tuple[np.ndarray, np.ndarray]:
     """Global token ids of the rows rank ``cp_rank`` holds, -1 for pads.
 
     Follows the page's steps literally, per sample:
@@ -59,7 +77,9 @@ def partition_index(seq_len: int, n_img, cu_seqlens, cp_size: int, cp_rank: int
     * §4.1: the image prefix is kept whole (every rank gets all of it) and
       only the text is split;
     * §1.1: the (padded) text is viewed as 2P chunks and rows
-      [cp_rank, 2*cp_size - cp_rank - 1] are index-selected, in that order;
+      [cp_rank, 2*cp_size - cp_rank - 1] are index-selected, in that order
+      (``split="contiguous"``: rows [2*cp_rank, 2*cp_rank + 1], see
+      ``owned_chunks``);
     * §5.3: with packed samples the split is done per sample, using the
       cu_seqlens boundaries; samples keep their order.
 
@@ -79,7 +99,7 @@ def partition_index(seq_len: int, n_img, cu_seqlens, cp_size: int, cp_rank: int
         padded = np.full(2 * P * c, -1, dtype=np.int64)
         padded[: len(text_ids)] = text_ids
         chunks = padded.reshape(2 * P, c)
-        select = np.array([r, 2 * P - r - 1])
+        select = owned_chunks(P, r, split)
         mine = chunks[select].reshape(-1)
         local = np.concatenate([image_ids, mine])
         pieces.append(local)
@@ -88,8 +108,8 @@ def partition_index(seq_len: int, n_img, cu_seqlens, cp_size: int, cp_rank: int
     return index.astype(np.int32), np.asarray(cu_rows, dtype=np.int32)
 
 
-def pair_counts(seq_len: int, n_img, cu_seqlens, cp_size: int, cp_rank: int
-                ) -> Tuple[int, int]:
+def pair_counts(seq_len: int, n_img, cu_seqlens, cp_size: int, cp_rank: int,
+                split: str = "head_tail") -> Tuple[int, int]:
     """Unmasked (query, key) pairs per head on one rank: (padded, real).
 
     With the causal mask a query at position p inside its sample sees keys
@@ -109,7 +129,7 @@ def pair_counts(seq_len: int, n_img, cu_seqlens, cp_size: int, cp_rank: int
         c = chunk_len(T, P)
         # positions inside the sample of every row this rank holds,
         # pads included at their padded offsets
-        offsets = np.arange(2 * P * c).reshape(2 * P, c)[[r, 2 * P - r - 1]].reshape(-1)
+        offsets = np.arange(2 * P * c).reshape(2 * P, c)[owned_chunks(P, r, split)].reshape(-1)
         positions = np.concatenate([np.arange(n), n + offsets])
         is_real = np.concatenate([np.ones(n, bool), offsets < T])
         padded_total += int(np.sum(positions + 1))
@@ -212,8 +232,8 @@ def causal_attention(q, k, v, cu_seqlens=None, rows: Optional[Sequence[int]] = N
 
 
 def rank_attention(q, k, v, n_img, cu_seqlens, cp_size: int, cp_rank: int,
-                   local_rows: Optional[Sequence[int]] = None, literal: bool = False
-                   ) -> Tuple[np.ndarray, np.ndarray]:
+                   local_rows: Optional[Sequence[int]] = None, literal: bool = False,
+                   split: str = "head_tail") -> Tuple[np.ndarray, np.ndarray]:
     """The rows of full-sequence causal attention that one CP rank holds.
 
     out [R, H, D], lse [H, R] in the rank-local row order of
@@ -224,7 +244,7 @@ def rank_attention(q, k, v, n_img, cu_seqlens, cp_size: int, cp_rank: int,
     because each row depends only on its own visible keys.
     """
     T, H, D = (int(x) for x in q.shape)
-    index, _ = partition_index(T, n_img, cu_seqlens, cp_size, cp_rank)
+    index, _ = partition_index(T, n_img, cu_seqlens, cp_size, cp_rank, split)
     if local_rows is None:
         local_rows = np.arange(len(index))
     local_rows = np.asarray(local_rows, dtype=np.int64)

@@ -51,5 +51,5 @@ def compare(out_gpu, lse_gpu, out_ref, lse_ref, dtype: str, what: str):
     return err_o, err_l
 
 
-def oracle_rows(q, k, v, n_img, cu, P, r, rows=None):
-    return oracle.rank_attention(q, k, v, n_img, cu, P, r, local_rows=rows)
+def oracle_rows(q, k, v, n_img, cu, P, r, rows=None, split="head_tail"):
+    return oracle.rank_attention(q, k, v, n_img, cu, P, r, local_rows=rows, split=split)

@@ -68,6 +68,44 @@ def test_partition_matches_oracle_random(cp):
         assert cp.pair_counts(T, n_img, cu, cp_size=P, cp_rank=r) == oracle.pair_counts(T, n_img, cu, P, r)
 
 
+def test_contiguous_split_matches_oracle(cp):
+    rng = np.random.default_rng(3)
+    for trial in range(200):
+        n = int(rng.integers(1, 5))
+        n_img, cu = workloads.random_meta(rng, n, 40, 200)
+        T = int(cu[-1])
+        P = int(rng.integers(1, 9))
+        r = int(rng.integers(0, P))
+        a, acu = cp.partition_index(T, n_img, cu, cp_size=P, cp_rank=r, split="contiguous")
+        b, bcu = oracle.partition_index(T, n_img, cu, P, r, split="contiguous")
+        assert np.array_equal(a, b) and np.array_equal(acu, bcu), (trial, n_img, cu, P, r)
+        assert cp.pair_counts(T, n_img, cu, cp_size=P, cp_rank=r, split="contiguous") == \
+            oracle.pair_counts(T, n_img, cu, P, r, split="contiguous")
+        H, Hkv = [(4, 4), (8, 2)][trial % 2]
+        st = cp.plan_stats(T, n_img, cu, cp_size=P, cp_rank=r, heads=H, kv_heads=Hkv, head_dim=128,
+                           dtype=trial % 2, split="contiguous")
+        assert st["covered_pairs"] == oracle.pair_counts(T, n_img, cu, P, r, split="contiguous")[1]
+    # ring steps of the plain split: rank r sees source ranks j <= r only
+    L, P = 8192, 4
+    c = L // (2 * P)
+    for r in range(P):
+        st = cp.plan_stats(L, cp_size=P, cp_rank=r, heads=4, kv_heads=4, head_dim=128, dtype=1,
+                           split="contiguous")
+        want = [0] * P
+        for s in range(P):
+            j = (r - s) % P
+            want[s] = (2 * c) * (2 * c + 1) // 2 if j == r else (4 * c * c if j < r else 0)
+        assert st["step_pairs"] == want, (r, st["step_pairs"], want)
+
+
+def test_unknown_split_is_rejected(cp):
+    idx = np.full(4, 77, np.int32)
+    rows = ctypes.c_int64(-5)
+    st = cp.cp_partition_index_ex(16, None, None, 1, 2, 0, 7, idx.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                  4, ctypes.byref(rows), None)
+    assert st == cp.CP_EUNSUPPORTED and rows.value == -5 and np.all(idx == 77)
+
+
 def test_single_sample_null_meta(cp):
     a, _ = cp.partition_index(1000, cp_size=3, cp_rank=2)
     b, _ = oracle.partition_index(1000, None, None, 3, 2)

@@ -38,16 +38,16 @@ def draw(seed, T, H, Hkv, D, dtype, q_scale=1.0):
     return [torch.from_numpy(a).to(dt) for a in (q, k, v)]
 
 
-def run_case(cp, q, k, v, n_img, cu, P, r, dtype, rows=None, what=""):
+def run_case(cp, q, k, v, n_img, cu, P, r, dtype, rows=None, what="", split="head_tail"):
     print(f"case {what} T={q.shape[0]} H={q.shape[1]} Hkv={k.shape[1]} D={q.shape[2]} P={P} r={r} "
-          f"dtype={dtype}", flush=True)
+          f"dtype={dtype} split={split}", flush=True)
     out, lse = cp.rank_fwd(q.to(DEV), k.to(DEV), v.to(DEV), cp_size=P, cp_rank=r, n_img=n_img,
-                           cu_seqlens=cu)
+                           cu_seqlens=cu, split=split)
     torch.cuda.synchronize()
     if rows is None:
-        ro, rl = oracle_rows(q, k, v, n_img, cu, P, r)
+        ro, rl = oracle_rows(q, k, v, n_img, cu, P, r, split=split)
         return compare(out, lse, ro, rl, dtype, what)
-    ro, rl = oracle_rows(q, k, v, n_img, cu, P, r, rows)
+    ro, rl = oracle_rows(q, k, v, n_img, cu, P, r, rows, split=split)
     return compare(out[torch.as_tensor(rows, device=DEV)], lse[:, torch.as_tensor(rows, device=DEV)],
                    ro, rl, dtype, what)
 
@@ -114,6 +114,8 @@ SMALL = [
     ("bf16-packed", [33, 0, 130, 7], [260, 45, 3, 700], 4, 4, 128, 4, "bf16"),
     ("bf16-all-image", [64, 100], [0, 129], 2, 2, 128, 2, "bf16"),
     ("bf16-P8-short", [0, 3], [9, 100], 2, 2, 128, 8, "bf16"),
+    ("bf16-P32-gqa4", [0], [3000], 4, 1, 128, 32, "bf16"),
+    ("bf16-gqa3", [11], [900], 6, 2, 128, 3, "bf16"),
 ]
 
 
@@ -126,6 +128,26 @@ def test_small_all_ranks(cp, case):
     q, k, v = draw(zlib.crc32(name.encode()) % 1000, T, H, Hkv, D, dtype)
     for r in range(P):
         run_case(cp, q, k, v, np.array(n_img, np.int32), cu, P, r, dtype, what=f"{name} r={r}")
+
+
+CONTIGUOUS = [
+    ("contig-f32", [0], [1000], 4, 2, 128, 3, "f32"),
+    ("contig-bf16-packed", [21, 0, 40], [700, 90, 333], 8, 2, 128, 4, "bf16"),
+    ("contig-bf16-d64", [0], [500], 4, 4, 64, 2, "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", CONTIGUOUS, ids=[c[0] for c in CONTIGUOUS])
+def test_contiguous_split_all_ranks(cp, case):
+    # the plain P-way split (section 1.1's unbalanced baseline) through the same kernels
+    name, n_img, text, H, Hkv, D, P, dtype = case
+    lens = np.array(n_img) + np.array(text)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(cu[-1])
+    q, k, v = draw(zlib.crc32(name.encode()) % 1000, T, H, Hkv, D, dtype)
+    for r in range(P):
+        run_case(cp, q, k, v, np.array(n_img, np.int32), cu, P, r, dtype, what=f"{name} r={r}",
+                 split="contiguous")
 
 
 def test_peaky_softmax(cp):

@@ -321,6 +321,38 @@ def test_naive_contiguous_split_is_unbalanced():
     assert len(balanced) == 1
 
 
+def test_contiguous_split_is_the_plain_split():
+    # section 1.1's plain split: rank r holds the r-th contiguous P-th of the
+    # (padded) text, so concatenating ranks 0..P-1 gives the text in order;
+    # the image prefix stays whole on every rank
+    for T, n, P in ((8192, 0, 4), (1001, 37, 3), (5, 2, 4)):
+        c = -(-T // (2 * P))
+        text = [t for t in range(n, n + T)] + [-1] * (2 * P * c - T)
+        joined = []
+        for r in range(P):
+            idx, cu_rows = oracle.partition_index(n + T, [n], None, P, r, split="contiguous")
+            assert list(idx[:n]) == list(range(n)) and list(cu_rows) == [0, len(idx)]
+            joined += list(idx[n:])
+            assert list(idx[n:]) == text[2 * r * c:(2 * r + 2) * c]
+        assert joined == text
+
+
+def test_contiguous_split_pair_counts_skew():
+    # per-rank causal pairs of the plain split grow as 1:3:5:7 for P=4
+    # (section 1.1: later tokens attend to more tokens); brute force
+    L, P = 8192, 4
+    per = L // P
+    for r in range(P):
+        brute = sum(p + 1 for p in range(r * per, (r + 1) * per))
+        assert oracle.pair_counts(L, None, None, P, r, split="contiguous") == (brute, brute)
+    pairs = [oracle.pair_counts(L, None, None, P, r, split="contiguous")[1] for r in range(P)]
+    assert [round(x / (per * per // 2)) for x in pairs] == [1, 3, 5, 7]
+    # both splits cover every causal pair once over the ranks
+    total = L * (L + 1) // 2
+    assert sum(pairs) == total
+    assert sum(oracle.pair_counts(L, None, None, P, r)[1] for r in range(P)) == total
+
+
 def test_brute_force():
     assert pin_brute_force() < 1e-12
 
@@ -446,8 +478,8 @@ def test_mutant_split_image_breaks_invariant3(monkeypatch):
     # section 3.1's failure mode: cutting the image together with the text
     real = cp_oracle.partition_index
 
-    def naive(seq_len, n_img, cu, P, r):
-        return real(seq_len, None, cu, P, r)
+    def naive(seq_len, n_img, cu, P, r, split="head_tail"):
+        return real(seq_len, None, cu, P, r, split)
     monkeypatch.setattr(cp_oracle, "partition_index", naive)
     assert pin_image_rows_identical() > 0 or pin_reassembly() > 0
 
