@@ -731,11 +731,30 @@ void attn_rank_bf16_d128_kernel(const AttnArgs a) {
     }
   }
 
+  const float lt = sum_with_partner(l);
+  if (a.per_step) {
+    // One step per unit (small grids): this step's partial goes out in the
+    // [P, R, H, D] / [P, H, R] layout for the separate LSE merge pass.
+    if (!row_ok) return;
+    const int step = steps[0].step;
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    float* const po = a.part_o + ((int64_t(step) * a.R + lrow) * a.H + h) * D + 4 * hh;
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+      for (int tq = 0; tq < 4; ++tq)
+        *reinterpret_cast<float4*>(po + 32 * db + 8 * tq) =
+            make_float4(o[db][4 * tq] * inv, o[db][4 * tq + 1] * inv, o[db][4 * tq + 2] * inv,
+                        o[db][4 * tq + 3] * inv);
+    if (hh == 0)
+      a.part_lse[(int64_t(step) * a.H + h) * a.R + lrow] =
+          lt > 0.f ? m_ref * a.scale + logf(lt) : -INFINITY;
+    return;
+  }
   // LSE merge of the unit's ring steps (Ring Attention's combination of
   // blockwise results): the last step is still in registers, the others
   // are in this wave's slots. m = max over steps of lse_s; w_s =
   // exp(lse_s - m); out = sum_s w_s O_s / sum_s w_s; lse = m + ln sum_s w_s.
-  const float lt = sum_with_partner(l);
   const float lse_last = lt > 0.f ? m_ref * a.scale + logf(lt) : -INFINITY;
   float m = lse_last;
   for (int st = 0; st < n_steps - 1; ++st)

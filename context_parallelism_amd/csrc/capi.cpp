@@ -128,7 +128,8 @@ cp_status rank_fwd(const void* q, const void* k, const void* v, int32_t dtype, i
     a.scale = float(1.0 / std::sqrt(double(head_dim)));
     a.scale_log2 = float(1.4426950408889634 / std::sqrt(double(head_dim)));
     const int n_entries = int(w.plan.entries.size());
-    if (w.unit_kernel) {
+    a.per_step = w.unit_per_step ? 1 : 0;
+    if (w.unit_kernel && !w.unit_per_step) {
       // all ring steps of a row tile in one workgroup, merged in the kernel
       if (launch_attn_bf16_units(a, w.shape.heads_per_wg, int(w.plan.units.size()), s) != hipSuccess)
         return CP_EHIP;
@@ -139,7 +140,11 @@ cp_status rank_fwd(const void* q, const void* k, const void* v, int32_t dtype, i
       if (mark(events, 5, s) != hipSuccess) return CP_EHIP;
       return CP_OK;
     }
-    hipError_t e = dtype == CP_DTYPE_BF16
+    // per-step partials for the merge pass: small bf16 head_dim-128 grids
+    // (unit kernel, one step per unit), head_dim 64, fp32
+    hipError_t e = w.unit_kernel
+                       ? launch_attn_bf16_units(a, w.shape.heads_per_wg, int(w.plan.step_units.size()), s)
+                   : dtype == CP_DTYPE_BF16
                        ? launch_attn_bf16(a, head_dim, w.shape.heads_per_wg, n_entries, s)
                        : launch_attn_f32(a, head_dim, n_entries, s);
     if (e != hipSuccess) return CP_EHIP;

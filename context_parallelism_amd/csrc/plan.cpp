@@ -203,6 +203,17 @@ void build_plan(const Meta& m, int32_t bm, int32_t bn, Plan& p) {
                    [](const PendingUnit& x, const PendingUnit& y) { return x.cost > y.cost; });
   p.units.reserve(units.size());
   for (const PendingUnit& u : units) p.units.push_back(u.u);
+  // step units: every entry alone, same order as the entries below
+  {
+    std::vector<PendingUnit> su;
+    su.reserve(pend.size());
+    for (size_t i = 0; i < pend.size(); ++i)
+      su.push_back({UnitRec{pend[i].e.tile, int32_t(i), int32_t(i) + 1, 0}, pend[i].cost});
+    std::stable_sort(su.begin(), su.end(),
+                     [](const PendingUnit& x, const PendingUnit& y) { return x.cost > y.cost; });
+    p.step_units.reserve(su.size());
+    for (const PendingUnit& u : su) p.step_units.push_back(u.u);
+  }
   std::stable_sort(pend.begin(), pend.end(),
                    [](const Pending& x, const Pending& y) { return x.cost > y.cost; });
   p.entries.reserve(pend.size());

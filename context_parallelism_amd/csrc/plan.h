@@ -95,6 +95,7 @@ struct Plan {
   std::vector<EntryRec> entries;  // launch order: longest first
   std::vector<EntryRec> tile_entries;  // the same entries in (tile, step) order
   std::vector<UnitRec> units;          // one per row tile, launch order: longest first
+  std::vector<UnitRec> step_units;     // one per entry (a single step), longest first
   int64_t pad_rows = 0;                // rank-local rows with index -1
   std::vector<SpanRec> spans;
   std::vector<uint32_t> row_mask;  // per rank-local row: steps with a partial

@@ -1,5 +1,6 @@
 #include "workspace.h"
 
+#include <cstdlib>
 #include <cstring>
 
 #include "cpattn.h"
@@ -9,6 +10,14 @@ namespace cpattn {
 namespace {
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 }  // namespace
+
+int64_t unit_min_workgroups() {
+  const char* env = std::getenv("CPATTN_UNIT_MIN_WORKGROUPS");
+  if (env == nullptr || *env == 0) return kUnitMinWorkgroups;
+  char* end = nullptr;
+  const long long v = std::strtoll(env, &end, 10);
+  return (end != env && v >= 0) ? int64_t(v) : kUnitMinWorkgroups;
+}
 
 int32_t vt_row_keys(int64_t seq_len) { return int32_t((seq_len + 63 + 63) / 64 * 64); }
 
@@ -42,8 +51,13 @@ int32_t prepare_workspace(int64_t seq_len, const int32_t* n_img, const int32_t* 
   off = align256(off + w.plan.spans.size() * sizeof(SpanRec));
   w.off_tile_entries = off;
   off = align256(off + w.plan.tile_entries.size() * sizeof(EntryRec));
+  w.unit_kernel = dtype == CP_DTYPE_BF16 && head_dim == 128;
+  if (w.unit_kernel) {
+    const int64_t n_hg = heads / w.shape.heads_per_wg;
+    w.unit_per_step = int64_t(w.plan.units.size()) * n_hg < unit_min_workgroups();
+  }
   w.off_units = off;
-  off = align256(off + w.plan.units.size() * sizeof(UnitRec));
+  off = align256(off + w.launch_units().size() * sizeof(UnitRec));
   w.plan_bytes = off;
   w.off_qr = off;
   off = align256(off + R * size_t(heads) * head_dim * esize);
@@ -52,9 +66,8 @@ int32_t prepare_workspace(int64_t seq_len, const int32_t* n_img, const int32_t* 
     w.tpad = vt_row_keys(seq_len);
     off = align256(off + size_t(kv_heads) * head_dim * size_t(w.tpad) * 2);
   }
-  w.unit_kernel = dtype == CP_DTYPE_BF16 && head_dim == 128;
   w.off_po = off;
-  if (w.unit_kernel) {
+  if (w.unit_kernel && !w.unit_per_step) {
     const size_t n_hg = size_t(heads / w.shape.heads_per_wg);
     off = align256(off + w.plan.units.size() * n_hg * size_t(cp_size) * kUnitWaves *
                              kUnitSlotFloats * sizeof(float));
@@ -80,7 +93,8 @@ void pack_plan(const Workspace& w, uint8_t* dst) {
   if (!p.spans.empty()) std::memcpy(dst + w.off_spans, p.spans.data(), p.spans.size() * sizeof(SpanRec));
   if (!p.tile_entries.empty())
     std::memcpy(dst + w.off_tile_entries, p.tile_entries.data(), p.tile_entries.size() * sizeof(EntryRec));
-  if (!p.units.empty()) std::memcpy(dst + w.off_units, p.units.data(), p.units.size() * sizeof(UnitRec));
+  const std::vector<UnitRec>& u = w.launch_units();
+  if (!u.empty()) std::memcpy(dst + w.off_units, u.data(), u.size() * sizeof(UnitRec));
 }
 
 }  // namespace cpattn

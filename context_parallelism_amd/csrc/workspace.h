@@ -25,10 +25,22 @@ struct Workspace {
   size_t off_index = 0, off_mask = 0, off_tiles = 0, off_entries = 0, off_spans = 0;
   size_t off_tile_entries = 0, off_units = 0;
   bool unit_kernel = false;  // bf16 head_dim 128: units with the in-kernel merge
+  bool unit_per_step = false;  // ... but one step per unit and the merge pass (small grids)
+  const std::vector<UnitRec>& launch_units() const {
+    return unit_per_step ? plan.step_units : plan.units;
+  }
   size_t plan_bytes = 0;
   size_t off_qr = 0, off_vt = 0, off_po = 0, off_pl = 0, total = 0;
   int32_t tpad = 0;  // keys per V^T row (0: no V^T region)
 };
+
+// Below this many workgroups the unit kernel takes one ring step per unit
+// (more, smaller workgroups) and the steps are merged in a separate pass:
+// two workgroups per compute unit of a 256-CU MI355X. The environment
+// variable CPATTN_UNIT_MIN_WORKGROUPS overrides it (read at every call; the
+// tests use it to run small problems through both modes).
+constexpr int64_t kUnitMinWorkgroups = 512;
+int64_t unit_min_workgroups();
 
 // Checks every argument, builds the plan and the layout. Returns a cp_status.
 int32_t prepare_workspace(int64_t seq_len, const int32_t* n_img, const int32_t* cu_seqlens,

@@ -119,15 +119,26 @@ SMALL = [
 ]
 
 
+@pytest.fixture(params=["units", "steps"])
+def unit_mode(request, monkeypatch):
+    # bf16 head_dim 128 runs whole row tiles per workgroup with the merge in
+    # the kernel, or -- below a workgroup count -- one ring step per
+    # workgroup and a merge pass; small problems are run through both
+    monkeypatch.setenv("CPATTN_UNIT_MIN_WORKGROUPS", "0" if request.param == "units" else "1000000000")
+    return request.param
+
+
 @pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
-def test_small_all_ranks(cp, case):
+def test_small_all_ranks(cp, case, unit_mode):
     name, n_img, text, H, Hkv, D, P, dtype = case
+    if unit_mode == "steps" and not (dtype == "bf16" and D == 128):
+        pytest.skip("one mode only: per-step kernels")
     lens = np.array(n_img) + np.array(text)
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     T = int(cu[-1])
     q, k, v = draw(zlib.crc32(name.encode()) % 1000, T, H, Hkv, D, dtype)
     for r in range(P):
-        run_case(cp, q, k, v, np.array(n_img, np.int32), cu, P, r, dtype, what=f"{name} r={r}")
+        run_case(cp, q, k, v, np.array(n_img, np.int32), cu, P, r, dtype, what=f"{name} r={r} {unit_mode}")
 
 
 CONTIGUOUS = [
@@ -138,7 +149,7 @@ CONTIGUOUS = [
 
 
 @pytest.mark.parametrize("case", CONTIGUOUS, ids=[c[0] for c in CONTIGUOUS])
-def test_contiguous_split_all_ranks(cp, case):
+def test_contiguous_split_all_ranks(cp, case, unit_mode):
     # the plain P-way split (section 1.1's unbalanced baseline) through the same kernels
     name, n_img, text, H, Hkv, D, P, dtype = case
     lens = np.array(n_img) + np.array(text)
@@ -146,11 +157,11 @@ def test_contiguous_split_all_ranks(cp, case):
     T = int(cu[-1])
     q, k, v = draw(zlib.crc32(name.encode()) % 1000, T, H, Hkv, D, dtype)
     for r in range(P):
-        run_case(cp, q, k, v, np.array(n_img, np.int32), cu, P, r, dtype, what=f"{name} r={r}",
+        run_case(cp, q, k, v, np.array(n_img, np.int32), cu, P, r, dtype, what=f"{name} r={r} {unit_mode}",
                  split="contiguous")
 
 
-def test_peaky_softmax(cp):
+def test_peaky_softmax(cp, unit_mode):
     q, k, v = draw(5, 700, 4, 4, 128, "bf16", q_scale=8.0)
     for r in range(2):
         run_case(cp, q, k, v, None, None, 2, r, "bf16", what=f"peaky r={r}")
@@ -171,6 +182,21 @@ def test_empty_input(cp):
 def workload_inputs(num, device=None):
     w = workloads.get(num)
     return w, workloads.make_inputs(w, device=device)
+
+
+def test_workload2_both_unit_modes_agree(cp, monkeypatch):
+    # the two bf16 head_dim-128 modes on one full-size share: same rows to
+    # within the bf16 bound, pads identical
+    w, (q, k, v) = workload_inputs(2)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    res = []
+    for val in ("0", "1000000000"):
+        monkeypatch.setenv("CPATTN_UNIT_MIN_WORKGROUPS", val)
+        out, lse = cp.rank_fwd(qd, kd, vd, cp_size=w.cp_size, cp_rank=1)
+        torch.cuda.synchronize()
+        res.append((out.float().cpu(), lse.cpu()))
+    assert (res[0][0] - res[1][0]).abs().max().item() <= TOL["bf16"][0]
+    assert (res[0][1] - res[1][1]).abs().max().item() <= TOL["bf16"][1]
 
 
 def test_workload1_full(cp):
