@@ -161,6 +161,50 @@ def compare_splits(w, args):
     print(json.dumps(line), flush=True)
 
 
+def compare_ulysses(w, args):
+    """One GPU's attention share of the same CP job in two layouts: the ring
+    (head-tail rank share, all heads, P steps) and Ulysses (after the
+    all-to-all over heads: every token, heads/P query and kv_heads/P KV
+    heads, one causal pass, no steps). Both hold the same useful work for a
+    single-sample text workload. The all-to-all itself is not run (one GPU)."""
+    import torch
+
+    import context_parallelism_amd as cp
+    import workloads
+
+    P = w.cp_size
+    if w.n_samples != 1 or any(w.n_img) or w.heads % P or w.kv_heads % P:
+        raise SystemExit("--ulysses needs a single-sample text workload whose head counts P divides")
+    dev = torch.device("cuda:0")
+    q, k, v = workloads.make_inputs(w)
+    hip = hip_runtime()
+    res = {}
+    # ring: the headline rank share
+    ra = cp.RankAttention(q.to(dev), k.to(dev), v.to(dev), cp_size=P, cp_rank=w.rank)
+    _, pairs = cp.pair_counts(w.seq_len, cp_size=P, cp_rank=w.rank)
+    call, attn = timed_calls(ra, hip, args.steps, args.warmup)
+    useful = 4.0 * w.head_dim * w.heads * pairs
+    res["ring"] = {"heads": w.heads, "kv_heads": w.kv_heads, "rows": ra.R, "useful_flop": useful,
+                   "call_ms": round(call, 4), "attention_ms": round(attn, 4),
+                   "TFLOPs": round(useful / (call * 1e-3) / 1e12, 2)}
+    del ra
+    # Ulysses: heads [0, H/P) with their KV heads [0, Hkv/P) -- same head map
+    hq, hk = w.heads // P, w.kv_heads // P
+    qu = q[:, :hq].contiguous().to(dev)
+    ku, vu = k[:, :hk].contiguous().to(dev), v[:, :hk].contiguous().to(dev)
+    ru = cp.RankAttention(qu, ku, vu, cp_size=1, cp_rank=0)
+    _, pairs_u = cp.pair_counts(w.seq_len, cp_size=1, cp_rank=0)
+    call, attn = timed_calls(ru, hip, args.steps, args.warmup)
+    useful_u = 4.0 * w.head_dim * hq * pairs_u
+    res["ulysses"] = {"heads": hq, "kv_heads": hk, "rows": ru.R, "useful_flop": useful_u,
+                      "call_ms": round(call, 4), "attention_ms": round(attn, 4),
+                      "TFLOPs": round(useful_u / (call * 1e-3) / 1e12, 2)}
+    line = {"mode": "compare_ulysses", "workload": w.name, "cp_size": P, "steps": args.steps,
+            "warmup": args.warmup, "shares": res,
+            "ring_over_ulysses_time": round(res["ring"]["call_ms"] / res["ulysses"]["call_ms"], 4)}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -177,6 +221,10 @@ def main():
                     help="instead of the headline line: time every rank share under both splits "
                          "and print one JSON line with the per-rank times (the CP step waits for "
                          "the slowest rank)")
+    ap.add_argument("--ulysses", action="store_true",
+                    help="instead of the headline line: one GPU's share under Ulysses (all-to-all "
+                         "over heads: full-sequence causal attention on heads/P and kv_heads/P) next "
+                         "to the ring rank share of the same workload; one JSON line")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="instead of the attention, run --steps plain device copies of this many MiB "
                          "(the reference kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -205,6 +253,9 @@ def main():
     w = workloads.get(args.workload)
     if args.compare_splits:
         compare_splits(w, args)
+        return
+    if args.ulysses:
+        compare_ulysses(w, args)
         return
     rank = w.rank if args.rank is None else args.rank
     if rank != w.rank:

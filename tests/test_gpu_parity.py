@@ -274,3 +274,30 @@ def test_workload2_reassembly_and_equal_work(cp):
         seen[idx] += 1
     assert np.all(seen == 1)
     assert len(pairs) == 1
+
+
+def test_ulysses_share_matches_ring_and_oracle(cp):
+    # the Ulysses layout of the same job (after an all-to-all over heads: all
+    # tokens, heads/P) is plain causal attention (cp_size 1) on a head
+    # subset; its rows must equal the ring rank shares reassembled, and the
+    # oracle on sampled rows
+    w, (q, k, v) = workload_inputs(2)
+    P = w.cp_size
+    hq, hk = w.heads // P, w.kv_heads // P
+    qu, ku, vu = q[:, :hq].contiguous(), k[:, :hk].contiguous(), v[:, :hk].contiguous()
+    ou, lu = cp.rank_fwd(qu.to(DEV), ku.to(DEV), vu.to(DEV), cp_size=1, cp_rank=0)
+    torch.cuda.synchronize()
+    idx, cu_rows = oracle.partition_index(w.seq_len, None, None, 1, 0)
+    rows = sample_rows(idx, cu_rows, 64, seed=77)
+    ro, rl = oracle_rows(qu, ku, vu, None, None, 1, 0, rows)
+    rt = torch.as_tensor(rows, device=DEV)
+    compare(ou[rt], lu[:, rt], ro, rl, "bf16", "ulysses share")
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    for r in range(P):
+        ridx, _ = cp.partition_index(w.seq_len, cp_size=P, cp_rank=r)
+        out, lse = cp.rank_fwd(qd, kd, vd, cp_size=P, cp_rank=r)
+        torch.cuda.synchronize()
+        it = torch.as_tensor(ridx, device=DEV, dtype=torch.long)
+        d_o = (out[:, :hq].float() - ou[it].float()).abs().max().item()
+        d_l = (lse[:hq] - lu[:, it]).abs().max().item()
+        assert d_o <= TOL["bf16"][0] and d_l <= TOL["bf16"][1], (r, d_o, d_l)
