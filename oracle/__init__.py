@@ -42,5 +42,7 @@ from .cp_oracle import (  # noqa: F401
     visible,
     causal_attention,
     rank_attention,
+    attend_backward,
+    rank_attention_backward,
     lse_merge,
 )

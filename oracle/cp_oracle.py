@@ -21,6 +21,8 @@ __all__ = [
     "visible",
     "causal_attention",
     "rank_attention",
+    "attend_backward",
+    "rank_attention_backward",
     "lse_merge",
 ]
 
@@ -262,6 +264,75 @@ def rank_attention(q, k, v, n_img, cu_seqlens, cp_size: int, cp_rank: int,
             out[real] = o
             lse[:, real] = l_
     return out, lse
+
+
+def attend_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, allowed: np.ndarray, scale: float,
+                    dout: np.ndarray) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Gradients of softmax attention (``attend``) for one head.
+
+    With S = q k^T * scale over the allowed keys, P = softmax(S) per row and
+    out = P v, a loss with gradient dout w.r.t. out has (chain rule through
+    the softmax, written out):
+      dV = P^T dout;  dP = dout v^T;  dS = P * (dP - sum_j P_j dP_j);
+      dq = dS k * scale;  dk = dS^T q * scale.
+    Rows with no allowed key contribute nothing. Returns (dq, dk, dv).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    s = np.where(allowed, (q @ k.T) * scale, -np.inf)
+    m = np.max(s, axis=1, initial=-np.inf)
+    any_key = np.isfinite(m)
+    e = np.where(allowed, np.exp(s - np.where(any_key, m, 0.0)[:, None]), 0.0)
+    l = e.sum(axis=1)
+    p = np.zeros_like(e)
+    p[any_key] = e[any_key] / l[any_key, None]
+    dv = p.T @ dout
+    dp = dout @ v.T
+    ds = p * (dp - np.sum(p * dp, axis=1, keepdims=True))
+    return (ds @ k) * scale, (ds.T @ q) * scale, dv
+
+
+def rank_attention_backward(q, k, v, dout, n_img, cu_seqlens, cp_size: int, cp_rank: int,
+                            split: str = "head_tail") -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Gradients of one CP rank's share of causal attention.
+
+    The share is the rank's rows of full-sequence causal attention
+    (``rank_attention``); ``dout`` [R, H, D] is a loss gradient w.r.t. those
+    rows, in the rank-local order. Returns dq [R, H, D] (pad rows 0), and
+    dk, dv [T, Hkv, D]: every key's gradient summed over the rank's rows
+    and over the query heads that read its KV head. Summing dk, dv over all
+    ranks (and scattering every rank's dq back by its index) gives the
+    gradients of the whole sequence -- the reduction the reverse ring or an
+    all-reduce performs across GPUs.
+    """
+    q, k, v, dout = _to64(q), _to64(k), _to64(v), _to64(dout)
+    T, H, D = q.shape
+    Hkv = k.shape[1]
+    scale = softmax_scale(D)
+    index, _ = partition_index(T, n_img, cu_seqlens, cp_size, cp_rank, split)
+    cu = np.array([0, T], dtype=np.int64) if cu_seqlens is None else np.asarray(cu_seqlens, dtype=np.int64)
+    dq = np.zeros((len(index), H, D))
+    dk = np.zeros((T, Hkv, D))
+    dv = np.zeros((T, Hkv, D))
+    ids = index.astype(np.int64)
+    sample_of = np.searchsorted(cu, np.maximum(ids, 0), side="right") - 1
+    for s in range(len(cu) - 1):
+        a, b = int(cu[s]), int(cu[s + 1])
+        sel = np.nonzero((ids >= 0) & (sample_of == s))[0]
+        if len(sel) == 0:
+            continue
+        rows = ids[sel]
+        keys = np.arange(a, b)
+        allowed = visible(keys, rows)
+        for h in range(H):
+            g = kv_head_of(h, H, Hkv)
+            gq, gk, gv = attend_backward(q[rows, h], k[a:b, g], v[a:b, g], allowed, scale, dout[sel, h])
+            dq[sel, h] = gq
+            dk[a:b, g] += gk
+            dv[a:b, g] += gv
+    return dq, dk, dv
 
 
 def lse_merge(outs: Sequence[np.ndarray], lses: Sequence[np.ndarray]

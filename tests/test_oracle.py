@@ -230,6 +230,103 @@ def pin_pair_counts():
     return bad
 
 
+def pin_backward_finite_differences(seed=7, n_checks=24, eps=1e-6):
+    """Analytic rank-share gradients against central differences of the
+    forward oracle's loss sum(out_rank * dout), image prefix and packing."""
+    rng = np.random.default_rng(seed)
+    n_img, cu = np.array([3, 0]), np.array([0, 9, 16])
+    T, H, Hkv, D, P = 16, 4, 2, 4, 2
+    q, k, v = rand_qkv(rng, T, H, Hkv, D)
+    err = 0.0
+    for r in range(P):
+        idx, _ = oracle.partition_index(T, n_img, cu, P, r)
+        dout = rng.standard_normal((len(idx), H, D))
+        dq, dk, dv = oracle.rank_attention_backward(q, k, v, dout, n_img, cu, P, r)
+
+        def loss(qq, kk, vv):
+            o, _ = oracle.rank_attention(qq, kk, vv, n_img, cu, P, r)
+            return float(np.sum(o * dout))
+        for which, arr in (("q", q), ("k", k), ("v", v)):
+            for _ in range(n_checks):
+                i = tuple(int(rng.integers(0, n)) for n in arr.shape)
+                hi, lo = arr.copy(), arr.copy()
+                hi[i] += eps
+                lo[i] -= eps
+                args_hi = {"q": (hi, k, v), "k": (q, hi, v), "v": (q, k, hi)}[which]
+                args_lo = {"q": (lo, k, v), "k": (q, lo, v), "v": (q, k, lo)}[which]
+                fd = (loss(*args_hi) - loss(*args_lo)) / (2 * eps)
+                if which == "q":
+                    loc = np.nonzero(idx == i[0])[0]
+                    an = dq[loc[0], i[1], i[2]] if len(loc) else 0.0
+                else:
+                    an = (dk if which == "k" else dv)[i]
+                err = max(err, abs(fd - an))
+    return err
+
+
+def pin_backward_torch(seed=8, T=40, H=4, Hkv=2, D=8, P=2):
+    """Against torch fp64 autograd of scaled_dot_product_attention with an
+    explicit causal mask, on the rank's rows (a library routine)."""
+    rng = np.random.default_rng(seed)
+    n_img = np.array([5])
+    q, k, v = rand_qkv(rng, T, H, Hkv, D)
+    err = 0.0
+    for r in range(P):
+        idx, _ = oracle.partition_index(T, n_img, None, P, r)
+        real = idx >= 0
+        dout = rng.standard_normal((len(idx), H, D))
+        dq, dk, dv = oracle.rank_attention_backward(q, k, v, dout, n_img, None, P, r)
+        tq = torch.from_numpy(q).requires_grad_()
+        tk = torch.from_numpy(k).requires_grad_()
+        tv = torch.from_numpy(v).requires_grad_()
+        mask = torch.tril(torch.ones(T, T, dtype=torch.bool))
+        o = torch.nn.functional.scaled_dot_product_attention(
+            tq.permute(1, 0, 2)[None], tk.permute(1, 0, 2)[None], tv.permute(1, 0, 2)[None],
+            attn_mask=mask, enable_gqa=True)[0].permute(1, 0, 2)
+        rows = torch.from_numpy(idx[real].astype(np.int64))
+        (o[rows] * torch.from_numpy(dout[real])).sum().backward()
+        err = max(err, np.abs(tq.grad.numpy()[idx[real]] - dq[real]).max(),
+                  np.abs(tk.grad.numpy() - dk).max(), np.abs(tv.grad.numpy() - dv).max())
+        assert np.all(dq[~real] == 0)
+    return err
+
+
+def pin_backward_reassembly(seed=9, P_list=(2, 4)):
+    """Summing dk, dv over the ranks and scattering dq back by each rank's
+    index gives the unsplit sequence's gradients (cp_size 1)."""
+    rng = np.random.default_rng(seed)
+    n_img, cu = np.array([4, 6]), np.array([0, 30, 57])
+    T, H, Hkv, D = 57, 2, 1, 8
+    q, k, v = rand_qkv(rng, T, H, Hkv, D)
+    dout_full = rng.standard_normal((T, H, D))
+    idx1, _ = oracle.partition_index(T, n_img, cu, 1, 0)
+    dq1, dk1, dv1 = oracle.rank_attention_backward(q, k, v, np.where((idx1 >= 0)[:, None, None],
+                                                                     dout_full[np.maximum(idx1, 0)], 0.0),
+                                                   n_img, cu, 1, 0)
+    full_dq = np.zeros((T, H, D))
+    full_dq[idx1[idx1 >= 0]] = dq1[idx1 >= 0]
+    err = 0.0
+    for P in P_list:
+        dq_sum, dk_sum, dv_sum = np.zeros((T, H, D)), np.zeros((T, Hkv, D)), np.zeros((T, Hkv, D))
+        image_rows = [np.arange(int(cu[s]), int(cu[s]) + int(n_img[s])) for s in range(len(n_img))]
+        image_ids = np.concatenate(image_rows)
+        for r in range(P):
+            idx, _ = oracle.partition_index(T, n_img, cu, P, r)
+            real = idx >= 0
+            # every rank outputs the image rows; the loss takes each token's
+            # gradient once, so image rows carry dout on one rank only
+            dout = np.zeros((len(idx), H, D))
+            keep = real & (~np.isin(idx, image_ids) | (r == 0))
+            dout[keep] = dout_full[idx[keep]]
+            dq, dk, dv = oracle.rank_attention_backward(q, k, v, dout, n_img, cu, P, r)
+            dq_sum[idx[real]] += dq[real]
+            dk_sum += dk
+            dv_sum += dv
+        err = max(err, np.abs(dq_sum - full_dq).max(), np.abs(dk_sum - dk1).max(),
+                  np.abs(dv_sum - dv1).max())
+    return err
+
+
 # ---------------------------------------------------------------- tests of the true oracle
 
 
@@ -351,6 +448,28 @@ def test_contiguous_split_pair_counts_skew():
     total = L * (L + 1) // 2
     assert sum(pairs) == total
     assert sum(oracle.pair_counts(L, None, None, P, r)[1] for r in range(P)) == total
+
+
+def test_backward_finite_differences():
+    assert pin_backward_finite_differences() < 1e-6
+
+
+def test_backward_torch_autograd():
+    assert pin_backward_torch() < 1e-12
+
+
+def test_backward_reassembly():
+    assert pin_backward_reassembly() < 1e-12
+
+
+def test_backward_single_key_row():
+    # a row that sees one key has P = 1 and dS = 0: its dq is exactly zero
+    rng = np.random.default_rng(10)
+    q, k, v = rand_qkv(rng, 8, 2, 2, 4)
+    idx, _ = oracle.partition_index(8, None, None, 2, 0)
+    dout = rng.standard_normal((len(idx), 2, 4))
+    dq, _, dv = oracle.rank_attention_backward(q, k, v, dout, None, None, 2, 0)
+    assert idx[0] == 0 and np.all(dq[0] == 0.0)
 
 
 def test_brute_force():
@@ -502,3 +621,30 @@ def test_mutant_merge_weights_are_caught(monkeypatch):
         return np.mean(np.stack(outs), axis=0), l  # plain average of partials
     monkeypatch.setattr(oracle, "lse_merge", bad)
     assert pin_merge_identity() > 1e-3
+
+
+def test_mutant_backward_dropped_delta_is_caught(monkeypatch):
+    real = cp_oracle.attend_backward
+
+    def bad(q, k, v, allowed, scale, dout):
+        q64, k64, v64, d64 = (np.asarray(x, dtype=np.float64) for x in (q, k, v, dout))
+        s_ = np.where(allowed, (q64 @ k64.T) * scale, -np.inf)
+        m = np.max(s_, axis=1, initial=-np.inf)
+        e = np.where(allowed, np.exp(s_ - np.where(np.isfinite(m), m, 0.0)[:, None]), 0.0)
+        p = e / np.maximum(e.sum(axis=1, keepdims=True), 1e-300)
+        ds = p * (d64 @ v64.T)  # the row term sum_j P_j dP_j dropped
+        return (ds @ k64) * scale, (ds.T @ q64) * scale, p.T @ d64
+    monkeypatch.setattr(cp_oracle, "attend_backward", bad)
+    assert real is not bad
+    assert pin_backward_finite_differences(n_checks=8) > 1e-3
+
+
+def test_mutant_backward_scale_is_caught(monkeypatch):
+    real = cp_oracle.attend_backward
+
+    def bad(q, k, v, allowed, scale, dout):
+        gq, gk, gv = real(q, k, v, allowed, scale, dout)
+        return gq / scale, gk, gv
+    monkeypatch.setattr(cp_oracle, "attend_backward", bad)
+    assert pin_backward_finite_differences(n_checks=8) > 1e-3
+
