@@ -21,6 +21,8 @@ from ._lib import (  # noqa: F401
     SIGNATURES,
     CpError,
     check,
+    cp_attn_rank_bwd,
+    cp_attn_rank_bwd_workspace_size,
     cp_attn_rank_fwd,
     cp_attn_rank_fwd_ex,
     cp_attn_rank_fwd_timed,
@@ -40,11 +42,13 @@ from ._lib import (  # noqa: F401
 from .api import (  # noqa: F401
     SPLITS,
     RankAttention,
+    RankAttentionBackward,
     gather_rows,
     lse_merge,
     pair_counts,
     partition_index,
     plan_stats,
+    rank_bwd,
     rank_fwd,
     workspace_size,
 )

@@ -57,6 +57,13 @@ SIGNATURES = [
     ("cp_attn_rank_fwd_ex", c_int32,
      [c_void_p, c_void_p, c_void_p, c_int32, c_int64, _P32, _P32, c_int32, c_int32, c_int32, c_int32,
       c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p, POINTER(c_void_p)]),
+    ("cp_attn_rank_bwd_workspace_size", c_int32,
+     [c_int64, _P32, _P32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32,
+      POINTER(c_size_t)]),
+    ("cp_attn_rank_bwd", c_int32,
+     [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int64, _P32, _P32, c_int32,
+      c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
+      c_size_t, c_void_p]),
     ("cp_status_string", c_char_p, [c_int32]),
 ]
 
@@ -119,3 +126,5 @@ cp_pair_counts_ex = _fn("cp_pair_counts_ex")
 cp_attn_rank_workspace_size_ex = _fn("cp_attn_rank_workspace_size_ex")
 cp_attn_rank_plan_stats_ex = _fn("cp_attn_rank_plan_stats_ex")
 cp_attn_rank_fwd_ex = _fn("cp_attn_rank_fwd_ex")
+cp_attn_rank_bwd_workspace_size = _fn("cp_attn_rank_bwd_workspace_size")
+cp_attn_rank_bwd = _fn("cp_attn_rank_bwd")

@@ -164,6 +164,65 @@ def rank_fwd(q, k, v, *, cp_size: int, cp_rank: int, n_img=None, cu_seqlens=None
                          cu_seqlens=cu_seqlens, split=split)()
 
 
+class RankAttentionBackward:
+    """Reusable per-rank backward (cp_attn_rank_bwd): plans the sizes once and
+    keeps the gradient and workspace tensors. dq is fp32 [R, H, D] in the
+    rank-local row order; dk, dv are fp32 [T, Hkv, D] over every key."""
+
+    def __init__(self, q, k, v, *, cp_size: int, cp_rank: int, n_img=None, cu_seqlens=None,
+                 split: str = "head_tail"):
+        import torch
+
+        for name, t in (("q", q), ("k", k), ("v", v)):
+            if not t.is_cuda or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous GPU tensor")
+        self.dtype = _dtype_code(q)
+        self.q, self.k, self.v = q, k, v
+        self.T, self.H, self.D = (int(x) for x in q.shape)
+        self.Hkv = int(k.shape[1])
+        self.cp_size, self.cp_rank, self.split = int(cp_size), int(cp_rank), _split_code(split)
+        self._keep, self._cu_p, self._img_p, self.n_samples = _meta(n_img, cu_seqlens)
+        rows = ctypes.c_int64(0)
+        check(_lib.cp_partition_index_ex(self.T, self._img_p, self._cu_p, self.n_samples, self.cp_size,
+                                         self.cp_rank, self.split, None, 0, ctypes.byref(rows), None),
+              "cp_partition_index_ex")
+        self.R = rows.value
+        b = ctypes.c_size_t(0)
+        check(_lib.cp_attn_rank_bwd_workspace_size(self.T, self._img_p, self._cu_p, self.n_samples,
+                                                   self.cp_size, self.cp_rank, self.split, self.H,
+                                                   self.Hkv, self.D, self.dtype, ctypes.byref(b)),
+              "cp_attn_rank_bwd_workspace_size")
+        self.ws_bytes = b.value
+        dev = q.device
+        self.dq = torch.empty((self.R, self.H, self.D), dtype=torch.float32, device=dev)
+        self.dk = torch.empty((self.T, self.Hkv, self.D), dtype=torch.float32, device=dev)
+        self.dv = torch.empty_like(self.dk)
+        self.workspace = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=dev)
+
+    def __call__(self, out, lse, dout):
+        for name, t in (("out", out), ("lse", lse), ("dout", dout)):
+            if not t.is_cuda or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous GPU tensor")
+        if tuple(out.shape) != (self.R, self.H, self.D) or tuple(dout.shape) != (self.R, self.H, self.D):
+            raise ValueError("out and dout must be [R, heads, head_dim] of this rank")
+        if tuple(lse.shape) != (self.H, self.R):
+            raise ValueError("lse must be [heads, R]")
+        check(_lib.cp_attn_rank_bwd(self.q.data_ptr(), self.k.data_ptr(), self.v.data_ptr(), out.data_ptr(),
+                                    lse.data_ptr(), dout.data_ptr(), self.dtype, self.T, self._img_p,
+                                    self._cu_p, self.n_samples, self.cp_size, self.cp_rank, self.split,
+                                    self.H, self.Hkv, self.D, self.dq.data_ptr(), self.dk.data_ptr(),
+                                    self.dv.data_ptr(), self.workspace.data_ptr(), self.ws_bytes,
+                                    _stream(self.q)), "cp_attn_rank_bwd")
+        return self.dq, self.dk, self.dv
+
+
+def rank_bwd(q, k, v, out, lse, dout, *, cp_size: int, cp_rank: int, n_img=None, cu_seqlens=None,
+             split: str = "head_tail"):
+    """Gradients of one rank's share: (dq [R,H,D], dk [T,Hkv,D], dv [T,Hkv,D]), fp32."""
+    return RankAttentionBackward(q, k, v, cp_size=cp_size, cp_rank=cp_rank, n_img=n_img,
+                                 cu_seqlens=cu_seqlens, split=split)(out, lse, dout)
+
+
 def gather_rows(src, index):
     """dst[i] = src[index[i]] (0 where index is -1); src a GPU tensor [N, ...]."""
     import torch

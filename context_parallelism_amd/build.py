@@ -23,12 +23,12 @@ LIB = os.path.join(PKG, "libcpattn.so")
 # Plain C++ (no HIP headers): the planner and the host-only entry points.
 HOST_SOURCES = ["plan.cpp", "workspace.cpp", "capi_host.cpp"]
 # Compiled as HIP for gfx950.
-DEVICE_SOURCES = ["capi.cpp", "gather.hip", "transpose_v.hip", "attn_bf16.hip", "attn_f32.hip",
+DEVICE_SOURCES = ["capi.cpp", "gather.hip", "transpose_v.hip", "attn_bf16.hip", "attn_bwd.hip", "attn_f32.hip",
                   "lse_merge.hip"]
 
 ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}", f"-I{CSRC}", "-Wall", "-Wno-unused-function"]
-# Packed fp32 VALU ops are kept out of the device code.
+# Packed-fp32 VALU instructions are switched off for the device code.
 DEVICE_FLAGS = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 

@@ -26,7 +26,8 @@ struct Staging {
 };
 thread_local Staging t_stage;
 
-hipError_t stage_and_upload(const Workspace& w, void* dst, hipStream_t stream) {
+template <typename Pack>
+hipError_t stage_and_upload(size_t plan_bytes, Pack pack, void* dst, hipStream_t stream) {
   Staging& s = t_stage;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -45,17 +46,17 @@ hipError_t stage_and_upload(const Workspace& w, void* dst, hipStream_t stream) {
     if (e != hipSuccess) return e;
     s.device = dev;
   }
-  if (s.cap < w.plan_bytes) {
+  if (s.cap < plan_bytes) {
     if (s.host) (void)hipHostFree(s.host);
     s.host = nullptr;
     s.cap = 0;
-    size_t cap = w.plan_bytes < (size_t(1) << 20) ? (size_t(1) << 20) : w.plan_bytes * 2;
+    size_t cap = plan_bytes < (size_t(1) << 20) ? (size_t(1) << 20) : plan_bytes * 2;
     e = hipHostMalloc(&s.host, cap, hipHostMallocPortable);
     if (e != hipSuccess) return e;
     s.cap = cap;
   }
-  pack_plan(w, static_cast<uint8_t*>(s.host));
-  e = hipMemcpyAsync(dst, s.host, w.plan_bytes, hipMemcpyHostToDevice, stream);
+  pack(static_cast<uint8_t*>(s.host));
+  e = hipMemcpyAsync(dst, s.host, plan_bytes, hipMemcpyHostToDevice, stream);
   if (e != hipSuccess) return e;
   e = hipEventRecord(s.copied, stream);
   if (e != hipSuccess) return e;
@@ -91,7 +92,8 @@ cp_status rank_fwd(const void* q, const void* k, const void* v, int32_t dtype, i
     const size_t esize = dtype == CP_DTYPE_BF16 ? 2 : 4;
 
     if (mark(events, 0, s) != hipSuccess) return CP_EHIP;
-    if (stage_and_upload(w, ws, s) != hipSuccess) return CP_EHIP;
+    if (stage_and_upload(w.plan_bytes, [&](uint8_t* dst) { pack_plan(w, dst); }, ws, s) != hipSuccess)
+      return CP_EHIP;
     if (mark(events, 1, s) != hipSuccess) return CP_EHIP;
     const int32_t* index = reinterpret_cast<const int32_t*>(ws + w.off_index);
     if (launch_gather(q, index, ws + w.off_qr, R, int64_t(heads) * head_dim * esize, s) != hipSuccess)
@@ -161,9 +163,98 @@ cp_status rank_fwd(const void* q, const void* k, const void* v, int32_t dtype, i
   }
 }
 
+cp_status rank_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                   const void* dout, int32_t dtype, int64_t seq_len, const int32_t* n_img,
+                   const int32_t* cu_seqlens, int32_t n_samples, int32_t cp_size, int32_t cp_rank,
+                   int32_t split, int32_t heads, int32_t kv_heads, int32_t head_dim, float* dq,
+                   float* dk, float* dv, void* workspace, size_t workspace_bytes, void* stream) {
+  try {
+    BwdWorkspace w;
+    int32_t st = prepare_bwd_workspace(seq_len, n_img, cu_seqlens, n_samples, cp_size, cp_rank, split,
+                                       heads, kv_heads, head_dim, dtype, w);
+    if (st != CP_OK) return st;
+    const int64_t R = w.meta.rows;
+    if (seq_len == 0) return CP_OK;  // no keys and no rows
+    if (!k || !v || !dk || !dv || !workspace) return CP_EINVAL;
+    if (R > 0 && (!q || !out || !lse || !dout || !dq)) return CP_EINVAL;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
+        !aligned(dout, 16) || !aligned(lse, 4) || !aligned(dq, 16) || !aligned(dk, 16) ||
+        !aligned(dv, 16) || !aligned(workspace, 256))
+      return CP_EINVAL;
+    if (workspace_bytes < w.total) return CP_ENOSPC;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    if (stage_and_upload(w.plan_bytes, [&](uint8_t* dst) { pack_bwd_plan(w, dst); }, ws, s) != hipSuccess)
+      return CP_EHIP;
+    BwdArgs a;
+    a.qr = ws + w.off_qr;
+    a.k = k;
+    a.v = v;
+    a.kt = ws + w.off_kt;
+    a.dout = dout;
+    a.qt = ws + w.off_qt;
+    a.dot = ws + w.off_dot;
+    a.lse = lse;
+    a.delta = reinterpret_cast<const float*>(ws + w.off_delta);
+    a.index = reinterpret_cast<const int32_t*>(ws + w.off_index);
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    a.tiles = reinterpret_cast<const TileRec*>(ws + w.off_tiles);
+    a.spans = reinterpret_cast<const SpanRec*>(ws + w.off_spans);
+    a.tile_entries = reinterpret_cast<const EntryRec*>(ws + w.off_tile_entries);
+    a.units = reinterpret_cast<const UnitRec*>(ws + w.off_units);
+    a.ktiles = reinterpret_cast<const KeyTileRec*>(ws + w.off_ktiles);
+    a.R = int32_t(R);
+    a.H = heads;
+    a.Hkv = kv_heads;
+    a.n_hg = w.n_hg;
+    a.group = heads / kv_heads;
+    a.tpad = w.tpad;
+    a.rpad = w.rpad;
+    a.scale = float(1.0 / std::sqrt(double(head_dim)));
+    a.scale_log2 = float(1.4426950408889634 / std::sqrt(double(head_dim)));
+    if (R > 0) {
+      const int64_t row_bytes = int64_t(heads) * head_dim * 2;
+      if (launch_gather(q, a.index, ws + w.off_qr, R, row_bytes, s) != hipSuccess) return CP_EHIP;
+      if (launch_bwd_delta(out, dout, reinterpret_cast<float*>(ws + w.off_delta), int32_t(R), heads, s) !=
+          hipSuccess)
+        return CP_EHIP;
+      if (launch_transpose_v(ws + w.off_qr, ws + w.off_qt, int32_t(R), heads, w.rpad, s) != hipSuccess)
+        return CP_EHIP;
+      if (launch_transpose_v(dout, ws + w.off_dot, int32_t(R), heads, w.rpad, s) != hipSuccess)
+        return CP_EHIP;
+      if (launch_transpose_v(k, ws + w.off_kt, int32_t(seq_len), kv_heads, w.tpad, s) != hipSuccess)
+        return CP_EHIP;
+      if (w.plan.rows.pad_rows > 0 &&
+          launch_fill_pad_rows(a.index, R, heads, head_dim, CP_DTYPE_F32, dq, nullptr, s) != hipSuccess)
+        return CP_EHIP;
+    }
+    // every key tile of every sample is written (zeros where no rank row sees it)
+    if (launch_bwd(a, w.heads_per_wg, R > 0 ? int(w.plan.rows.units.size()) : 0,
+                   int(w.plan.ktiles.size()), s) != hipSuccess)
+      return CP_EHIP;
+    return CP_OK;
+  } catch (const std::exception&) {
+    return CP_EINVAL;
+  }
+}
+
 }  // namespace
 
 extern "C" {
+
+cp_status cp_attn_rank_bwd(const void* q, const void* k, const void* v, const void* out,
+                           const float* lse, const void* dout, int32_t dtype, int64_t seq_len,
+                           const int32_t* n_img, const int32_t* cu_seqlens, int32_t n_samples,
+                           int32_t cp_size, int32_t cp_rank, int32_t split, int32_t heads,
+                           int32_t kv_heads, int32_t head_dim, float* dq, float* dk, float* dv,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  return rank_bwd(q, k, v, out, lse, dout, dtype, seq_len, n_img, cu_seqlens, n_samples, cp_size,
+                  cp_rank, split, heads, kv_heads, head_dim, dq, dk, dv, workspace, workspace_bytes,
+                  stream);
+}
+
 
 cp_status cp_attn_rank_fwd(const void* q, const void* k, const void* v, int32_t dtype,
                            int64_t seq_len, const int32_t* n_img, const int32_t* cu_seqlens,

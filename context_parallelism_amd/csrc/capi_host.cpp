@@ -134,6 +134,24 @@ cp_status cp_attn_rank_plan_stats(int64_t seq_len, const int32_t* n_img, const i
                                     n_entries, kv_tiles, covered_pairs, step_pairs);
 }
 
+cp_status cp_attn_rank_bwd_workspace_size(int64_t seq_len, const int32_t* n_img,
+                                          const int32_t* cu_seqlens, int32_t n_samples,
+                                          int32_t cp_size, int32_t cp_rank, int32_t split,
+                                          int32_t heads, int32_t kv_heads, int32_t head_dim,
+                                          int32_t dtype, size_t* bytes) {
+  if (bytes == nullptr) return CP_EINVAL;
+  try {
+    BwdWorkspace w;
+    int32_t st = prepare_bwd_workspace(seq_len, n_img, cu_seqlens, n_samples, cp_size, cp_rank, split,
+                                       heads, kv_heads, head_dim, dtype, w);
+    if (st != CP_OK) return st;
+    *bytes = w.total;
+    return CP_OK;
+  } catch (const std::exception&) {
+    return CP_EINVAL;
+  }
+}
+
 const char* cp_status_string(cp_status s) {
   switch (s) {
     case CP_OK: return "success";

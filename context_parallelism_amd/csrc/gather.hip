@@ -35,7 +35,7 @@ __global__ __launch_bounds__(kGatherThreads) void gather_rows_kernel(
     if (pos[u] < total_vec) dst[pos[u]] = val[u];
 }
 
-// Pad rows (index -1) of the outputs: zero output row, lse -inf. One thread
+// Pad rows (index -1) of the outputs: zero output row, lse -inf (if lse is set). One thread
 // per (row, 16-byte piece of a row); piece 0 also writes the row's lse.
 __global__ __launch_bounds__(kGatherThreads) void fill_pad_rows_kernel(
     const int32_t* __restrict__ index, uint4* __restrict__ out, float* __restrict__ lse,
@@ -45,7 +45,7 @@ __global__ __launch_bounds__(kGatherThreads) void fill_pad_rows_kernel(
   const uint32_t row = i / row_vec, piece = i % row_vec;
   if (index[row] >= 0) return;
   out[i] = make_uint4(0, 0, 0, 0);
-  if (piece < heads) lse[uint64_t(piece) * n_rows + row] = -INFINITY;
+  if (lse != nullptr && piece < heads) lse[uint64_t(piece) * n_rows + row] = -INFINITY;
 }
 
 }  // namespace
@@ -54,7 +54,7 @@ hipError_t launch_fill_pad_rows(const int32_t* index, int64_t n_rows, int32_t he
                                 int32_t head_dim, int32_t dtype, void* out, float* lse,
                                 hipStream_t stream) {
   if (n_rows == 0) return hipSuccess;
-  const int64_t row_bytes = int64_t(heads) * head_dim * (dtype == 1 ? 2 : 4);
+  const int64_t row_bytes = int64_t(heads) * head_dim * (dtype == 1 ? 2 : 4);  // bf16 or fp32
   const uint64_t row_vec = uint64_t(row_bytes) / 16;
   const uint64_t total = row_vec * uint64_t(n_rows);
   // piece h < heads writes head h's lse: needs at least `heads` pieces per row

@@ -33,6 +33,36 @@ struct AttnArgs {
   float scale;           // 1 / sqrt(D)
 };
 
+// Backward (bf16, head_dim 128).
+struct BwdArgs {
+  const void* qr;      // gathered rank-local Q [R, H, 128]
+  const void* k;       // [T, Hkv, 128]
+  const void* v;       // [T, Hkv, 128]
+  const void* kt;      // K^T blocked by 8 keys [Hkv][tpad/8][128][8]
+  const void* dout;    // [R, H, 128]
+  const void* qt;      // Q^T of the rank rows, blocked by 8 rows [H][rpad/8][128][8]
+  const void* dot;     // dout^T, same layout
+  const float* lse;    // forward lse [H, R]
+  const float* delta;  // rowsum(dout * out) [H, R]
+  const int32_t* index;  // global id per rank row, -1 for pads
+  float* dq;           // [R, H, 128]
+  float* dk;           // [T, Hkv, 128]
+  float* dv;           // [T, Hkv, 128]
+  const TileRec* tiles;
+  const SpanRec* spans;
+  const EntryRec* tile_entries;
+  const UnitRec* units;
+  const KeyTileRec* ktiles;
+  int32_t R, H, Hkv, n_hg, group, tpad, rpad;
+  float scale, scale_log2;
+};
+
+hipError_t launch_bwd_delta(const void* out, const void* dout, float* delta, int32_t R, int32_t H,
+                            hipStream_t stream);
+// dQ for every unit, then dK/dV for every key tile.
+hipError_t launch_bwd(const BwdArgs& a, int heads_per_wg, int n_units, int n_ktiles,
+                      hipStream_t stream);
+
 hipError_t launch_gather(const void* src, const int32_t* index, void* dst, int64_t n_rows,
                          int64_t row_bytes, hipStream_t stream);
 

@@ -221,4 +221,35 @@ void build_plan(const Meta& m, int32_t bm, int32_t bn, Plan& p) {
   for (int32_t g : p.index) p.pad_rows += g < 0;
 }
 
+void build_bwd_plan(const Meta& m, int32_t rows_bm, BwdPlan& b) {
+  b = BwdPlan();
+  build_plan(m, rows_bm, kBlockN, b.rows);
+  const std::vector<int32_t>& index = b.rows.index;
+  struct Pending { KeyTileRec k; int64_t cost; };
+  std::vector<Pending> pend;
+  for (size_t si = 0; si < m.samples.size(); ++si) {
+    const SampleGeom& g = m.samples[si];
+    const int64_t s0 = g.a, s1 = g.a + g.n_img + g.text;  // the sample's tokens
+    const int64_t l0 = g.local0, l1 = g.local0 + g.n_img + 2 * int64_t(g.c);  // its rank rows
+    const int32_t rb1 = int32_t((l1 + kBwdRowBlock - 1) / kBwdRowBlock);
+    // rank rows of the sample are in increasing global order apart from pads
+    // (-1), so the rows that see key k0 start at the first real row >= k0
+    int64_t first = l0;
+    for (int64_t k0 = s0; k0 < s1; k0 += kBwdKeyTile) {
+      while (first < l1 && (index[size_t(first)] < 0 || index[size_t(first)] < k0)) ++first;
+      KeyTileRec t{int32_t(k0), int32_t(std::min<int64_t>(k0 + kBwdKeyTile, s1)), 0, 0,
+                   int32_t(s0), int32_t(s1), 0, 0};
+      if (first < l1) {
+        t.rb0 = int32_t(first / kBwdRowBlock);
+        t.rb1 = rb1;
+      }
+      pend.push_back({t, int64_t(t.rb1 - t.rb0)});
+    }
+  }
+  std::stable_sort(pend.begin(), pend.end(),
+                   [](const Pending& x, const Pending& y) { return x.cost > y.cost; });
+  b.ktiles.reserve(pend.size());
+  for (const Pending& q : pend) b.ktiles.push_back(q.k);
+}
+
 }  // namespace cpattn

@@ -113,4 +113,21 @@ void step_ranges(const Meta& m, int32_t sample, int32_t step, std::vector<SpanRe
 // descending key-tile count (`bn` keys per tile).
 void build_plan(const Meta& m, int32_t bm, int32_t bn, Plan& p);
 
+// ---------------------------------------------------------------- backward
+// dK/dV work: keys [k0, k1) of one sample [s0, s1) (k1 <= s1), and the
+// 32-row blocks of rank-local rows [32 rb0, 32 rb1) that hold every rank row
+// of that sample with a global id >= k0 (other rows of those blocks are
+// masked by their index).
+constexpr int kBwdRowBlock = 32;   // rank-local rows per dK/dV row block
+constexpr int kBwdKeyTile = 128;   // keys per dK/dV workgroup (4 waves x 32)
+struct KeyTileRec { int32_t k0, k1, rb0, rb1, s0, s1, pad0, pad1; };
+
+struct BwdPlan {
+  Plan rows;                        // dQ: row tiles with their ring-step spans and units
+  std::vector<KeyTileRec> ktiles;   // dK/dV: every key tile of every sample, longest first
+};
+
+// rows_bm: rows per dQ row tile.
+void build_bwd_plan(const Meta& m, int32_t rows_bm, BwdPlan& b);
+
 }  // namespace cpattn

@@ -97,4 +97,68 @@ void pack_plan(const Workspace& w, uint8_t* dst) {
   if (!u.empty()) std::memcpy(dst + w.off_units, u.data(), u.size() * sizeof(UnitRec));
 }
 
+int32_t prepare_bwd_workspace(int64_t seq_len, const int32_t* n_img, const int32_t* cu_seqlens,
+                              int32_t n_samples, int32_t cp_size, int32_t cp_rank, int32_t split,
+                              int32_t heads, int32_t kv_heads, int32_t head_dim, int32_t dtype,
+                              BwdWorkspace& w) {
+  if (dtype != CP_DTYPE_F32 && dtype != CP_DTYPE_BF16) return CP_EUNSUPPORTED;
+  if (heads < 1 || kv_heads < 1 || heads % kv_heads != 0) return CP_EINVAL;
+  if (head_dim != 64 && head_dim != 128) return CP_EUNSUPPORTED;
+  if (dtype != CP_DTYPE_BF16 || head_dim != 128) return CP_EUNSUPPORTED;  // backward: bf16, 128
+  int32_t st = build_meta(seq_len, n_img, cu_seqlens, n_samples, cp_size, cp_rank, w.meta, split);
+  if (st != CP_OK) return st;
+  w.heads = heads;
+  w.kv_heads = kv_heads;
+  w.head_dim = head_dim;
+  const int32_t group = heads / kv_heads;
+  w.heads_per_wg = (group % 4 == 0) ? 4 : (group % 2 == 0) ? 2 : 1;
+  w.rows_per_tile = 32 * 4 / w.heads_per_wg;  // dQ: 4 waves of 32 rows
+  w.n_hg = heads / w.heads_per_wg;
+  build_bwd_plan(w.meta, w.rows_per_tile, w.plan);
+  const Plan& p = w.plan.rows;
+  const size_t R = size_t(w.meta.rows);
+  size_t off = 0;
+  w.off_index = off;
+  off = align256(off + R * sizeof(int32_t));
+  w.off_tiles = off;
+  off = align256(off + p.tiles.size() * sizeof(TileRec));
+  w.off_spans = off;
+  off = align256(off + p.spans.size() * sizeof(SpanRec));
+  w.off_tile_entries = off;
+  off = align256(off + p.tile_entries.size() * sizeof(EntryRec));
+  w.off_units = off;
+  off = align256(off + p.units.size() * sizeof(UnitRec));
+  w.off_ktiles = off;
+  off = align256(off + w.plan.ktiles.size() * sizeof(KeyTileRec));
+  w.plan_bytes = off;
+  w.rpad = int32_t((R + 63) / 64 * 64);
+  w.tpad = vt_row_keys(seq_len);
+  w.off_qr = off;
+  off = align256(off + R * size_t(heads) * head_dim * 2);
+  w.off_qt = off;
+  off = align256(off + size_t(heads) * w.rpad * head_dim * 2);
+  w.off_dot = off;
+  off = align256(off + size_t(heads) * w.rpad * head_dim * 2);
+  w.off_kt = off;
+  off = align256(off + size_t(kv_heads) * w.tpad * head_dim * 2);
+  w.off_delta = off;
+  off = align256(off + size_t(heads) * R * sizeof(float));
+  w.total = off;
+  return CP_OK;
+}
+
+void pack_bwd_plan(const BwdWorkspace& w, uint8_t* dst) {
+  std::memset(dst, 0, w.plan_bytes);
+  const Plan& p = w.plan.rows;
+  auto put = [&](size_t off, const void* src, size_t bytes) {
+    if (bytes) std::memcpy(dst + off, src, bytes);
+  };
+  put(w.off_index, p.index.data(), p.index.size() * sizeof(int32_t));
+  put(w.off_tiles, p.tiles.data(), p.tiles.size() * sizeof(TileRec));
+  put(w.off_spans, p.spans.data(), p.spans.size() * sizeof(SpanRec));
+  put(w.off_tile_entries, p.tile_entries.data(), p.tile_entries.size() * sizeof(EntryRec));
+  put(w.off_units, p.units.data(), p.units.size() * sizeof(UnitRec));
+  put(w.off_ktiles, w.plan.ktiles.data(), w.plan.ktiles.size() * sizeof(KeyTileRec));
+}
+
 }  // namespace cpattn

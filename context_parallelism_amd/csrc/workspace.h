@@ -48,6 +48,31 @@ int32_t prepare_workspace(int64_t seq_len, const int32_t* n_img, const int32_t* 
                           int32_t kv_heads, int32_t head_dim, int32_t dtype, Workspace& w,
                           int32_t split = 0);
 
+// Backward workspace (bf16, head_dim 128), each region 256-byte aligned:
+//   plan  : index int32[R], dQ row tiles, spans, step-ordered entries, units,
+//           dK/dV key tiles (uploaded from the host in one copy);
+//   qr    : gathered rank-local Q rows [R, H, 128] bf16;
+//   qt    : Q^T of those rows, blocked by 8 rows: [H][rpad/8][128][8];
+//   dot   : dout^T, same layout;
+//   kt    : K^T blocked by 8 keys: [Hkv][tpad/8][128][8];
+//   delta : rowsum(dout * out) fp32 [H, R].
+struct BwdWorkspace {
+  Meta meta;
+  BwdPlan plan;
+  int32_t heads = 0, kv_heads = 0, head_dim = 0;
+  int32_t heads_per_wg = 1, rows_per_tile = 0, n_hg = 0;
+  size_t off_index = 0, off_tiles = 0, off_spans = 0, off_tile_entries = 0, off_units = 0,
+         off_ktiles = 0, plan_bytes = 0;
+  size_t off_qr = 0, off_qt = 0, off_dot = 0, off_kt = 0, off_delta = 0, total = 0;
+  int32_t rpad = 0, tpad = 0;
+};
+
+int32_t prepare_bwd_workspace(int64_t seq_len, const int32_t* n_img, const int32_t* cu_seqlens,
+                              int32_t n_samples, int32_t cp_size, int32_t cp_rank, int32_t split,
+                              int32_t heads, int32_t kv_heads, int32_t head_dim, int32_t dtype,
+                              BwdWorkspace& w);
+void pack_bwd_plan(const BwdWorkspace& w, uint8_t* dst);
+
 // Keys per V^T row: a multiple of 64 that covers every 64-key window
 // starting below seq_len.
 int32_t vt_row_keys(int64_t seq_len);

@@ -255,6 +255,44 @@ cp_status cp_attn_rank_fwd_ex(const void *q, const void *k, const void *v, int32
                               float *lse, void *workspace, size_t workspace_bytes, void *stream,
                               void *const *events);
 
+/*
+ * cp_attn_rank_bwd -- gradients of one CP rank's attention share.
+ *
+ * For a loss whose gradient w.r.t. the rank's forward output is dout, the
+ * softmax-attention chain rule over the same rows and ring-step keys as
+ * cp_attn_rank_fwd: with P = exp(S - lse) (S = q k^T / sqrt(head_dim),
+ * lse the forward's), Delta = rowsum(dout * out):
+ *   dv = P^T dout;  ds = P * (dout v^T - Delta);
+ *   dq = ds k / sqrt(head_dim);  dk = ds^T q / sqrt(head_dim).
+ * Ring Attention's backward passes the same blockwise steps around the
+ * ring in reverse; on one GPU every step's K/V is in HBM and the gradient
+ * of a key simply sums over the rank's rows.
+ *
+ * q, k, v: as for cp_attn_rank_fwd (device, THD); out, lse: that call's
+ * outputs for the same arguments; dout: device [R, heads, head_dim] in
+ * dtype. split: CP_SPLIT_*.
+ * dq: device fp32 [R, heads, head_dim] (rank-local rows; pad rows 0).
+ * dk, dv: device fp32 [seq_len, kv_heads, head_dim]: every key's gradient
+ *   from this rank's rows, summed over the query heads of its KV head (0
+ *   for keys no row of the rank sees). Summing dk, dv over all ranks of a
+ *   CP group, and scattering each rank's dq back by its index, gives the
+ *   gradients of the whole sequence (the reverse ring / all-reduce).
+ * workspace: device, cp_attn_rank_bwd_workspace_size bytes, 256-byte
+ *   aligned. Supported: dtype CP_DTYPE_BF16 with head_dim 128; otherwise
+ *   CP_EUNSUPPORTED. Deterministic (no atomics).
+ */
+cp_status cp_attn_rank_bwd_workspace_size(int64_t seq_len, const int32_t *n_img,
+                                          const int32_t *cu_seqlens, int32_t n_samples,
+                                          int32_t cp_size, int32_t cp_rank, int32_t split,
+                                          int32_t heads, int32_t kv_heads, int32_t head_dim,
+                                          int32_t dtype, size_t *bytes);
+cp_status cp_attn_rank_bwd(const void *q, const void *k, const void *v, const void *out,
+                           const float *lse, const void *dout, int32_t dtype, int64_t seq_len,
+                           const int32_t *n_img, const int32_t *cu_seqlens, int32_t n_samples,
+                           int32_t cp_size, int32_t cp_rank, int32_t split, int32_t heads,
+                           int32_t kv_heads, int32_t head_dim, float *dq, float *dk, float *dv,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
 const char *cp_status_string(cp_status s);
 
 #ifdef __cplusplus
