@@ -205,6 +205,55 @@ def compare_ulysses(w, args):
     print(json.dumps(line), flush=True)
 
 
+def bench_backward(w, args):
+    """cp_attn_rank_bwd on the rank share: delta, transposes, dQ and dK/dV.
+    Useful FLOPs follow the usual backward count of five products per
+    (query, key) pair -- QK^T, dO V^T, P^T dO, dS^T Q, dS K -- i.e. 2.5x the
+    forward's (the kernels recompute QK^T and dO V^T once more: 7 products)."""
+    import numpy as np
+    import torch
+
+    import context_parallelism_amd as cp
+    import workloads
+
+    if w.dtype != "bf16" or w.head_dim != 128:
+        raise SystemExit("--backward: bf16 with head_dim 128 only")
+    dev = torch.device("cuda:0")
+    q, k, v = workloads.make_inputs(w)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    n_img = w.n_img_array if any(w.n_img) else None
+    cu = w.cu_seqlens if w.n_samples > 1 else None
+    out, lse = cp.rank_fwd(qd, kd, vd, cp_size=w.cp_size, cp_rank=w.rank, n_img=n_img, cu_seqlens=cu,
+                           split=args.split)
+    g = torch.Generator(device="cpu").manual_seed(w.seed + 7)
+    dout = torch.randn(out.shape, generator=g).to(torch.bfloat16).to(dev)
+    bw = cp.RankAttentionBackward(qd, kd, vd, cp_size=w.cp_size, cp_rank=w.rank, n_img=n_img,
+                                  cu_seqlens=cu, split=args.split)
+    for _ in range(args.warmup):
+        bw(out, lse, dout)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for a, b in evs:
+        a.record()
+        bw(out, lse, dout)
+        b.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = np.array([a.elapsed_time(b) for a, b in evs])
+    _, pairs = cp.pair_counts(w.seq_len, n_img, cu, cp_size=w.cp_size, cp_rank=w.rank, split=args.split)
+    useful = 2.5 * 4.0 * w.head_dim * w.heads * pairs
+    med = float(np.median(ms))
+    line = {"mode": "backward", "metric": "useful causal attn backward TFLOP/s per CP-rank share (1 GPU)",
+            "value": round(useful / (med * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "ms_median": round(med, 4),
+            "ms_p10": round(float(np.percentile(ms, 10)), 4), "ms_p90": round(float(np.percentile(ms, 90)), 4),
+            "wall_ms_per_call": round(wall / args.steps * 1e3, 4), "useful_flop": useful,
+            "pct_of_peak": round(100.0 * useful / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+            "config": {"workload": w.name, "cp_rank": w.rank, "split": args.split, "rank_rows": bw.R}}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -225,13 +274,16 @@ def main():
                     help="instead of the headline line: one GPU's share under Ulysses (all-to-all "
                          "over heads: full-sequence causal attention on heads/P and kv_heads/P) next "
                          "to the ring rank share of the same workload; one JSON line")
+    ap.add_argument("--backward", action="store_true",
+                    help="instead of the headline line: time cp_attn_rank_bwd (gradients of the rank "
+                         "share) on the workload; one JSON line")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="instead of the attention, run --steps plain device copies of this many MiB "
                          "(the reference kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one CP rank's share on one GPU; --gpus {args.gpus} is not supported "
-              "(no multi-GPU path is built: see DESIGN.md, 'How the path would shard')", file=sys.stderr)
+              "(no multi-GPU path is built in this library)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -256,6 +308,9 @@ def main():
         return
     if args.ulysses:
         compare_ulysses(w, args)
+        return
+    if args.backward:
+        bench_backward(w, args)
         return
     rank = w.rank if args.rank is None else args.rank
     if rank != w.rank:

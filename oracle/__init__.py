@@ -18,7 +18,7 @@ Sources (cited by page address and section):
   blockwise partial results are combined by their log-sum-exp, which
   reproduces the softmax over the union of the key blocks exactly.
 
-Readings where the pages are silent (each is listed in the design doc):
+Readings where the pages are silent:
 
 * text not divisible by 2P is padded at its end to a multiple of 2P; pad
   rows are outputs of value 0 with lse = -inf and pad keys are never seen;
