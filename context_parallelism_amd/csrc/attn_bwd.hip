@@ -12,12 +12,15 @@
 // over the rank's rows and the query heads that read its KV head.
 //
 // Three kernels, no atomics (results are deterministic):
-//  * delta: Delta[h][r] = sum_d dO[r][h][d] * O[r][h][d];
+//  * prep: Delta[h][r] = sum_d dO[r][h][d] * O[r][h][d], and per 32-row block
+//    and head a record of lse * log2(e), Delta and each row's visible key
+//    range that the dK/dV kernel stages through LDS with its operands;
 //  * dQ: one workgroup of 4 waves per (row tile, head group); each wave owns
 //    32 rows of one head and walks the tile's key spans over all ring steps,
 //    recomputing S^T = K Q^T and dP^T = V dO^T (K and V rows from LDS, Q and
 //    dO in registers) and accumulating dQ^T += K^T dS^T (K^T from a blocked
-//    copy, as the forward reads V^T);
+//    copy, as the forward reads V^T); K, V and K^T tiles stream through a
+//    three-slot LDS ring, two tiles ahead;
 //  * dK/dV: one workgroup of 4 waves per (128-key tile, KV head); each wave
 //    owns 32 keys, keeps its K and V rows in registers, and walks the
 //    rank's 32-row blocks that see the tile, for every query head of the KV
@@ -25,7 +28,9 @@
 //    dV += P^T dO and dK += dS^T Q with Q^T and dO^T read from blocked
 //    copies. The accumulator layout of S (keys in lanes, rows in
 //    registers) is directly the A operand of those products once the rows
-//    are read in the order sigma (bits 2 and 3 of the row swapped).
+//    are read in the order sigma (bits 2 and 3 of the row swapped). The
+//    row blocks stream through a four-slot LDS ring, three blocks ahead, so
+//    no wave waits on memory inside a step.
 #include "kernels.h"
 
 namespace cpattn {
@@ -41,6 +46,32 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kBufferWord3 = 0x00020000;  // raw buffer access, gfx9 family
 constexpr int kWaitVmcnt0 = 0x0F70;       // s_waitcnt vmcnt(0), expcnt and lgkmcnt untouched
+
+// s_waitcnt immediate for vmcnt(n) alone (n < 64: low four bits in [3:0],
+// high two in [15:14]; expcnt 7 and lgkmcnt 15 mean "no wait").
+constexpr int wait_vmcnt(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+
+// Plan records are read through the constant address space so that the
+// uniform loads become scalar loads (counted by lgkmcnt, not by the vmcnt
+// that tracks the LDS-DMA ring).
+template <typename T>
+using const_ptr = const __attribute__((address_space(4))) T*;
+template <typename T>
+__device__ inline const_ptr<T> scalar_view(const T* p) {
+  return (const_ptr<T>)(p);
+}
+// Copy of plan record i (a struct of int32 words) through a scalar view.
+template <typename T>
+__device__ inline T scalar_load(const T* p, int64_t i) {
+  static_assert(sizeof(T) % 4 == 0, "int32 words");
+  const const_ptr<int32_t> q = (const_ptr<int32_t>)(p + i);
+  int32_t w[sizeof(T) / 4];
+#pragma unroll
+  for (size_t k = 0; k < sizeof(T) / 4; ++k) w[k] = q[k];
+  T r;
+  __builtin_memcpy(&r, w, sizeof(T));
+  return r;
+}
 constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
@@ -56,24 +87,40 @@ __device__ inline float sum_with_partner16(float x) {
   return x;
 }
 
-// ---------------------------------------------------------------- delta
-// 16 lanes per (row, head) pair, 8 elements each; 16 pairs per 256 threads.
-__global__ __launch_bounds__(256) void delta_kernel(const __bf16* __restrict__ out,
-                                                   const __bf16* __restrict__ dout,
-                                                   float* __restrict__ delta, int32_t R, int32_t H) {
+// ---------------------------------------------------------------- prep
+// 16 lanes per (row, head) pair, 8 elements each; 16 pairs per 256 threads;
+// rows up to 32 nrb (rows >= R get pad records).
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const __bf16* __restrict__ out,
+                                                      const __bf16* __restrict__ dout,
+                                                      const float* __restrict__ lse,
+                                                      const int32_t* __restrict__ index,
+                                                      const int32_t* __restrict__ row_lo,
+                                                      float* __restrict__ delta, int32_t* __restrict__ rec,
+                                                      int32_t R, int32_t H, int32_t nrb) {
   const int64_t pair = int64_t(blockIdx.x) * 16 + (threadIdx.x >> 4);
   const int sub = threadIdx.x & 15;
-  const bool ok = pair < int64_t(R) * H;
+  const bool ok = pair < int64_t(nrb) * kBwdRowBlock * H;
   const int64_t pc = ok ? pair : 0;  // inactive groups read pair 0 and store nothing
   const int r = int(pc / H), h = int(pc % H);
-  const int64_t off = pc * 128 + sub * 8;  // [R, H, 128]: pair (r, h) starts at (r H + h) 128
-  const bf16x8 o = *reinterpret_cast<const bf16x8*>(out + off);
-  const bf16x8 d = *reinterpret_cast<const bf16x8*>(dout + off);
+  const bool in = r < R;
   float s = 0.f;
+  if (in) {
+    const int64_t off = (int64_t(r) * H + h) * 128 + sub * 8;  // [R, H, 128]
+    const bf16x8 o = *reinterpret_cast<const bf16x8*>(out + off);
+    const bf16x8 d = *reinterpret_cast<const bf16x8*>(dout + off);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) s = __builtin_fmaf(float(o[i]), float(d[i]), s);
+    for (int i = 0; i < 8; ++i) s = __builtin_fmaf(float(o[i]), float(d[i]), s);
+  }
   s = sum_with_partner16(s);
-  if (ok && sub == 0) delta[int64_t(h) * R + r] = s;
+  if (!ok || sub != 0) return;
+  if (in) delta[int64_t(h) * R + r] = s;
+  const int gid = in ? index[r] : -1;
+  const bool real = gid >= 0;
+  int32_t* const w = rec + (int64_t(h) * nrb + r / kBwdRowBlock) * (4 * kBwdRowBlock) + r % kBwdRowBlock;
+  w[0] = __float_as_int(real ? lse[int64_t(h) * R + r] * kLog2e : INFINITY);
+  w[kBwdRowBlock] = __float_as_int(real ? s : 0.f);
+  w[2 * kBwdRowBlock] = real ? row_lo[r] : 0;
+  w[3 * kBwdRowBlock] = real ? gid - row_lo[r] : -1;
 }
 
 // Scalar walk over a unit's 64-key tiles (as in the forward).
@@ -88,19 +135,17 @@ void dq_kernel(const BwdArgs a) {
   constexpr int D = 128, BN = 64, NQ = 8, ND = 4, RB = 4 / G;
   constexpr int TILE = BN * D * 2;     // bytes of a K, V or K^T tile
   constexpr int CH = TILE / 1024 / 4;  // LDS-DMA instructions per wave per tensor
-  __shared__ __attribute__((aligned(1024))) char k0s[TILE];
-  __shared__ __attribute__((aligned(1024))) char k1s[TILE];
-  __shared__ __attribute__((aligned(1024))) char v0s[TILE];
-  __shared__ __attribute__((aligned(1024))) char v1s[TILE];
-  __shared__ __attribute__((aligned(1024))) char t0s[TILE];
-  __shared__ __attribute__((aligned(1024))) char t1s[TILE];
+  constexpr int PER_STAGE = 3 * CH;    // LDS-DMA instructions per wave per tile
+  __shared__ __attribute__((aligned(1024))) char k0s[TILE], k1s[TILE], k2s[TILE];
+  __shared__ __attribute__((aligned(1024))) char v0s[TILE], v1s[TILE], v2s[TILE];
+  __shared__ __attribute__((aligned(1024))) char t0s[TILE], t1s[TILE], t2s[TILE];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hg = blockIdx.x % a.n_hg;
-  const UnitRec unit = a.units[blockIdx.x / a.n_hg];
-  const TileRec tile = a.tiles[unit.tile];
-  const EntryRec* const steps = a.tile_entries + unit.e0;
+  const UnitRec unit = scalar_load(a.units, blockIdx.x / a.n_hg);
+  const TileRec tile = scalar_load(a.tiles, unit.tile);
+  const const_ptr<EntryRec> steps = scalar_view(a.tile_entries) + unit.e0;
   const int n_steps = unit.e1 - unit.e0;
   const int h = hg * G + (wave % G);
   const int rsub = wave / G;
@@ -112,7 +157,7 @@ void dq_kernel(const BwdArgs a) {
   const int grow = tile.g0 + rin;
   const int wave_lo = tile.g0 + rsub * 32;
   static_assert(RB * G == 4, "4 waves");
-  const SpanRec* spans = a.spans + steps[0].span_begin;
+  const const_ptr<SpanRec> spans = scalar_view(a.spans) + steps[0].span_begin;
   const int n_spans = steps[n_steps - 1].span_end - steps[0].span_begin;
   int n_tiles = 0;
   for (int i = 0; i < n_spans; ++i) n_tiles += (spans[i].k1 - (spans[i].k0 & ~7) + BN - 1) / BN;
@@ -252,25 +297,37 @@ void dq_kernel(const BwdArgs a) {
         }
   };
 
+  // Ring of three LDS slots: tile t sits in slot t % 3; while tile t is
+  // consumed, tile t + 1 is in flight and tile t + 2 is issued into the slot
+  // tile t - 1 left (every wave finished it before this step's barrier).
   Cursor cs, cl;
   start(cs);
   start(cl);
   issue(cl, k0s, v0s, t0s);
-  for (int t = 0; t < n_tiles; t += 2) {
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    __syncthreads();
+  if (n_tiles > 1) {
     advance(cl);
-    if (t + 1 < n_tiles) issue(cl, k1s, v1s, t1s);
-    tile_step(cs, k0s, v0s, t0s);
-    advance(cs);
-    if (t + 1 >= n_tiles) break;
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    __syncthreads();
-    advance(cl);
-    if (t + 2 < n_tiles) issue(cl, k0s, v0s, t0s);
-    tile_step(cs, k1s, v1s, t1s);
-    advance(cs);
+    issue(cl, k1s, v1s, t1s);
   }
+#define DQ_STEP(T, KC, VC, TC, KN, VN, TN)                   \
+  {                                                          \
+    if ((T) + 1 < n_tiles)                                   \
+      __builtin_amdgcn_s_waitcnt(wait_vmcnt(PER_STAGE));     \
+    else                                                     \
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);               \
+    asm volatile("s_barrier" ::: "memory");                  \
+    if ((T) + 2 < n_tiles) {                                 \
+      advance(cl);                                           \
+      issue(cl, KN, VN, TN);                                 \
+    }                                                        \
+    tile_step(cs, KC, VC, TC);                               \
+    advance(cs);                                             \
+  }
+  for (int t = 0; t < n_tiles; t += 3) {
+    DQ_STEP(t, k0s, v0s, t0s, k2s, v2s, t2s);
+    if (t + 1 < n_tiles) DQ_STEP(t + 1, k1s, v1s, t1s, k0s, v0s, t0s);
+    if (t + 2 < n_tiles) DQ_STEP(t + 2, k2s, v2s, t2s, k1s, v1s, t1s);
+  }
+#undef DQ_STEP
 
   if (!row_ok) return;
   float* const dq = a.dq + (int64_t(lrow) * a.H + h) * D + 4 * hh;
@@ -288,31 +345,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void dkdv_kernel(const BwdArgs a) {
   constexpr int D = 128, NQ = 8, ND = 4, RBK = kBwdRowBlock;
   constexpr int ROWT = RBK * D * 2;    // bytes of a 32-row Q, dO, Q^T or dO^T tile
-  constexpr int CH = ROWT / 1024 / 4;  // LDS-DMA instructions per wave per tensor (2)
+  constexpr int CH = ROWT / 1024 / 4;  // 16-byte LDS-DMA instructions per wave per tile (2)
   static_assert(kBwdKeyTile == 128 && RBK == 32, "4 waves of 32 keys, 32-row blocks");
-  __shared__ __attribute__((aligned(1024))) char q0s[ROWT], q1s[ROWT];
-  __shared__ __attribute__((aligned(1024))) char d0s[ROWT], d1s[ROWT];
-  __shared__ __attribute__((aligned(1024))) char qt0s[ROWT], qt1s[ROWT];
-  __shared__ __attribute__((aligned(1024))) char dt0s[ROWT], dt1s[ROWT];
+  // One ring slot: Q | dO | Q^T | dO^T | row records (every wave loads 256 B
+  // of records; 512 B are the record, the rest reads as zeros).
+  constexpr int OQ = 0, OD = ROWT, OQT = 2 * ROWT, ODT = 3 * ROWT, OREC = 4 * ROWT;
+  constexpr int STAGE = 4 * ROWT + 1024;
+  constexpr int REC_BYTES = 4 * RBK * 4;
+  constexpr int PER_STAGE = 4 * CH + 1;  // LDS-DMA instructions per wave per slot
+  __shared__ __attribute__((aligned(1024))) char st0[STAGE], st1[STAGE], st2[STAGE], st3[STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = blockIdx.x % a.Hkv;
-  const KeyTileRec kt = a.ktiles[blockIdx.x / a.Hkv];
+  const KeyTileRec kt = scalar_load(a.ktiles, blockIdx.x / a.Hkv);
+  const const_ptr<int32_t> blk = scalar_view(a.blk);
   const int kl = lane & 31, hh = lane >> 5;
-  const int key = kt.k0 + 32 * wave + kl;  // this lane's key (column of S)
+  const int kw0 = kt.k0 + 32 * wave;  // the wave's first key
+  const int key = kw0 + kl;           // this lane's key (column of S)
 
   // K and V rows of the wave's 32 keys as B operands: lane holds key kl,
   // d = 16 jj + 8 hh + 0..7. Keys >= k1 read as zeros.
   bf16x8 kf[NQ], vf[NQ];
   {
     const int tok_bytes = a.Hkv * D * 2;
-    const int k0w = kt.k0 + 32 * wave;
-    const int valid = max(min(kt.k1 - k0w, 32), 0) * tok_bytes;
-    const __amdgpu_buffer_rsrc_t kr =
-        make_rsrc(static_cast<const char*>(a.k) + (int64_t(k0w) * a.Hkv + g) * D * 2, valid);
-    const __amdgpu_buffer_rsrc_t vr =
-        make_rsrc(static_cast<const char*>(a.v) + (int64_t(k0w) * a.Hkv + g) * D * 2, valid);
+    const int valid = __builtin_amdgcn_readfirstlane(max(min(kt.k1 - kw0, 32), 0) * tok_bytes);
+    const int64_t base = (int64_t(kw0) * a.Hkv + g) * D * 2;
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(static_cast<const char*>(a.k) + base, valid);
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(static_cast<const char*>(a.v) + base, valid);
 #pragma unroll
     for (int jj = 0; jj < NQ; ++jj) {
       const int off = kl * tok_bytes + (16 * jj + 8 * hh) * 2;
@@ -336,7 +396,12 @@ void dkdv_kernel(const BwdArgs a) {
     const int d = 16 * c + (lane >> 2), s = lane & 3;
     tgo[i] = (s ^ ((d >> 2) & 3)) * (D * 16) + d * 16;
   }
-  auto issue = [&](int rb, int h, char* qd, char* dd, char* qtd, char* dtd) {
+  // the (row block, head) steps: rb in [rb0, rb1) outer, the query heads of
+  // KV head g (a.group of them) inner
+  const int group = a.group;
+  const int n_blocks = (kt.rb1 - kt.rb0) * group;
+  auto issue = [&](int j, char* st) {
+    const int rb = kt.rb0 + j / group, h = g * group + j % group;
     const int r0 = rb * RBK;
     const int valid = __builtin_amdgcn_readfirstlane(max(min(a.R - r0, RBK), 0) * row_bytes);
     const int64_t noff = (int64_t(r0) * a.H + h) * D * 2;
@@ -345,14 +410,17 @@ void dkdv_kernel(const BwdArgs a) {
     const int64_t toff = (int64_t(h) * a.rpad + r0) * D * 2;
     const __amdgpu_buffer_rsrc_t qtr = make_rsrc(static_cast<const char*>(a.qt) + toff, ROWT);
     const __amdgpu_buffer_rsrc_t dtr = make_rsrc(static_cast<const char*>(a.dot) + toff, ROWT);
+    const __amdgpu_buffer_rsrc_t rr = make_rsrc(a.rec + (int64_t(h) * a.nrb + rb) * (4 * RBK), REC_BYTES);
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       const int slot = (wave * CH + i) * 1024;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(qr, (lds_void*)(qd + slot), 16, ngo[i], 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(dr, (lds_void*)(dd + slot), 16, ngo[i], 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(qtr, (lds_void*)(qtd + slot), 16, tgo[i], 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(dtr, (lds_void*)(dtd + slot), 16, tgo[i], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(qr, (lds_void*)(st + OQ + slot), 16, ngo[i], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(dr, (lds_void*)(st + OD + slot), 16, ngo[i], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(qtr, (lds_void*)(st + OQT + slot), 16, tgo[i], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(dtr, (lds_void*)(st + ODT + slot), 16, tgo[i], 0, 0, 0);
     }
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (lds_void*)(st + OREC + wave * 256), 4, wave * 256 + 4 * lane,
+                                             0, 0, 0);
   };
   // A operands of S and dP: lane reads row sigma(kl) of the Q / dO tile
   const int srow = (kl & ~12) | ((kl & 4) << 1) | ((kl & 8) >> 1);
@@ -380,8 +448,8 @@ void dkdv_kernel(const BwdArgs a) {
   const float c2 = a.scale_log2;
 
   // one (row block, query head) step. Register t of lane half hh holds row
-  // 32 rb + rr(t): rr = 8 hh + t (t < 8), 16 + 8 hh + t - 8 (t >= 8).
-  auto block_step = [&](int rb, int h, const char* qs, const char* ds, const char* qts, const char* dts) {
+  // 32 rb + 16 (t / 8) + 8 hh + t % 8 of the block.
+  auto block_step = [&](int j, const char* st) {
     f32x16 s, dp;
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
@@ -390,94 +458,95 @@ void dkdv_kernel(const BwdArgs a) {
     }
 #pragma unroll
     for (int jj = 0; jj < NQ; ++jj) {
-      const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qs + nro[jj]);
-      const bf16x8 da = *reinterpret_cast<const bf16x8*>(ds + nro[jj]);
+      const bf16x8 qa = *reinterpret_cast<const bf16x8*>(st + OQ + nro[jj]);
+      const bf16x8 da = *reinterpret_cast<const bf16x8*>(st + OD + nro[jj]);
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[jj], s, 0, 0, 0);
       dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vf[jj], dp, 0, 0, 0);
     }
-    // per-row lse, delta and global id: two runs of 8 rows per lane half
-    const int r0 = rb * RBK;
-    const __amdgpu_buffer_rsrc_t lr = make_rsrc(a.lse + int64_t(h) * a.R, a.R * 4);
-    const __amdgpu_buffer_rsrc_t er = make_rsrc(a.delta + int64_t(h) * a.R, a.R * 4);
-    const __amdgpu_buffer_rsrc_t ir = make_rsrc(a.index, a.R * 4);
-    float lse_r[16], dl_r[16];
-    int gid_r[16];
+    const int* const rec = reinterpret_cast<const int*>(st + OREC);
+    // every row of the block sees every key of the wave unless the block
+    // holds a causal edge or a sample boundary; then S = -inf where the key
+    // is outside [sample start, row's global id]
+    const int rb = kt.rb0 + j / group;
+    if (!(blk[2 * rb] <= kw0 && kw0 + 31 <= blk[2 * rb + 1])) {
+#pragma unroll
+      for (int run = 0; run < 2; ++run)
+#pragma unroll
+        for (int q4 = 0; q4 < 2; ++q4) {
+          const int row = 16 * run + 8 * hh + 4 * q4;
+          const i32x4 lo = *reinterpret_cast<const i32x4*>(rec + 2 * RBK + row);
+          const i32x4 sp = *reinterpret_cast<const i32x4*>(rec + 3 * RBK + row);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int t = 8 * run + 4 * q4 + e;
+            const bool vis = uint32_t(key - lo[e]) <= uint32_t(sp[e]);
+            s[t] = vis ? s[t] : -INFINITY;
+          }
+        }
+    }
+    // P = exp2(S c2 - lse log2 e) (0 for pad rows, whose record holds +inf),
+    // dS = P (dP - Delta)
+    bf16x8 pa[2], dsa[2];
 #pragma unroll
     for (int run = 0; run < 2; ++run)
 #pragma unroll
       for (int q4 = 0; q4 < 2; ++q4) {
-        const int row = r0 + 16 * run + 8 * hh + 4 * q4;
-        const f32x4 l4 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(lr, row * 4, 0, 0));
-        const f32x4 d4 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(er, row * 4, 0, 0));
-        const i32x4 g4 = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(ir, row * 4, 0, 0));
+        const int row = 16 * run + 8 * hh + 4 * q4;
+        const f32x4 l2 = *reinterpret_cast<const f32x4*>(rec + row);
+        const f32x4 dl = *reinterpret_cast<const f32x4*>(rec + RBK + row);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int t = 8 * run + 4 * q4 + e;
-          const bool in = row + e < a.R;
-          lse_r[t] = l4[e];
-          dl_r[t] = d4[e];
-          gid_r[t] = in ? g4[e] : -1;
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t], c2, -l2[e]));
+          pa[run][4 * q4 + e] = (__bf16)p;
+          dsa[run][4 * q4 + e] = (__bf16)(p * (dp[t] - dl[e]));
         }
       }
-    bf16x8 pa[2], dsa[2];
-#pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      const int gid = gid_r[t];
-      const bool vis = gid >= 0 && key <= gid && gid < kt.s1 && key < kt.k1;
-      const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[t], c2, -lse_r[t] * kLog2e)) : 0.f;
-      pa[t >> 3][t & 7] = (__bf16)p;
-      dsa[t >> 3][t & 7] = (__bf16)(p * (dp[t] - dl_r[t]));
-    }
 #pragma unroll
     for (int db = 0; db < ND; ++db)
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        const bf16x8 dob = *reinterpret_cast<const bf16x8*>(dts + tro[db][kk]);
-        const bf16x8 qb = *reinterpret_cast<const bf16x8*>(qts + tro[db][kk]);
+        const bf16x8 dob = *reinterpret_cast<const bf16x8*>(st + ODT + tro[db][kk]);
+        const bf16x8 qb = *reinterpret_cast<const bf16x8*>(st + OQT + tro[db][kk]);
         dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[kk], dob, dv[db], 0, 0, 0);
         dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dsa[kk], qb, dk[db], 0, 0, 0);
       }
   };
 
-  // the (row block, head) steps: rb in [rb0, rb1) outer, the query heads
-  // of KV head g (a.group of them) inner
-  const int group = a.group;
-  const int n_blocks = (kt.rb1 - kt.rb0) * group;
-  auto step_at = [&](int i, int& rb, int& h) {
-    rb = kt.rb0 + i / group;
-    h = g * group + i % group;
-  };
-  if (n_blocks > 0) {
-    int rb, h;
-    step_at(0, rb, h);
-    issue(rb, h, q0s, d0s, qt0s, dt0s);
+  // Ring of four LDS slots: block step j sits in slot j % 4; while step j is
+  // consumed, steps j + 1 and j + 2 are in flight and step j + 3 is issued
+  // into the slot step j - 1 left (every wave finished it before this
+  // step's barrier).
+  if (n_blocks > 0) issue(0, st0);
+  if (n_blocks > 1) issue(1, st1);
+  if (n_blocks > 2) issue(2, st2);
+#define DKDV_STEP(J, CUR, NXT)                                  \
+  {                                                             \
+    if ((J) + 2 < n_blocks)                                     \
+      __builtin_amdgcn_s_waitcnt(wait_vmcnt(2 * PER_STAGE));    \
+    else if ((J) + 1 < n_blocks)                                \
+      __builtin_amdgcn_s_waitcnt(wait_vmcnt(PER_STAGE));        \
+    else                                                        \
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);                  \
+    asm volatile("s_barrier" ::: "memory");                     \
+    if ((J) + 3 < n_blocks) issue((J) + 3, NXT);                \
+    block_step((J), CUR);                                       \
   }
-  for (int i = 0; i < n_blocks; i += 2) {
-    int rb, h, rbn, hn;
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    __syncthreads();
-    if (i + 1 < n_blocks) {
-      step_at(i + 1, rbn, hn);
-      issue(rbn, hn, q1s, d1s, qt1s, dt1s);
-    }
-    step_at(i, rb, h);
-    block_step(rb, h, q0s, d0s, qt0s, dt0s);
-    if (i + 1 >= n_blocks) break;
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    __syncthreads();
-    if (i + 2 < n_blocks) {
-      step_at(i + 2, rbn, hn);
-      issue(rbn, hn, q0s, d0s, qt0s, dt0s);
-    }
-    step_at(i + 1, rb, h);
-    block_step(rb, h, q1s, d1s, qt1s, dt1s);
+  // (guarded steps rather than early exits: one loop exit keeps the
+  // accumulators in place instead of copying them at every exit)
+  for (int i = 0; i < n_blocks; i += 4) {
+    DKDV_STEP(i, st0, st3);
+    if (i + 1 < n_blocks) DKDV_STEP(i + 1, st1, st0);
+    if (i + 2 < n_blocks) DKDV_STEP(i + 2, st2, st1);
+    if (i + 3 < n_blocks) DKDV_STEP(i + 3, st3, st2);
   }
+#undef DKDV_STEP
 
   // accumulator register t of lane half hh: key 32 wave + (t/4)*8 + 4 hh + t%4,
   // d = 32 db + kl
 #pragma unroll
   for (int t = 0; t < 16; ++t) {
-    const int k = kt.k0 + 32 * wave + (t >> 2) * 8 + 4 * hh + (t & 3);
+    const int k = kw0 + (t >> 2) * 8 + 4 * hh + (t & 3);
     if (k >= kt.k1) continue;
     float* const dkp = a.dk + (int64_t(k) * a.Hkv + g) * D + kl;
     float* const dvp = a.dv + (int64_t(k) * a.Hkv + g) * D + kl;
@@ -508,13 +577,15 @@ hipError_t launch_bwd_g(const BwdArgs& a, int n_units, int n_ktiles, hipStream_t
 
 }  // namespace
 
-hipError_t launch_bwd_delta(const void* out, const void* dout, float* delta, int32_t R, int32_t H,
-                            hipStream_t stream) {
+hipError_t launch_bwd_prep(const void* out, const void* dout, const float* lse, const int32_t* index,
+                           const int32_t* row_lo, float* delta, int32_t* rec, int32_t R, int32_t H,
+                           int32_t nrb, hipStream_t stream) {
   if (R == 0) return hipSuccess;
-  const int64_t blocks = (int64_t(R) * H + 15) / 16;
+  const int64_t blocks = (int64_t(nrb) * kBwdRowBlock * H + 15) / 16;
   if (blocks >= (int64_t(1) << 31)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(delta_kernel, dim3(uint32_t(blocks)), dim3(256), 0, stream,
-                     static_cast<const __bf16*>(out), static_cast<const __bf16*>(dout), delta, R, H);
+  hipLaunchKernelGGL(bwd_prep_kernel, dim3(uint32_t(blocks)), dim3(256), 0, stream,
+                     static_cast<const __bf16*>(out), static_cast<const __bf16*>(dout), lse, index, row_lo,
+                     delta, rec, R, H, nrb);
   return hipGetLastError();
 }
 

@@ -197,6 +197,8 @@ cp_status rank_bwd(const void* q, const void* k, const void* v, const void* out,
     a.lse = lse;
     a.delta = reinterpret_cast<const float*>(ws + w.off_delta);
     a.index = reinterpret_cast<const int32_t*>(ws + w.off_index);
+    a.rec = reinterpret_cast<const int32_t*>(ws + w.off_rec);
+    a.blk = reinterpret_cast<const int32_t*>(ws + w.off_blk);
     a.dq = dq;
     a.dk = dk;
     a.dv = dv;
@@ -212,13 +214,15 @@ cp_status rank_bwd(const void* q, const void* k, const void* v, const void* out,
     a.group = heads / kv_heads;
     a.tpad = w.tpad;
     a.rpad = w.rpad;
+    a.nrb = w.nrb;
     a.scale = float(1.0 / std::sqrt(double(head_dim)));
     a.scale_log2 = float(1.4426950408889634 / std::sqrt(double(head_dim)));
     if (R > 0) {
       const int64_t row_bytes = int64_t(heads) * head_dim * 2;
       if (launch_gather(q, a.index, ws + w.off_qr, R, row_bytes, s) != hipSuccess) return CP_EHIP;
-      if (launch_bwd_delta(out, dout, reinterpret_cast<float*>(ws + w.off_delta), int32_t(R), heads, s) !=
-          hipSuccess)
+      if (launch_bwd_prep(out, dout, lse, a.index, reinterpret_cast<const int32_t*>(ws + w.off_row_lo),
+                          reinterpret_cast<float*>(ws + w.off_delta), reinterpret_cast<int32_t*>(ws + w.off_rec),
+                          int32_t(R), heads, w.nrb, s) != hipSuccess)
         return CP_EHIP;
       if (launch_transpose_v(ws + w.off_qr, ws + w.off_qt, int32_t(R), heads, w.rpad, s) != hipSuccess)
         return CP_EHIP;

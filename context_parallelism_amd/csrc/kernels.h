@@ -45,6 +45,9 @@ struct BwdArgs {
   const float* lse;    // forward lse [H, R]
   const float* delta;  // rowsum(dout * out) [H, R]
   const int32_t* index;  // global id per rank row, -1 for pads
+  const int32_t* rec;  // dK/dV row records [H][nrb][4][32]: lse * log2 e (+inf for pads),
+                       // delta, sample start, global id - sample start
+  const int32_t* blk;  // per 32-row block {largest sample start, smallest global id}
   float* dq;           // [R, H, 128]
   float* dk;           // [T, Hkv, 128]
   float* dv;           // [T, Hkv, 128]
@@ -53,12 +56,15 @@ struct BwdArgs {
   const EntryRec* tile_entries;
   const UnitRec* units;
   const KeyTileRec* ktiles;
-  int32_t R, H, Hkv, n_hg, group, tpad, rpad;
+  int32_t R, H, Hkv, n_hg, group, tpad, rpad, nrb;
   float scale, scale_log2;
 };
 
-hipError_t launch_bwd_delta(const void* out, const void* dout, float* delta, int32_t R, int32_t H,
-                            hipStream_t stream);
+// delta[h][r] = rowsum(dout * out) for every rank row, and the dK/dV row
+// records (rec, nrb 32-row blocks; row_lo: sample start per row).
+hipError_t launch_bwd_prep(const void* out, const void* dout, const float* lse, const int32_t* index,
+                           const int32_t* row_lo, float* delta, int32_t* rec, int32_t R, int32_t H,
+                           int32_t nrb, hipStream_t stream);
 // dQ for every unit, then dK/dV for every key tile.
 hipError_t launch_bwd(const BwdArgs& a, int heads_per_wg, int n_units, int n_ktiles,
                       hipStream_t stream);

@@ -250,6 +250,25 @@ void build_bwd_plan(const Meta& m, int32_t rows_bm, BwdPlan& b) {
                    [](const Pending& x, const Pending& y) { return x.cost > y.cost; });
   b.ktiles.reserve(pend.size());
   for (const Pending& q : pend) b.ktiles.push_back(q.k);
+
+  const int64_t R = m.rows;
+  b.row_lo.assign(size_t(R), 0);
+  for (const SampleGeom& g : m.samples) {
+    const int64_t l1 = g.local0 + g.n_img + 2 * int64_t(g.c);
+    for (int64_t l = g.local0; l < l1; ++l) b.row_lo[size_t(l)] = int32_t(g.a);
+  }
+  const int64_t nrb = (R + kBwdRowBlock - 1) / kBwdRowBlock;
+  b.blk.assign(size_t(2 * nrb), 0);
+  for (int64_t rb = 0; rb < nrb; ++rb) {
+    int32_t lo_max = INT32_MIN, hi_min = INT32_MAX;
+    for (int64_t l = rb * kBwdRowBlock; l < std::min(R, (rb + 1) * kBwdRowBlock); ++l) {
+      if (index[size_t(l)] < 0) continue;
+      lo_max = std::max(lo_max, b.row_lo[size_t(l)]);
+      hi_min = std::min(hi_min, index[size_t(l)]);
+    }
+    b.blk[size_t(2 * rb)] = lo_max;
+    b.blk[size_t(2 * rb + 1)] = hi_min;
+  }
 }
 
 }  // namespace cpattn

@@ -125,6 +125,12 @@ struct KeyTileRec { int32_t k0, k1, rb0, rb1, s0, s1, pad0, pad1; };
 struct BwdPlan {
   Plan rows;                        // dQ: row tiles with their ring-step spans and units
   std::vector<KeyTileRec> ktiles;   // dK/dV: every key tile of every sample, longest first
+  std::vector<int32_t> row_lo;      // per rank row: global id of its sample's first token (0 for pads)
+  // per 32-row block: the largest sample start and the smallest global id
+  // over its real rows (INT32_MIN / INT32_MAX when it has none); a key range
+  // [k0, k1] is visible to every row of the block when lo_max <= k0 and
+  // k1 <= hi_min
+  std::vector<int32_t> blk;         // [n_blocks][2] = {lo_max, hi_min}
 };
 
 // rows_bm: rows per dQ row tile.

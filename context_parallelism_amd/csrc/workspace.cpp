@@ -130,7 +130,12 @@ int32_t prepare_bwd_workspace(int64_t seq_len, const int32_t* n_img, const int32
   off = align256(off + p.units.size() * sizeof(UnitRec));
   w.off_ktiles = off;
   off = align256(off + w.plan.ktiles.size() * sizeof(KeyTileRec));
+  w.off_row_lo = off;
+  off = align256(off + w.plan.row_lo.size() * sizeof(int32_t));
+  w.off_blk = off;
+  off = align256(off + w.plan.blk.size() * sizeof(int32_t));
   w.plan_bytes = off;
+  w.nrb = int32_t((R + kBwdRowBlock - 1) / kBwdRowBlock);
   w.rpad = int32_t((R + 63) / 64 * 64);
   w.tpad = vt_row_keys(seq_len);
   w.off_qr = off;
@@ -143,6 +148,8 @@ int32_t prepare_bwd_workspace(int64_t seq_len, const int32_t* n_img, const int32
   off = align256(off + size_t(kv_heads) * w.tpad * head_dim * 2);
   w.off_delta = off;
   off = align256(off + size_t(heads) * R * sizeof(float));
+  w.off_rec = off;
+  off = align256(off + size_t(heads) * w.nrb * 4 * kBwdRowBlock * sizeof(int32_t));
   w.total = off;
   return CP_OK;
 }
@@ -159,6 +166,8 @@ void pack_bwd_plan(const BwdWorkspace& w, uint8_t* dst) {
   put(w.off_tile_entries, p.tile_entries.data(), p.tile_entries.size() * sizeof(EntryRec));
   put(w.off_units, p.units.data(), p.units.size() * sizeof(UnitRec));
   put(w.off_ktiles, w.plan.ktiles.data(), w.plan.ktiles.size() * sizeof(KeyTileRec));
+  put(w.off_row_lo, w.plan.row_lo.data(), w.plan.row_lo.size() * sizeof(int32_t));
+  put(w.off_blk, w.plan.blk.data(), w.plan.blk.size() * sizeof(int32_t));
 }
 
 }  // namespace cpattn
