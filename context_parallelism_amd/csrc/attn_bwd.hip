@@ -29,8 +29,9 @@
 //    copies. The accumulator layout of S (keys in lanes, rows in
 //    registers) is directly the A operand of those products once the rows
 //    are read in the order sigma (bits 2 and 3 of the row swapped). The
-//    row blocks stream through a four-slot LDS ring, three blocks ahead, so
-//    no wave waits on memory inside a step.
+//    row blocks stream through a four-slot LDS ring, two blocks ahead, so
+//    no wave waits on memory inside a step, and each wave overlaps a
+//    step's softmax with the previous step's dV/dK products.
 #include "kernels.h"
 
 namespace cpattn {
@@ -449,8 +450,13 @@ void dkdv_kernel(const BwdArgs a) {
 
   // one (row block, query head) step. Register t of lane half hh holds row
   // 32 rb + 16 (t / 8) + 8 hh + t % 8 of the block.
-  auto block_step = [&](int j, const char* st) {
-    f32x16 s, dp;
+  // A block step is split in three so that a wave overlaps one step's
+  // softmax arithmetic with the previous step's dV/dK products:
+  //   scores(j):   S = Q K^T and dP = dO V^T (rows of step j's slot);
+  //   softmax(j):  P and dS from S, dP and the slot's row records;
+  //   products:    dV += P^T dO and dK += dS^T Q (Q^T, dO^T of the step's slot).
+  // Register t of lane half hh holds row 32 rb + 16 (t / 8) + 8 hh + t % 8.
+  auto scores = [&](int j, const char* st, f32x16& s, f32x16& dp) {
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
       s[t] = 0.f;
@@ -463,10 +469,10 @@ void dkdv_kernel(const BwdArgs a) {
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[jj], s, 0, 0, 0);
       dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vf[jj], dp, 0, 0, 0);
     }
-    const int* const rec = reinterpret_cast<const int*>(st + OREC);
     // every row of the block sees every key of the wave unless the block
     // holds a causal edge or a sample boundary; then S = -inf where the key
     // is outside [sample start, row's global id]
+    const int* const rec = reinterpret_cast<const int*>(st + OREC);
     const int rb = kt.rb0 + j / group;
     if (!(blk[2 * rb] <= kw0 && kw0 + 31 <= blk[2 * rb + 1])) {
 #pragma unroll
@@ -484,9 +490,11 @@ void dkdv_kernel(const BwdArgs a) {
           }
         }
     }
-    // P = exp2(S c2 - lse log2 e) (0 for pad rows, whose record holds +inf),
-    // dS = P (dP - Delta)
-    bf16x8 pa[2], dsa[2];
+  };
+  // P = exp2(S c2 - lse log2 e) (0 for pad rows, whose record holds +inf),
+  // dS = P (dP - Delta), both as bf16 A operands
+  auto softmax = [&](const char* st, const f32x16& s, const f32x16& dp, bf16x8 (&pa)[2], bf16x8 (&dsa)[2]) {
+    const int* const rec = reinterpret_cast<const int*>(st + OREC);
 #pragma unroll
     for (int run = 0; run < 2; ++run)
 #pragma unroll
@@ -502,6 +510,8 @@ void dkdv_kernel(const BwdArgs a) {
           dsa[run][4 * q4 + e] = (__bf16)(p * (dp[t] - dl[e]));
         }
       }
+  };
+  auto products = [&](const bf16x8 (&pa)[2], const bf16x8 (&dsa)[2], const char* st) {
 #pragma unroll
     for (int db = 0; db < ND; ++db)
 #pragma unroll
@@ -513,34 +523,69 @@ void dkdv_kernel(const BwdArgs a) {
       }
   };
 
-  // Ring of four LDS slots: block step j sits in slot j % 4; while step j is
-  // consumed, steps j + 1 and j + 2 are in flight and step j + 3 is issued
-  // into the slot step j - 1 left (every wave finished it before this
-  // step's barrier).
-  if (n_blocks > 0) issue(0, st0);
-  if (n_blocks > 1) issue(1, st1);
-  if (n_blocks > 2) issue(2, st2);
-#define DKDV_STEP(J, CUR, NXT)                                  \
+  // Ring of four LDS slots: block step j sits in slot j % 4. In iteration j
+  // a wave computes scores(j), then products(j - 1) interleaved with
+  // softmax(j); steps j + 1 and j + 2 are in flight meanwhile. Step j + 2 is
+  // issued into the slot of step j - 2, which every wave finished in
+  // iteration j - 1, before this iteration's barrier. Every iteration issues
+  // one stage (past the end, the last step again, into a free slot), so the
+  // count of loads in flight after step j's is always one stage. The slot of
+  // step -1 (st3) holds zeros so that the first iteration's products add
+  // nothing.
+  {
+    const uint4 z = make_uint4(0, 0, 0, 0);
+    uint4* const z3 = reinterpret_cast<uint4*>(st3 + OQT);
+#pragma unroll
+    for (int i = 0; i < 2 * ROWT / 16 / 256; ++i) z3[i * 256 + tid] = z;
+  }
+  bf16x8 pa[2], dsa[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      pa[i][e] = (__bf16)0.f;
+      dsa[i][e] = (__bf16)0.f;
+    }
+  const int last = n_blocks - 1;
+  if (n_blocks > 0) {
+    issue(0, st0);
+    issue(min(1, last), st1);
+  }
+#define DKDV_STEP(J, CUR, PREV, NXT)                            \
   {                                                             \
-    if ((J) + 2 < n_blocks)                                     \
-      __builtin_amdgcn_s_waitcnt(wait_vmcnt(2 * PER_STAGE));    \
-    else if ((J) + 1 < n_blocks)                                \
-      __builtin_amdgcn_s_waitcnt(wait_vmcnt(PER_STAGE));        \
-    else                                                        \
-      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);                  \
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt(PER_STAGE));          \
     asm volatile("s_barrier" ::: "memory");                     \
-    if ((J) + 3 < n_blocks) issue((J) + 3, NXT);                \
-    block_step((J), CUR);                                       \
+    issue(min((J) + 2, last), NXT);                             \
+    f32x16 s, dp;                                               \
+    scores((J), CUR, s, dp);                                    \
+    products(pa, dsa, PREV);                                    \
+    softmax(CUR, s, dp, pa, dsa);                               \
   }
-  // (guarded steps rather than early exits: one loop exit keeps the
-  // accumulators in place instead of copying them at every exit)
-  for (int i = 0; i < n_blocks; i += 4) {
-    DKDV_STEP(i, st0, st3);
-    if (i + 1 < n_blocks) DKDV_STEP(i + 1, st1, st0);
-    if (i + 2 < n_blocks) DKDV_STEP(i + 2, st2, st1);
-    if (i + 3 < n_blocks) DKDV_STEP(i + 3, st3, st2);
+  int i = 0;
+  for (; i + 4 <= n_blocks; i += 4) {
+    DKDV_STEP(i, st0, st3, st2);
+    DKDV_STEP(i + 1, st1, st0, st3);
+    DKDV_STEP(i + 2, st2, st1, st0);
+    DKDV_STEP(i + 3, st3, st2, st1);
   }
+  if (i < n_blocks) DKDV_STEP(i, st0, st3, st2);
+  if (i + 1 < n_blocks) DKDV_STEP(i + 1, st1, st0, st3);
+  if (i + 2 < n_blocks) DKDV_STEP(i + 2, st2, st1, st0);
 #undef DKDV_STEP
+  // the last step's products (its slot is (n_blocks - 1) % 4); the stages
+  // issued past the end land before the kernel exits
+  if (n_blocks > 0) {
+    const int slot = last & 3;
+    if (slot == 0)
+      products(pa, dsa, st0);
+    else if (slot == 1)
+      products(pa, dsa, st1);
+    else if (slot == 2)
+      products(pa, dsa, st2);
+    else
+      products(pa, dsa, st3);
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
   // accumulator register t of lane half hh: key 32 wave + (t/4)*8 + 4 hh + t%4,
   // d = 32 db + kl
