@@ -101,3 +101,117 @@ def test_backward_deterministic(cp):
     b = bw(out, lse, dout)
     torch.cuda.synchronize()
     assert all(torch.equal(x, y) for x, y in zip(a, b))
+
+
+# ------------------------------------------------ full-size shares, sampled
+# At the full workload sizes the oracle computes, one by one, what depends
+# on few rows: dq of sampled rank rows (a row's dq depends on that row
+# alone), and dk/dv of the last keys of each sample that the rank's rows see
+# (only the rows at or after such a key see it). Keys no rank row sees must
+# be exactly 0, and sum_keys dv = sum_rows dout per KV head (softmax rows sum
+# to 1), within the bf16 rounding of P (unit roundoff 2^-8, doubled).
+
+def _f32(t):
+    return t.detach().float().cpu().numpy()
+
+
+def _exact_dq_rows(q, k, v, dout, idx, cu, rows, H, Hkv):
+    D = q.shape[2]
+    scale = oracle.softmax_scale(D)
+    ids = idx[rows].astype(np.int64)
+    smp = np.searchsorted(cu, ids, side="right") - 1
+    ref = np.zeros((len(rows), H, D))
+    for s in np.unique(smp):
+        sel = np.nonzero(smp == s)[0]
+        a, b = int(cu[s]), int(cu[s + 1])
+        allowed = oracle.visible(np.arange(a, b), ids[sel])
+        for h in range(H):
+            g = oracle.kv_head_of(h, H, Hkv)
+            gq, _, _ = oracle.attend_backward(_f32(q[ids[sel], h]), _f32(k[a:b, g]), _f32(v[a:b, g]), allowed,
+                                              scale, _f32(dout[rows[sel], h]))
+            ref[sel, h] = gq
+    return ref
+
+
+def _exact_last_keys(q, k, v, dout, idx, cu, s, n_keys, H, Hkv):
+    """dk, dv of the last n_keys keys (of sample s) that the rank's rows see."""
+    D = q.shape[2]
+    scale = oracle.softmax_scale(D)
+    a, b = int(cu[s]), int(cu[s + 1])
+    ids = idx.astype(np.int64)
+    mine = np.nonzero((ids >= a) & (ids < b))[0]
+    j0 = max(int(ids[mine].max()) - n_keys + 1, a)
+    sel = mine[ids[mine] >= j0]  # every rank row that sees a key >= j0
+    allowed = oracle.visible(np.arange(a, b), ids[sel])
+    n = int(ids[mine].max()) + 1 - j0
+    dk = np.zeros((n, Hkv, D))
+    dv = np.zeros_like(dk)
+    for h in range(H):
+        g = oracle.kv_head_of(h, H, Hkv)
+        _, gk, gv = oracle.attend_backward(_f32(q[ids[sel], h]), _f32(k[a:b, g]), _f32(v[a:b, g]), allowed,
+                                           scale, _f32(dout[sel, h]))
+        dk[:, g] += gk[j0 - a:j0 - a + n]
+        dv[:, g] += gv[j0 - a:j0 - a + n]
+    return j0, dk, dv
+
+
+@pytest.mark.parametrize("num", [4, 5])
+def test_backward_workload_sampled(cp, num):
+    import workloads
+    from gpu_common import sample_rows
+
+    w = workloads.get(num)
+    q, k, v = workloads.make_inputs(w)
+    r = w.ranks[0]
+    cu = w.cu_seqlens if w.n_samples > 1 else None
+    n_img = w.n_img_array if any(w.n_img) else None
+    idx, cu_rows = oracle.partition_index(w.seq_len, n_img, cu, w.cp_size, r)
+    H, Hkv, D = w.heads, w.kv_heads, w.head_dim
+    rng = np.random.default_rng(w.seed + 7)
+    dout = torch.from_numpy(rng.standard_normal((len(idx), H, D), dtype=np.float32)).to(torch.bfloat16)
+    dout[torch.from_numpy(idx < 0)] = 0
+    print(f"bwd workload {num} rank {r}: R={len(idx)} T={w.seq_len}", flush=True)
+    qd, kd, vd, dd = (t.to(DEV) for t in (q, k, v, dout))
+    out, lse = cp.rank_fwd(qd, kd, vd, cp_size=w.cp_size, cp_rank=r, n_img=n_img, cu_seqlens=cu)
+    bw = cp.RankAttentionBackward(qd, kd, vd, cp_size=w.cp_size, cp_rank=r, n_img=n_img, cu_seqlens=cu)
+    dq, dk, dv = (t.clone() for t in bw(out, lse, dd))
+    dq2, dk2, dv2 = bw(out, lse, dd)
+    torch.cuda.synchronize()
+    assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
+    assert torch.isfinite(dq).all() and torch.isfinite(dk).all() and torch.isfinite(dv).all()
+    assert torch.all(dq[torch.from_numpy(idx < 0).to(DEV)] == 0)
+
+    cu64 = np.array([0, w.seq_len], np.int64) if cu is None else np.asarray(cu, np.int64)
+    rows = sample_rows(idx, cu_rows, 12, seed=num)
+    rows = rows[idx[rows] >= 0]
+    ref = _exact_dq_rows(q, k, v, dout, idx, cu64, rows, H, Hkv)
+    e = rel_err(dq[torch.as_tensor(rows, device=DEV)], ref)
+    print(f"  dq on {len(rows)} sampled rows: rel max-abs {e:.2e}", flush=True)
+    assert e <= BWD_RTOL
+
+    # keys that no rank row sees: exactly zero
+    ids = idx.astype(np.int64)
+    seen = np.zeros(w.seq_len, bool)
+    for s in range(len(cu64) - 1):
+        mine = ids[(ids >= cu64[s]) & (ids < cu64[s + 1])]
+        if len(mine):
+            seen[cu64[s]:mine.max() + 1] = True
+    unseen = torch.as_tensor(~seen, device=DEV)
+    assert torch.all(dk[unseen] == 0) and torch.all(dv[unseen] == 0)
+
+    for s in range(min(len(cu64) - 1, 3)):
+        j0, rk, rv = _exact_last_keys(q, k, v, dout, idx, cu64, s, 24, H, Hkv)
+        sl = slice(j0, j0 + rk.shape[0])
+        ek, ev = rel_err(dk[sl], rk), rel_err(dv[sl], rv)
+        print(f"  sample {s}: dk/dv of keys [{j0}, {j0 + rk.shape[0]}) rel max-abs {ek:.2e} / {ev:.2e}", flush=True)
+        assert max(ek, ev) <= BWD_RTOL
+
+    # sum over keys of dv = sum over the rank's rows of dout, per KV head
+    grp = H // Hkv
+    do64 = dout.double().numpy().reshape(len(idx), Hkv, grp, D)
+    want = do64.sum(axis=(0, 2))
+    bound = 2.0 ** -7 * np.abs(do64).sum(axis=(0, 2)) + 1e-3
+    got = dv.double().sum(dim=0).cpu().numpy()
+    worst = float((np.abs(got - want) / bound).max())
+    print(f"  sum_keys dv vs sum_rows dout: worst |diff| / bound {worst:.3f}", flush=True)
+    assert worst <= 1.0

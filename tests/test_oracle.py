@@ -648,3 +648,36 @@ def test_mutant_backward_scale_is_caught(monkeypatch):
     monkeypatch.setattr(cp_oracle, "attend_backward", bad)
     assert pin_backward_finite_differences(n_checks=8) > 1e-3
 
+
+
+def test_backward_sampling_helpers_match_full_oracle():
+    # the full-size GPU backward test checks sampled dq rows and the last
+    # keys of each sample with oracle pieces (attend_backward over a subset of
+    # rows); on a small packed case those pieces equal the full oracle
+    import importlib.util
+    import os
+
+    import torch
+
+    path = os.path.join(os.path.dirname(__file__), "test_gpu_backward.py")
+    spec = importlib.util.spec_from_file_location("gpu_backward_helpers", path)
+    m = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(m)
+    T, H, Hkv, D, P, r = 700, 4, 2, 128, 3, 1
+    cu = np.array([0, 300, 700], np.int32)
+    img = np.array([10, 0], np.int32)
+    idx, _ = oracle.partition_index(T, img, cu, P, r)
+    q, k, v, dout = m.draw(5, T, H, Hkv, D, len(idx))
+    dout[torch.from_numpy(idx < 0)] = 0
+    fq, fk, fv = oracle.rank_attention_backward(q, k, v, dout, img, cu, P, r)
+    rows = np.nonzero(idx >= 0)[0][::17]
+    ref = m._exact_dq_rows(q, k, v, dout, idx, cu.astype(np.int64), rows, H, Hkv)
+    assert np.abs(ref - fq[rows]).max() <= 1e-12
+    for s in range(2):
+        j0, rk, rv = m._exact_last_keys(q, k, v, dout, idx, cu.astype(np.int64), s, 24, H, Hkv)
+        assert len(rk) == 24
+        assert np.abs(rk - fk[j0:j0 + 24]).max() <= 1e-12
+        assert np.abs(rv - fv[j0:j0 + 24]).max() <= 1e-12
+    # sum over keys of dv = sum over rows of dout, per KV head
+    do64 = dout.double().numpy().reshape(len(idx), Hkv, H // Hkv, D)
+    assert np.abs(fv.sum(axis=0) - do64.sum(axis=(0, 2))).max() <= 1e-9
