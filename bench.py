@@ -2,8 +2,9 @@
 
 Default workload: text L=65536, P=8 (16 chunks of 4096), rank 3, GQA 32/8
 heads, head_dim 128, bf16 Q/K/V ~ N(0,1), batch 1. One step is one call of
-cp_attn_rank_fwd: host plan + upload, Q gather, per-step attention over all
-P ring steps, LSE merge. Inputs are resident in HBM before timing starts.
+cp_attn_rank_fwd: host plan + upload, V relayout, attention over all P ring
+steps (the Q gather fused into the kernel's Q loads), LSE merge. Inputs are
+resident in HBM before timing starts.
 
 Prints one JSON line. ``roofline`` covers the dominant kernel (the per-step
 attention): achieved = useful FLOPs per launch / its average duration, timed
@@ -362,8 +363,6 @@ def main():
     attn_ms = float(stage[:, 3].mean())
     achieved = useful / (attn_ms * 1e-3) / 1e12
     R = ra.R
-    esize = 2 if w.dtype == "bf16" else 4
-    gather_bytes = 2 * R * w.heads * w.head_dim * esize
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -391,7 +390,6 @@ def main():
                       "call_median": round(float(np.median(call)), 4),
                       "call_p10": round(float(np.percentile(call, 10)), 4),
                       "call_p90": round(float(np.percentile(call, 90)), 4)},
-        "gather_GBps": round(gather_bytes / (float(stage[:, 1].mean()) * 1e-3) / 1e9, 1),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic_from_profile(),

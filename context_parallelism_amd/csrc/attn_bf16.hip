@@ -110,7 +110,7 @@ void attn_step_bf16_kernel(const AttnArgs a) {
   // Q as the B operand of S^T = K Q^T: lane holds q[row][16*jj + 8*hh + 0..7].
   bf16x8 qf[NQ];
   {
-    const __bf16* qp = static_cast<const __bf16*>(a.qr) + (int64_t(lrow) * a.H + h) * D + 8 * hh;
+    const __bf16* qp = static_cast<const __bf16*>(a.q) + (int64_t(grow) * a.H + h) * D + 8 * hh;
 #pragma unroll
     for (int jj = 0; jj < NQ; ++jj) {
       if (row_ok) {
@@ -402,7 +402,7 @@ void attn_rank_bf16_d128_kernel(const AttnArgs a) {
 
   bf16x8 qf[NQ];
   {
-    const __bf16* qp = static_cast<const __bf16*>(a.qr) + (int64_t(lrow) * a.H + h) * D + 8 * hh;
+    const __bf16* qp = static_cast<const __bf16*>(a.q) + (int64_t(grow) * a.H + h) * D + 8 * hh;
 #pragma unroll
     for (int jj = 0; jj < NQ; ++jj) {
       if (row_ok) {

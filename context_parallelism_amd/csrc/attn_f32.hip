@@ -31,7 +31,7 @@ __global__ __launch_bounds__(kThreads) void attn_step_f32_kernel(AttnArgs a) {
   const int lrow = tile.local0 + rin;
   const int grow = tile.g0 + rin;
   const int kvh = h / a.group;
-  const float* qp = static_cast<const float*>(a.qr) + (int64_t(lrow) * a.H + h) * D + half * HALF;
+  const float* qp = static_cast<const float*>(a.q) + (int64_t(grow) * a.H + h) * D + half * HALF;
   const float* kg = static_cast<const float*>(a.k);
   const float* vg = static_cast<const float*>(a.v);
   const int64_t tok_stride = int64_t(a.Hkv) * D;

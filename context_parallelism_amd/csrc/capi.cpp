@@ -89,15 +89,14 @@ cp_status rank_fwd(const void* q, const void* k, const void* v, int32_t dtype, i
     if (workspace_bytes < w.total) return CP_ENOSPC;
     hipStream_t s = static_cast<hipStream_t>(stream);
     uint8_t* ws = static_cast<uint8_t*>(workspace);
-    const size_t esize = dtype == CP_DTYPE_BF16 ? 2 : 4;
 
     if (mark(events, 0, s) != hipSuccess) return CP_EHIP;
     if (stage_and_upload(w.plan_bytes, [&](uint8_t* dst) { pack_plan(w, dst); }, ws, s) != hipSuccess)
       return CP_EHIP;
     if (mark(events, 1, s) != hipSuccess) return CP_EHIP;
+    // The attention kernels read each row tile's Q rows in place (a tile is
+    // a run of consecutive global ids), so the gather has no pass of its own.
     const int32_t* index = reinterpret_cast<const int32_t*>(ws + w.off_index);
-    if (launch_gather(q, index, ws + w.off_qr, R, int64_t(heads) * head_dim * esize, s) != hipSuccess)
-      return CP_EHIP;
     if (mark(events, 2, s) != hipSuccess) return CP_EHIP;
 
     AttnArgs a;
@@ -109,7 +108,7 @@ cp_status rank_fwd(const void* q, const void* k, const void* v, int32_t dtype, i
       a.vt = ws + w.off_vt;
     }
     if (mark(events, 3, s) != hipSuccess) return CP_EHIP;
-    a.qr = ws + w.off_qr;
+    a.q = q;
     a.k = k;
     a.v = v;
     a.part_o = reinterpret_cast<float*>(ws + w.off_po);

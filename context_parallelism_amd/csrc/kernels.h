@@ -10,7 +10,8 @@
 namespace cpattn {
 
 struct AttnArgs {
-  const void* qr;        // gathered rank-local Q [R, H, D]
+  const void* q;         // Q [T, H, D]: a row tile is a run of consecutive global ids, so its
+                         // rows are read in place (the rank's gather fused into the Q load)
   const void* k;         // [T, Hkv, D]
   const void* v;         // [T, Hkv, D]
   const void* vt;        // V^T [Hkv, D, tpad] (bf16, head_dim 128 only), zero past T

@@ -73,7 +73,7 @@ inline int64_t text_pairs(const SampleGeom& g, int64_t lo, int64_t cnt) {
 }  // namespace
 
 void fill_index(const Meta& m, int32_t* index, int32_t* cu_rows_local) {
-  const int32_t P = m.P, r = m.r;
+  const int32_t r = m.r;
   for (size_t s = 0; s < m.samples.size(); ++s) {
     const SampleGeom& g = m.samples[s];
     if (cu_rows_local) cu_rows_local[s] = int32_t(g.local0);
@@ -93,7 +93,7 @@ void fill_index(const Meta& m, int32_t* index, int32_t* cu_rows_local) {
 }
 
 void pair_counts(const Meta& m, int64_t* padded, int64_t* real) {
-  const int32_t P = m.P, r = m.r;
+  const int32_t r = m.r;
   int64_t pp = 0, rr = 0;
   for (const SampleGeom& g : m.samples) {
     int64_t img = int64_t(g.n_img) * (g.n_img + 1) / 2;  // image row i sees i + 1 keys
@@ -113,7 +113,7 @@ void pair_counts(const Meta& m, int64_t* padded, int64_t* real) {
 
 std::vector<Segment> segments(const Meta& m) {
   std::vector<Segment> out;
-  const int32_t P = m.P, r = m.r;
+  const int32_t r = m.r;
   for (size_t s = 0; s < m.samples.size(); ++s) {
     const SampleGeom& g = m.samples[s];
     if (g.n_img > 0) out.push_back({g.local0, g.a, g.n_img, int32_t(s), 0});

@@ -37,7 +37,6 @@ int32_t prepare_workspace(int64_t seq_len, const int32_t* n_img, const int32_t* 
   w.shape = tile_shape(dtype, heads / kv_heads, head_dim);
   build_plan(w.meta, w.shape.rows, kBlockN, w.plan);
   const size_t R = size_t(w.meta.rows);
-  const size_t esize = dtype == CP_DTYPE_BF16 ? 2 : 4;
   size_t off = 0;
   w.off_index = off;
   off = align256(off + R * sizeof(int32_t));
@@ -59,8 +58,6 @@ int32_t prepare_workspace(int64_t seq_len, const int32_t* n_img, const int32_t* 
   w.off_units = off;
   off = align256(off + w.launch_units().size() * sizeof(UnitRec));
   w.plan_bytes = off;
-  w.off_qr = off;
-  off = align256(off + R * size_t(heads) * head_dim * esize);
   w.off_vt = off;
   if (dtype == CP_DTYPE_BF16 && head_dim == 128) {
     w.tpad = vt_row_keys(seq_len);

@@ -108,9 +108,8 @@ cp_status cp_pair_counts(int64_t seq_len, const int32_t *n_img, const int32_t *c
 /*
  * cp_attn_rank_workspace_size -- bytes of device workspace that
  * cp_attn_rank_fwd needs for these arguments (host only). The workspace
- * holds the uploaded plan, the gathered rank-local Q rows, the V^T copy
- * (bf16, head_dim 128), and the per-step partial outputs (fp32) and
- * log-sum-exps.
+ * holds the uploaded plan, the V^T copy (bf16, head_dim 128), and the
+ * per-step partial outputs (fp32) and log-sum-exps.
  */
 cp_status cp_attn_rank_workspace_size(int64_t seq_len, const int32_t *n_img,
                                       const int32_t *cu_seqlens, int32_t n_samples,
@@ -143,7 +142,9 @@ cp_status cp_attn_rank_plan_stats(int64_t seq_len, const int32_t *n_img, const i
  * Steps, all enqueued on `stream` (no host synchronisation):
  *   1. plan on the host (partition, per-step key spans, work list) and
  *      upload it into the workspace;
- *   2. gather the rank's query rows from q (page section 1.1, index_select);
+ *   2. gather the rank's query rows from q (page section 1.1, index_select):
+ *      fused into step 3's query loads -- a row tile is a run of
+ *      consecutive global ids, read in place from q;
  *   3. for every ring step s = 0..P-1 (source rank j = (r - s) mod P; the
  *      image prefix and the rank's own chunks at s = 0, chunks j and
  *      2P-1-j at s > 0), blockwise causal attention of the rank's rows to
@@ -176,7 +177,8 @@ cp_status cp_attn_rank_fwd(const void *q, const void *k, const void *v, int32_t 
 /*
  * cp_attn_rank_fwd_timed -- cp_attn_rank_fwd that also records six
  * caller-created hipEvent_t on `stream` at its stage boundaries:
- * events[0] before the plan upload, [1] after it, [2] after the gather,
+ * events[0] before the plan upload, [1] after it, [2] after the gather
+ * (which the attention kernels now do as they load Q: [2] follows [1]),
  * [3] after the V relayout (bf16, head_dim 128; otherwise right after [2]),
  * [4] after the per-step attention, [5] after the merge. A caller can then
  * time one stage with hipEventElapsedTime, without a profiler. events may
