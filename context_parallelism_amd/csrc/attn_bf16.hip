@@ -300,24 +300,27 @@ void attn_step_bf16_kernel(const AttnArgs a) {
 // workgroup's 8 waves share every K/V tile.
 //
 // Differences from the kernel above:
-//  * V is read from a V^T copy made once per call, blocked by 8 keys
-//    (vt[g][key/8][d][key%8]), so the PV operand needs no transposing
-//    read: each lane's 8 keys at one d are 16 contiguous bytes, read with
-//    ds_read_b128 like K, and a 64-key tile is one contiguous 16 KiB run.
+//  * V stays in its [T, Hkv, D] layout. The PV product O^T = V^T P^T needs,
+//    per lane, 8 consecutive keys at one d; gfx950's transposing LDS read
+//    (ds_read_b64_tr_b16) gives exactly that from a row-major V tile: in a
+//    16-lane group, lane j receives element j % 4 of the 4-element rows that
+//    lanes 4e + j / 4 address (e = 0..3). Two such reads (keys +0..3 and
+//    +4..7) form one 8-key operand.
 //  * Lane ql of the QK^T operand reads K row sigma(ql), sigma swapping bits
 //    2 and 3 of the row index. The S^T accumulator register r of lane half
 //    hh then holds key 16*(r/8) + 8*hh + r%8: eight consecutive keys per
-//    MFMA operand, exactly the keys of the lane's contiguous V^T read.
-//  * K and V^T tiles go from HBM straight into LDS (buffer_load ... lds),
-//    no staging registers. One wave instruction fills 1 KiB of LDS (lane l
-//    at byte 16*l), so rows are unpadded and bank conflicts are avoided by
+//    MFMA operand, exactly the keys of the lane's PV operand.
+//  * K and V tiles go from HBM straight into LDS (buffer_load ... lds), no
+//    staging registers. One wave instruction fills 1 KiB of LDS (lane l at
+//    byte 16*l), so rows are unpadded and bank conflicts are avoided by
 //    XOR-swizzling 16-byte granules: K granule g of row r sits at
-//    g ^ (r & 15) (16 rows read together land on 16 granule slots); V^T
-//    granule g of row d sits at g ^ ((d >> 1) & 7) (128-byte rows, two per
-//    bank sweep, 16 rows read together land on 16 slots). All LDS read
-//    addresses are per-lane constants plus immediates.
-//  * Key tiles start at multiples of 8 keys so V^T rows load 16-byte
-//    aligned; keys below the span start are masked like those past its end.
+//    g ^ (r & 15) (16 rows read together land on 16 granule slots); V
+//    granule g of row r sits at g ^ f(r), f(r) = ((r & 3) << 2) | ((r >> 2) & 3),
+//    so the 4 rows x 4 granules a half-wave's transposing read touches land
+//    on 16 distinct slots. All LDS read addresses are per-lane constants
+//    plus immediates.
+//  * Key tiles start at multiples of 8 keys (keys below the span start are
+//    masked like those past its end).
 //  * Ping-pong: each wave alternates a softmax phase (VALU: exp, sum,
 //    convert) and a matrix phase (MFMA: PV of tile t, QK^T of tile t+1).
 //    Group 1 runs one phase behind group 0 and every phase ends at a
@@ -340,7 +343,7 @@ template <int G>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_rank_bf16_d128_kernel(const AttnArgs a) {
   constexpr int D = 128, BN = kBlockN;
-  constexpr int TILE = BN * D * 2;           // bytes of one K (or V^T) tile
+  constexpr int TILE = BN * D * 2;           // bytes of one K (or V) tile
   constexpr int CH = TILE / 1024 / 4;        // LDS-DMA instructions per loading wave per tensor
   constexpr int ND = D / 32, NQ = D / 16;
   constexpr int RB = 4 / G;                  // row blocks per wave group
@@ -418,29 +421,38 @@ void attn_rank_bf16_d128_kernel(const AttnArgs a) {
   // phases. Wave wg fills 1-KiB pieces wg*CH..+CH-1 of each tile.
   const int tok_bytes = a.Hkv * D * 2;
   const char* kbase = static_cast<const char*>(a.k) + int64_t(kvh) * D * 2;
-  // V^T: 8-key blocks of 128 d-rows (16 bytes each); a tile at kt is the
-  // contiguous 16 KiB starting at key block kt / 8
-  const char* vtbase = static_cast<const char*>(a.vt) + int64_t(kvh) * a.tpad * D * 2;
+  const char* vbase = static_cast<const char*>(a.v) + int64_t(kvh) * D * 2;
+  // V granule swizzle of tile row r (see the kernel notes)
+  auto vswz = [](int r) { return ((r & 3) << 2) | ((r >> 2) & 3); };
   int kgo[CH], vgo[CH];
 #pragma unroll
   for (int i = 0; i < CH; ++i) {
     const int c = wg * CH + i;
     const int krow = 4 * c + (lane >> 4), kp = lane & 15;
     kgo[i] = krow * tok_bytes + 16 * (kp ^ (krow & 15));
-    const int d = 8 * c + (lane >> 3), vp = lane & 7;
-    vgo[i] = (vp ^ ((d >> 1) & 7)) * (D * 16) + d * 16;
+    vgo[i] = krow * tok_bytes + 16 * (kp ^ vswz(krow));
   }
 
   const int srow = (ql & ~12) | ((ql & 4) << 1) | ((ql & 8) >> 1);
   int kro[NQ];
 #pragma unroll
   for (int jj = 0; jj < NQ; ++jj) kro[jj] = srow * 256 + 16 * ((2 * jj + hh) ^ (srow & 15));
-  const int vx = (ql >> 1) & 7;
-  int vro[2][2];
+  // PV operand reads: for d block db and key half tb (keys +4 tb .. +4 tb + 3
+  // of the lane's 8), this lane addresses tile row 8 (g >> 1) + 4 tb + s / 4
+  // (plus the 16-key step's row offset, an immediate) at d
+  // 32 db + 16 (g & 1) + 4 (s % 4), where g = lane / 16 and s = lane % 16.
+  int vtr[ND][2];
+  {
+    const int g16 = lane >> 4, s16 = lane & 15;
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+    for (int db = 0; db < ND; ++db)
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) vro[kb][sub] = ql * 128 + 16 * ((4 * kb + 2 * sub + hh) ^ vx);
+      for (int tb = 0; tb < 2; ++tb) {
+        const int r = 8 * (g16 >> 1) + 4 * tb + (s16 >> 2);
+        const int gran = 4 * db + 2 * (g16 & 1) + ((s16 & 3) >> 1);
+        vtr[db][tb] = r * 256 + 16 * (gran ^ vswz(r)) + 8 * (s16 & 1);
+      }
+  }
 
   f32x16 sc[2];     // scores of the tile whose softmax is next
   bf16x8 pb[2][2];  // probabilities of the tile whose PV is next
@@ -470,14 +482,19 @@ void attn_rank_bf16_d128_kernel(const AttnArgs a) {
     }
   };
   auto pv = [&](const char* vb0) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 #pragma unroll
     for (int db = 0; db < ND; ++db)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub) {
-          const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vb0 + db * 32 * 128 + vro[kb][sub]);
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[kb][sub], o[db], 0, 0, 0);
+          const char* const rb = vb0 + (32 * kb + 16 * sub) * 256;
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(rb + vtr[db][0]));
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(rb + vtr[db][1]));
+          const s16x8 v8 = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v8), pb[kb][sub], o[db], 0, 0, 0);
         }
   };
   // Register fences: an empty asm that "reads and writes" the values forces
@@ -607,8 +624,8 @@ void attn_rank_bf16_d128_kernel(const AttnArgs a) {
   };
   auto vrsrc = [&](const TileCursor& c) {
     const int kt = __builtin_amdgcn_readfirstlane(c.kt);
-    const int valid = __builtin_amdgcn_readfirstlane(max(a.tpad - kt, 0) * D * 2);
-    return make_rsrc(vtbase + int64_t(kt) * D * 2, valid);
+    const int valid = __builtin_amdgcn_readfirstlane(max(min(c.k1 - kt, BN), 0) * tok_bytes);
+    return make_rsrc(vbase + int64_t(kt) * tok_bytes, valid);
   };
   // Phase barrier: a bare s_barrier. __syncthreads() would add a release
   // fence, i.e. wait for every outstanding memory operation of the wave --
@@ -631,8 +648,8 @@ void attn_rank_bf16_d128_kernel(const AttnArgs a) {
                                                vgo[i], 0, 0, 0);
     }
   };
-  // Matrix phase: PV of tile t and QK^T of tile t+1, 32 MFMAs each fed by
-  // one 1-KiB LDS read issued kLdsAhead MFMAs ahead. With loads, one
+  // Matrix phase: PV of tile t and QK^T of tile t+1, 32 MFMAs fed by LDS
+  // reads issued kLdsAhead MFMAs ahead. With loads, one
   // LDS-DMA instruction goes out every four MFMAs, so the memory queue never
   // holds up the matrix work. On the last tile the QK^T reads a stale K
   // slot; those scores are never used.
@@ -640,30 +657,19 @@ void attn_rank_bf16_d128_kernel(const AttnArgs a) {
     __builtin_amdgcn_s_setprio(1);  // favour this wave's MFMA issue
     pv(vb);
     qk(kb);
-    if (loads) {
-      load_group(krsrc(ck), vrsrc(cv), kdst, vdst);
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kLdsAhead, 0);
-      int d = kLdsAhead;
+    // LDS reads per MFMA: two for the 16 PV MFMAs (transposing reads), one
+    // for the 16 QK^T MFMAs; each MFMA's reads go out kLdsAhead MFMAs ahead
+    static_assert(kLdsAhead <= 16, "the first kLdsAhead MFMAs are PV MFMAs");
+    if (loads) load_group(krsrc(ck), vrsrc(cv), kdst, vdst);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * kLdsAhead, 0);
 #pragma unroll
-      for (int i = 0; i < 2 * CH; ++i) {
-        __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
-#pragma unroll
-        for (int q = 0; q < 32 / (2 * CH); ++q) {
-          __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-          if (d < 32) {
-            __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-            ++d;
-          }
-        }
-      }
-    } else {
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kLdsAhead, 0);
-#pragma unroll
-      for (int i = 0; i < 32 - kLdsAhead; ++i) {
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    for (int i = 0; i < 32; ++i) {
+      if (loads && i % (32 / (2 * CH)) == 0) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      if (i + kLdsAhead < 16)
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+      else if (i + kLdsAhead < 32)
         __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, kLdsAhead, 0);
     }
     fence_s();
     __builtin_amdgcn_s_setprio(0);

@@ -100,13 +100,8 @@ cp_status rank_fwd(const void* q, const void* k, const void* v, int32_t dtype, i
     if (mark(events, 2, s) != hipSuccess) return CP_EHIP;
 
     AttnArgs a;
-    a.vt = nullptr;
-    a.tpad = w.tpad;
-    if (w.tpad > 0) {
-      if (launch_transpose_v(v, ws + w.off_vt, int32_t(seq_len), kv_heads, w.tpad, s) != hipSuccess)
-        return CP_EHIP;
-      a.vt = ws + w.off_vt;
-    }
+    // (no V relayout: the bf16 head_dim-128 kernel reads V tiles row-major
+    // and transposes them in its LDS reads)
     if (mark(events, 3, s) != hipSuccess) return CP_EHIP;
     a.q = q;
     a.k = k;

@@ -58,11 +58,6 @@ int32_t prepare_workspace(int64_t seq_len, const int32_t* n_img, const int32_t* 
   w.off_units = off;
   off = align256(off + w.launch_units().size() * sizeof(UnitRec));
   w.plan_bytes = off;
-  w.off_vt = off;
-  if (dtype == CP_DTYPE_BF16 && head_dim == 128) {
-    w.tpad = vt_row_keys(seq_len);
-    off = align256(off + size_t(kv_heads) * head_dim * size_t(w.tpad) * 2);
-  }
   w.off_po = off;
   if (w.unit_kernel && !w.unit_per_step) {
     const size_t n_hg = size_t(heads / w.shape.heads_per_wg);

@@ -2,7 +2,6 @@
 // workspace holds, each region 256-byte aligned:
 //   plan   : index int32[R], step mask uint32[R], tiles, entries, spans,
 //            step-ordered entries, units (uploaded from the host in one copy);
-//   vt     : V^T blocked by 8 keys (bf16 with head_dim 128 only; else empty);
 //   part_o : per-step partial outputs, fp32. Per-step kernels: [P, R, H, D].
 //            Unit kernel (bf16, head_dim 128): one slot per (workgroup, step,
 //            wave) of kUnitSlotFloats, in the wave's own register order;
@@ -29,8 +28,7 @@ struct Workspace {
     return unit_per_step ? plan.step_units : plan.units;
   }
   size_t plan_bytes = 0;
-  size_t off_vt = 0, off_po = 0, off_pl = 0, total = 0;
-  int32_t tpad = 0;  // keys per V^T row (0: no V^T region)
+  size_t off_po = 0, off_pl = 0, total = 0;
 };
 
 // Below this many workgroups the unit kernel takes one ring step per unit
