@@ -18,17 +18,18 @@
 //  * dQ: one workgroup of 4 waves per (row tile, head group); each wave owns
 //    32 rows of one head and walks the tile's key spans over all ring steps,
 //    recomputing S^T = K Q^T and dP^T = V dO^T (K and V rows from LDS, Q and
-//    dO in registers) and accumulating dQ^T += K^T dS^T (K^T from a blocked
-//    copy, as the forward reads V^T); K, V and K^T tiles stream through a
-//    three-slot LDS ring, two tiles ahead;
+//    dO in registers) and accumulating dQ^T += K^T dS^T, the K^T operand
+//    read from the same row-major K tile with transposing LDS reads; K and V
+//    tiles stream through a three-slot LDS ring, two tiles ahead;
 //  * dK/dV: one workgroup of 4 waves per (128-key tile, KV head); each wave
 //    owns 32 keys, keeps its K and V rows in registers, and walks the
 //    rank's 32-row blocks that see the tile, for every query head of the KV
 //    head: S = Q K^T and dP = dO V^T (Q, dO rows from LDS), then
-//    dV += P^T dO and dK += dS^T Q with Q^T and dO^T read from blocked
-//    copies. The accumulator layout of S (keys in lanes, rows in
-//    registers) is directly the A operand of those products once the rows
-//    are read in the order sigma (bits 2 and 3 of the row swapped). The
+//    dV += P^T dO and dK += dS^T Q, the dO and Q operands read from the
+//    same row-major tiles with transposing LDS reads. The accumulator layout
+//    of S (keys in lanes, rows in registers) is directly the A operand of
+//    those products once the rows are read in the order sigma (bits 2 and 3
+//    of the row swapped). The
 //    row blocks stream through a four-slot LDS ring, two blocks ahead, so
 //    no wave waits on memory inside a step, and each wave overlaps a
 //    step's softmax with the previous step's dV/dK products.
@@ -40,6 +41,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
@@ -51,6 +53,35 @@ constexpr int kWaitVmcnt0 = 0x0F70;       // s_waitcnt vmcnt(0), expcnt and lgkm
 // s_waitcnt immediate for vmcnt(n) alone (n < 64: low four bits in [3:0],
 // high two in [15:14]; expcnt 7 and lgkmcnt 15 mean "no wait").
 constexpr int wait_vmcnt(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+
+// Granule swizzle of row r of a row-major LDS tile (16-byte granule g of row
+// r sits at slot g ^ tile_swizzle(r)). It is a bijection of r & 15, so 16
+// rows read at one granule land on 16 slots, and the 4 rows x 4 granules
+// that a half-wave's transposing read touches land on 16 slots too.
+__device__ inline int tile_swizzle(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
+// Transposing LDS read (ds_read_b64_tr_b16): in a 16-lane group, lane j
+// receives element j % 4 of the 4-element rows that lanes 4e + j / 4
+// address (e = 0..3). tr_offsets gives, for an operand of 8 consecutive tile
+// rows R0 + 8 (lane / 32) + 0..7 at column c0 + lane % 32 (R0 a multiple of
+// 16, c0 of 32; the row offset R0 * 256 is added by the caller), the two
+// per-lane byte offsets of its halves (rows +0..3 and +4..7); the tile has
+// 256-byte rows swizzled by tile_swizzle.
+__device__ inline void tr_offsets(int lane, int c0, int (&off)[2]) {
+  const int g = lane >> 4, s = lane & 15;
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb) {
+    const int r = 8 * (g >> 1) + 4 * tb + (s >> 2);
+    const int gran = c0 / 8 + 2 * (g & 1) + ((s & 3) >> 1);
+    off[tb] = r * 256 + 16 * (gran ^ tile_swizzle(r)) + 8 * (s & 1);
+  }
+}
+__device__ inline bf16x8 tr_read8(const char* base, const int (&off)[2]) {
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + off[0]));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + off[1]));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
 
 // Plan records are read through the constant address space so that the
 // uniform loads become scalar loads (counted by lgkmcnt, not by the vmcnt
@@ -134,12 +165,11 @@ template <int G>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void dq_kernel(const BwdArgs a) {
   constexpr int D = 128, BN = 64, NQ = 8, ND = 4, RB = 4 / G;
-  constexpr int TILE = BN * D * 2;     // bytes of a K, V or K^T tile
+  constexpr int TILE = BN * D * 2;     // bytes of a K or V tile
   constexpr int CH = TILE / 1024 / 4;  // LDS-DMA instructions per wave per tensor
-  constexpr int PER_STAGE = 3 * CH;    // LDS-DMA instructions per wave per tile
+  constexpr int PER_STAGE = 2 * CH;    // LDS-DMA instructions per wave per tile
   __shared__ __attribute__((aligned(1024))) char k0s[TILE], k1s[TILE], k2s[TILE];
   __shared__ __attribute__((aligned(1024))) char v0s[TILE], v1s[TILE], v2s[TILE];
-  __shared__ __attribute__((aligned(1024))) char t0s[TILE], t1s[TILE], t2s[TILE];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -202,46 +232,38 @@ void dq_kernel(const BwdArgs a) {
   const float dl = row_ok ? a.delta[int64_t(h) * a.R + lrow] : 0.f;
   const float c2 = a.scale_log2;
 
-  // LDS-DMA offsets (as in the forward: K rows swizzled g ^ (r & 15), K^T
-  // rows g ^ ((d >> 1) & 7)); every wave loads a quarter of each tile.
+  // LDS-DMA offsets: K and V rows are 256-byte tile rows swizzled by
+  // tile_swizzle; every wave loads a quarter of each tile.
   const int tok_bytes = a.Hkv * D * 2;
   const char* kbase = static_cast<const char*>(a.k) + int64_t(kvh) * D * 2;
   const char* vbase = static_cast<const char*>(a.v) + int64_t(kvh) * D * 2;
-  const char* tbase = static_cast<const char*>(a.kt) + int64_t(kvh) * a.tpad * D * 2;
-  int kgo[CH], tgo[CH];
+  int kgo[CH];
 #pragma unroll
   for (int i = 0; i < CH; ++i) {
     const int c = wave * CH + i;
     const int krow = 4 * c + (lane >> 4), kp = lane & 15;
-    kgo[i] = krow * tok_bytes + 16 * (kp ^ (krow & 15));
-    const int d = 8 * c + (lane >> 3), vp = lane & 7;
-    tgo[i] = (vp ^ ((d >> 1) & 7)) * (D * 16) + d * 16;
+    kgo[i] = krow * tok_bytes + 16 * (kp ^ tile_swizzle(krow));
   }
-  auto issue = [&](const Cursor& c, char* kd, char* vd, char* td) {
+  auto issue = [&](const Cursor& c, char* kd, char* vd) {
     const int kt = __builtin_amdgcn_readfirstlane(c.kt);
     const int valid = __builtin_amdgcn_readfirstlane(max(min(c.k1 - kt, BN), 0) * tok_bytes);
     const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase + int64_t(kt) * tok_bytes, valid);
     const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase + int64_t(kt) * tok_bytes, valid);
-    const int tvalid = __builtin_amdgcn_readfirstlane(max(a.tpad - kt, 0) * D * 2);
-    const __amdgpu_buffer_rsrc_t tr = make_rsrc(tbase + int64_t(kt) * D * 2, tvalid);
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(kd + (wave * CH + i) * 1024), 16, kgo[i], 0, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(vd + (wave * CH + i) * 1024), 16, kgo[i], 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(tr, (lds_void*)(td + (wave * CH + i) * 1024), 16, tgo[i], 0, 0, 0);
     }
   };
 
   const int srow = (ql & ~12) | ((ql & 4) << 1) | ((ql & 8) >> 1);
   int kro[NQ];
 #pragma unroll
-  for (int jj = 0; jj < NQ; ++jj) kro[jj] = srow * 256 + 16 * ((2 * jj + hh) ^ (srow & 15));
-  const int vx = (ql >> 1) & 7;
-  int tro[2][2];
+  for (int jj = 0; jj < NQ; ++jj) kro[jj] = srow * 256 + 16 * ((2 * jj + hh) ^ tile_swizzle(srow));
+  // K^T operands of dQ^T += K^T dS^T: transposing reads of the K tile
+  int ktr[ND][2];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub) tro[kb][sub] = ql * 128 + 16 * ((4 * kb + 2 * sub + hh) ^ vx);
+  for (int db = 0; db < ND; ++db) tr_offsets(lane, 32 * db, ktr[db]);
 
   f32x16 acc[ND];  // dQ^T: d = 32 db + 8 (t/4) + 4 hh + t%4 ... (rows in lanes)
 #pragma unroll
@@ -249,7 +271,7 @@ void dq_kernel(const BwdArgs a) {
 #pragma unroll
     for (int t = 0; t < 16; ++t) acc[db][t] = 0.f;
 
-  auto tile_step = [&](const Cursor& c, const char* ks, const char* vs, const char* ts) {
+  auto tile_step = [&](const Cursor& c, const char* ks, const char* vs) {
     f32x16 s[2], dp[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -293,7 +315,7 @@ void dq_kernel(const BwdArgs a) {
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub) {
-          const bf16x8 tf = *reinterpret_cast<const bf16x8*>(ts + db * 32 * 128 + tro[kb][sub]);
+          const bf16x8 tf = tr_read8(ks + (32 * kb + 16 * sub) * 256, ktr[db]);
           acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tf, dsb[kb][sub], acc[db], 0, 0, 0);
         }
   };
@@ -304,12 +326,12 @@ void dq_kernel(const BwdArgs a) {
   Cursor cs, cl;
   start(cs);
   start(cl);
-  issue(cl, k0s, v0s, t0s);
+  issue(cl, k0s, v0s);
   if (n_tiles > 1) {
     advance(cl);
-    issue(cl, k1s, v1s, t1s);
+    issue(cl, k1s, v1s);
   }
-#define DQ_STEP(T, KC, VC, TC, KN, VN, TN)                   \
+#define DQ_STEP(T, KC, VC, KN, VN)                           \
   {                                                          \
     if ((T) + 1 < n_tiles)                                   \
       __builtin_amdgcn_s_waitcnt(wait_vmcnt(PER_STAGE));     \
@@ -318,15 +340,15 @@ void dq_kernel(const BwdArgs a) {
     asm volatile("s_barrier" ::: "memory");                  \
     if ((T) + 2 < n_tiles) {                                 \
       advance(cl);                                           \
-      issue(cl, KN, VN, TN);                                 \
+      issue(cl, KN, VN);                                     \
     }                                                        \
-    tile_step(cs, KC, VC, TC);                               \
+    tile_step(cs, KC, VC);                                   \
     advance(cs);                                             \
   }
   for (int t = 0; t < n_tiles; t += 3) {
-    DQ_STEP(t, k0s, v0s, t0s, k2s, v2s, t2s);
-    if (t + 1 < n_tiles) DQ_STEP(t + 1, k1s, v1s, t1s, k0s, v0s, t0s);
-    if (t + 2 < n_tiles) DQ_STEP(t + 2, k2s, v2s, t2s, k1s, v1s, t1s);
+    DQ_STEP(t, k0s, v0s, k2s, v2s);
+    if (t + 1 < n_tiles) DQ_STEP(t + 1, k1s, v1s, k0s, v0s);
+    if (t + 2 < n_tiles) DQ_STEP(t + 2, k2s, v2s, k1s, v1s);
   }
 #undef DQ_STEP
 
@@ -348,12 +370,12 @@ void dkdv_kernel(const BwdArgs a) {
   constexpr int ROWT = RBK * D * 2;    // bytes of a 32-row Q, dO, Q^T or dO^T tile
   constexpr int CH = ROWT / 1024 / 4;  // 16-byte LDS-DMA instructions per wave per tile (2)
   static_assert(kBwdKeyTile == 128 && RBK == 32, "4 waves of 32 keys, 32-row blocks");
-  // One ring slot: Q | dO | Q^T | dO^T | row records (every wave loads 256 B
-  // of records; 512 B are the record, the rest reads as zeros).
-  constexpr int OQ = 0, OD = ROWT, OQT = 2 * ROWT, ODT = 3 * ROWT, OREC = 4 * ROWT;
-  constexpr int STAGE = 4 * ROWT + 1024;
+  // One ring slot: Q | dO | row records (every wave loads 256 B of records;
+  // 512 B are the record, the rest reads as zeros).
+  constexpr int OQ = 0, OD = ROWT, OREC = 2 * ROWT;
+  constexpr int STAGE = 2 * ROWT + 1024;
   constexpr int REC_BYTES = 4 * RBK * 4;
-  constexpr int PER_STAGE = 4 * CH + 1;  // LDS-DMA instructions per wave per slot
+  constexpr int PER_STAGE = 2 * CH + 1;  // LDS-DMA instructions per wave per slot
   __shared__ __attribute__((aligned(1024))) char st0[STAGE], st1[STAGE], st2[STAGE], st3[STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -382,20 +404,16 @@ void dkdv_kernel(const BwdArgs a) {
     }
   }
 
-  // LDS-DMA offsets. Q and dO row tiles (32 rows x 256 B, granule
-  // g ^ (row & 15)): instruction i of this wave fills rows 4c..4c+3,
-  // c = 2 wave + i. Q^T and dO^T tiles (128 d-rows x 64 B of 32 rows,
-  // granule g ^ ((d >> 2) & 3)): instruction i fills d-rows 16c..16c+15; the
-  // blocked source holds 8 rows x 128 d per 2 KiB.
+  // LDS-DMA offsets. Q and dO row tiles are 32 rows x 256 B, swizzled by
+  // tile_swizzle: instruction i of this wave fills rows 4c..4c+3,
+  // c = 2 wave + i.
   const int row_bytes = a.H * D * 2;
-  int ngo[CH], tgo[CH];
+  int ngo[CH];
 #pragma unroll
   for (int i = 0; i < CH; ++i) {
     const int c = wave * CH + i;
     const int r = 4 * c + (lane >> 4), p = lane & 15;
-    ngo[i] = r * row_bytes + 16 * (p ^ (r & 15));
-    const int d = 16 * c + (lane >> 2), s = lane & 3;
-    tgo[i] = (s ^ ((d >> 2) & 3)) * (D * 16) + d * 16;
+    ngo[i] = r * row_bytes + 16 * (p ^ tile_swizzle(r));
   }
   // the (row block, head) steps: rb in [rb0, rb1) outer, the query heads of
   // KV head g (a.group of them) inner
@@ -408,17 +426,12 @@ void dkdv_kernel(const BwdArgs a) {
     const int64_t noff = (int64_t(r0) * a.H + h) * D * 2;
     const __amdgpu_buffer_rsrc_t qr = make_rsrc(static_cast<const char*>(a.qr) + noff, valid);
     const __amdgpu_buffer_rsrc_t dr = make_rsrc(static_cast<const char*>(a.dout) + noff, valid);
-    const int64_t toff = (int64_t(h) * a.rpad + r0) * D * 2;
-    const __amdgpu_buffer_rsrc_t qtr = make_rsrc(static_cast<const char*>(a.qt) + toff, ROWT);
-    const __amdgpu_buffer_rsrc_t dtr = make_rsrc(static_cast<const char*>(a.dot) + toff, ROWT);
     const __amdgpu_buffer_rsrc_t rr = make_rsrc(a.rec + (int64_t(h) * a.nrb + rb) * (4 * RBK), REC_BYTES);
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       const int slot = (wave * CH + i) * 1024;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(qr, (lds_void*)(st + OQ + slot), 16, ngo[i], 0, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(dr, (lds_void*)(st + OD + slot), 16, ngo[i], 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(qtr, (lds_void*)(st + OQT + slot), 16, tgo[i], 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(dtr, (lds_void*)(st + ODT + slot), 16, tgo[i], 0, 0, 0);
     }
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (lds_void*)(st + OREC + wave * 256), 4, wave * 256 + 4 * lane,
                                              0, 0, 0);
@@ -427,16 +440,12 @@ void dkdv_kernel(const BwdArgs a) {
   const int srow = (kl & ~12) | ((kl & 4) << 1) | ((kl & 8) >> 1);
   int nro[NQ];
 #pragma unroll
-  for (int jj = 0; jj < NQ; ++jj) nro[jj] = srow * 256 + 16 * ((2 * jj + hh) ^ (srow & 15));
-  // B operands of dV and dK: lane reads d-row 32 db + kl, rows 16 kk + 8 hh + 0..7
-  int tro[ND][2];
+  for (int jj = 0; jj < NQ; ++jj) nro[jj] = srow * 256 + 16 * ((2 * jj + hh) ^ tile_swizzle(srow));
+  // B operands of dV and dK (rows 16 kk + 8 hh + 0..7 at d = 32 db + kl):
+  // transposing reads of the dO and Q tiles
+  int ttr[ND][2];
 #pragma unroll
-  for (int db = 0; db < ND; ++db)
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const int d = 32 * db + kl;
-      tro[db][kk] = d * 64 + 16 * ((2 * kk + hh) ^ ((d >> 2) & 3));
-    }
+  for (int db = 0; db < ND; ++db) tr_offsets(lane, 32 * db, ttr[db]);
 
   f32x16 dk[ND], dv[ND];
 #pragma unroll
@@ -516,8 +525,8 @@ void dkdv_kernel(const BwdArgs a) {
     for (int db = 0; db < ND; ++db)
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        const bf16x8 dob = *reinterpret_cast<const bf16x8*>(st + ODT + tro[db][kk]);
-        const bf16x8 qb = *reinterpret_cast<const bf16x8*>(st + OQT + tro[db][kk]);
+        const bf16x8 dob = tr_read8(st + OD + 16 * kk * 256, ttr[db]);
+        const bf16x8 qb = tr_read8(st + OQ + 16 * kk * 256, ttr[db]);
         dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[kk], dob, dv[db], 0, 0, 0);
         dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dsa[kk], qb, dk[db], 0, 0, 0);
       }
@@ -534,7 +543,7 @@ void dkdv_kernel(const BwdArgs a) {
   // nothing.
   {
     const uint4 z = make_uint4(0, 0, 0, 0);
-    uint4* const z3 = reinterpret_cast<uint4*>(st3 + OQT);
+    uint4* const z3 = reinterpret_cast<uint4*>(st3 + OQ);
 #pragma unroll
     for (int i = 0; i < 2 * ROWT / 16 / 256; ++i) z3[i * 256 + tid] = z;
   }

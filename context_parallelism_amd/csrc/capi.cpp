@@ -184,10 +184,7 @@ cp_status rank_bwd(const void* q, const void* k, const void* v, const void* out,
     a.qr = ws + w.off_qr;
     a.k = k;
     a.v = v;
-    a.kt = ws + w.off_kt;
     a.dout = dout;
-    a.qt = ws + w.off_qt;
-    a.dot = ws + w.off_dot;
     a.lse = lse;
     a.delta = reinterpret_cast<const float*>(ws + w.off_delta);
     a.index = reinterpret_cast<const int32_t*>(ws + w.off_index);
@@ -206,8 +203,6 @@ cp_status rank_bwd(const void* q, const void* k, const void* v, const void* out,
     a.Hkv = kv_heads;
     a.n_hg = w.n_hg;
     a.group = heads / kv_heads;
-    a.tpad = w.tpad;
-    a.rpad = w.rpad;
     a.nrb = w.nrb;
     a.scale = float(1.0 / std::sqrt(double(head_dim)));
     a.scale_log2 = float(1.4426950408889634 / std::sqrt(double(head_dim)));
@@ -217,12 +212,6 @@ cp_status rank_bwd(const void* q, const void* k, const void* v, const void* out,
       if (launch_bwd_prep(out, dout, lse, a.index, reinterpret_cast<const int32_t*>(ws + w.off_row_lo),
                           reinterpret_cast<float*>(ws + w.off_delta), reinterpret_cast<int32_t*>(ws + w.off_rec),
                           int32_t(R), heads, w.nrb, s) != hipSuccess)
-        return CP_EHIP;
-      if (launch_transpose_v(ws + w.off_qr, ws + w.off_qt, int32_t(R), heads, w.rpad, s) != hipSuccess)
-        return CP_EHIP;
-      if (launch_transpose_v(dout, ws + w.off_dot, int32_t(R), heads, w.rpad, s) != hipSuccess)
-        return CP_EHIP;
-      if (launch_transpose_v(k, ws + w.off_kt, int32_t(seq_len), kv_heads, w.tpad, s) != hipSuccess)
         return CP_EHIP;
       if (w.plan.rows.pad_rows > 0 &&
           launch_fill_pad_rows(a.index, R, heads, head_dim, CP_DTYPE_F32, dq, nullptr, s) != hipSuccess)

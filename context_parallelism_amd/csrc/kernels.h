@@ -14,8 +14,6 @@ struct AttnArgs {
                          // rows are read in place (the rank's gather fused into the Q load)
   const void* k;         // [T, Hkv, D]
   const void* v;         // [T, Hkv, D]
-  const void* vt;        // V^T [Hkv, D, tpad] (bf16, head_dim 128 only), zero past T
-  int32_t tpad;          // keys per V^T row
   float* part_o;         // [P, R, H, D] fp32, normalised per step
   float* part_lse;       // [P, H, R] fp32, natural log
   const TileRec* tiles;
@@ -39,10 +37,7 @@ struct BwdArgs {
   const void* qr;      // gathered rank-local Q [R, H, 128]
   const void* k;       // [T, Hkv, 128]
   const void* v;       // [T, Hkv, 128]
-  const void* kt;      // K^T blocked by 8 keys [Hkv][tpad/8][128][8]
   const void* dout;    // [R, H, 128]
-  const void* qt;      // Q^T of the rank rows, blocked by 8 rows [H][rpad/8][128][8]
-  const void* dot;     // dout^T, same layout
   const float* lse;    // forward lse [H, R]
   const float* delta;  // rowsum(dout * out) [H, R]
   const int32_t* index;  // global id per rank row, -1 for pads
@@ -57,7 +52,7 @@ struct BwdArgs {
   const EntryRec* tile_entries;
   const UnitRec* units;
   const KeyTileRec* ktiles;
-  int32_t R, H, Hkv, n_hg, group, tpad, rpad, nrb;
+  int32_t R, H, Hkv, n_hg, group, nrb;
   float scale, scale_log2;
 };
 
@@ -72,11 +67,6 @@ hipError_t launch_bwd(const BwdArgs& a, int heads_per_wg, int n_units, int n_kti
 
 hipError_t launch_gather(const void* src, const int32_t* index, void* dst, int64_t n_rows,
                          int64_t row_bytes, hipStream_t stream);
-
-// V [T, Hkv, 128] bf16 -> V^T [Hkv, 128, tpad], zeros for keys >= T.
-// tpad: multiple of 64, >= T + 63 (every 64-key window starting below T).
-hipError_t launch_transpose_v(const void* v, void* vt, int32_t T, int32_t Hkv, int32_t tpad,
-                              hipStream_t stream);
 
 hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, int heads_per_wg, int n_entries,
                             hipStream_t stream);

@@ -19,7 +19,6 @@ int64_t unit_min_workgroups() {
   return (end != env && v >= 0) ? int64_t(v) : kUnitMinWorkgroups;
 }
 
-int32_t vt_row_keys(int64_t seq_len) { return int32_t((seq_len + 63 + 63) / 64 * 64); }
 
 int32_t prepare_workspace(int64_t seq_len, const int32_t* n_img, const int32_t* cu_seqlens,
                           int32_t n_samples, int32_t cp_size, int32_t cp_rank, int32_t heads,
@@ -128,16 +127,8 @@ int32_t prepare_bwd_workspace(int64_t seq_len, const int32_t* n_img, const int32
   off = align256(off + w.plan.blk.size() * sizeof(int32_t));
   w.plan_bytes = off;
   w.nrb = int32_t((R + kBwdRowBlock - 1) / kBwdRowBlock);
-  w.rpad = int32_t((R + 63) / 64 * 64);
-  w.tpad = vt_row_keys(seq_len);
   w.off_qr = off;
   off = align256(off + R * size_t(heads) * head_dim * 2);
-  w.off_qt = off;
-  off = align256(off + size_t(heads) * w.rpad * head_dim * 2);
-  w.off_dot = off;
-  off = align256(off + size_t(heads) * w.rpad * head_dim * 2);
-  w.off_kt = off;
-  off = align256(off + size_t(kv_heads) * w.tpad * head_dim * 2);
   w.off_delta = off;
   off = align256(off + size_t(heads) * R * sizeof(float));
   w.off_rec = off;

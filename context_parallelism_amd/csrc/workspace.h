@@ -50,9 +50,6 @@ int32_t prepare_workspace(int64_t seq_len, const int32_t* n_img, const int32_t* 
 //           dK/dV key tiles, sample start per row int32[R], per 32-row
 //           block bounds int32[nrb][2] (uploaded from the host in one copy);
 //   qr    : gathered rank-local Q rows [R, H, 128] bf16;
-//   qt    : Q^T of those rows, blocked by 8 rows: [H][rpad/8][128][8];
-//   dot   : dout^T, same layout;
-//   kt    : K^T blocked by 8 keys: [Hkv][tpad/8][128][8];
 //   delta : rowsum(dout * out) fp32 [H, R];
 //   rec   : dK/dV row records [H][nrb][4][32] (nrb = ceil(R / 32)): per row
 //           lse * log2(e), delta, sample start, global id - sample start.
@@ -63,8 +60,8 @@ struct BwdWorkspace {
   int32_t heads_per_wg = 1, rows_per_tile = 0, n_hg = 0;
   size_t off_index = 0, off_tiles = 0, off_spans = 0, off_tile_entries = 0, off_units = 0,
          off_ktiles = 0, off_row_lo = 0, off_blk = 0, plan_bytes = 0;
-  size_t off_qr = 0, off_qt = 0, off_dot = 0, off_kt = 0, off_delta = 0, off_rec = 0, total = 0;
-  int32_t rpad = 0, tpad = 0, nrb = 0;
+  size_t off_qr = 0, off_delta = 0, off_rec = 0, total = 0;
+  int32_t nrb = 0;
 };
 
 int32_t prepare_bwd_workspace(int64_t seq_len, const int32_t* n_img, const int32_t* cu_seqlens,
@@ -72,10 +69,6 @@ int32_t prepare_bwd_workspace(int64_t seq_len, const int32_t* n_img, const int32
                               int32_t heads, int32_t kv_heads, int32_t head_dim, int32_t dtype,
                               BwdWorkspace& w);
 void pack_bwd_plan(const BwdWorkspace& w, uint8_t* dst);
-
-// Keys per V^T row: a multiple of 64 that covers every 64-key window
-// starting below seq_len.
-int32_t vt_row_keys(int64_t seq_len);
 
 // Writes the plan region (w.plan_bytes bytes) into dst.
 void pack_plan(const Workspace& w, uint8_t* dst);
