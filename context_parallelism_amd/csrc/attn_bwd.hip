@@ -15,24 +15,28 @@
 //  * prep: Delta[h][r] = sum_d dO[r][h][d] * O[r][h][d], and per 32-row block
 //    and head a record of lse * log2(e), Delta and each row's visible key
 //    range that the dK/dV kernel stages through LDS with its operands;
-//  * dQ: one workgroup of 4 waves per (row tile, head group); each wave owns
-//    32 rows of one head and walks the tile's key spans over all ring steps,
+//  * dQ: one workgroup of 4 waves per (row tile, head group), two
+//    workgroups per compute unit; each wave owns 32 rows of one head and
+//    walks the tile's key spans over all ring steps, 32 keys at a time,
 //    recomputing S^T = K Q^T and dP^T = V dO^T (K and V rows from LDS, Q and
 //    dO in registers) and accumulating dQ^T += K^T dS^T, the K^T operand
 //    read from the same row-major K tile with transposing LDS reads; K and V
-//    tiles stream through a three-slot LDS ring, two tiles ahead;
-//  * dK/dV: one workgroup of 4 waves per (128-key tile, KV head); each wave
-//    owns 32 keys, keeps its K and V rows in registers, and walks the
-//    rank's 32-row blocks that see the tile, for every query head of the KV
-//    head: S = Q K^T and dP = dO V^T (Q, dO rows from LDS), then
-//    dV += P^T dO and dK += dS^T Q, the dO and Q operands read from the
-//    same row-major tiles with transposing LDS reads. The accumulator layout
-//    of S (keys in lanes, rows in registers) is directly the A operand of
-//    those products once the rows are read in the order sigma (bits 2 and 3
-//    of the row swapped). The
-//    row blocks stream through a four-slot LDS ring, two blocks ahead, so
-//    no wave waits on memory inside a step, and each wave overlaps a
-//    step's softmax with the previous step's dV/dK products.
+//    tiles stream through a three-slot LDS ring (48 KiB), two tiles ahead;
+//  * dK/dV: one workgroup of 8 waves per (128-key tile, KV head); waves w
+//    and w + 4 share a SIMD and 32 keys, and walk the rank's 32-row blocks
+//    that see the tile, for every query head of the KV head. Wave w keeps
+//    the keys' K rows in registers and computes S = Q K^T, P and
+//    dV += P^T dO; wave w + 4 keeps V, computes dP = dO V^T, takes P
+//    through LDS, and computes dS = P (dP - Delta) and dK += dS^T Q, one
+//    step behind. The two waves of a SIMD alternate matrix and vector
+//    phases (ping-pong, two barriers per step). The dO and Q operands of
+//    the products are read from the
+//    same row-major tiles with transposing LDS reads. The accumulator
+//    layout of S (keys in lanes, rows in registers) is directly the A
+//    operand of those products once the rows are read in the order sigma
+//    (bits 2 and 3 of the row swapped). The row blocks stream through a
+//    four-slot LDS ring, two blocks ahead, so no wave waits on memory
+//    inside a step.
 #include "kernels.h"
 
 namespace cpattn {
@@ -162,9 +166,9 @@ struct Cursor {
 
 // ---------------------------------------------------------------- dQ
 template <int G>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void dq_kernel(const BwdArgs a) {
-  constexpr int D = 128, BN = 64, NQ = 8, ND = 4, RB = 4 / G;
+  constexpr int D = 128, BN = 32, KB = BN / 32, NQ = 8, ND = 4, RB = 4 / G;
   constexpr int TILE = BN * D * 2;     // bytes of a K or V tile
   constexpr int CH = TILE / 1024 / 4;  // LDS-DMA instructions per wave per tensor
   constexpr int PER_STAGE = 2 * CH;    // LDS-DMA instructions per wave per tile
@@ -272,9 +276,9 @@ void dq_kernel(const BwdArgs a) {
     for (int t = 0; t < 16; ++t) acc[db][t] = 0.f;
 
   auto tile_step = [&](const Cursor& c, const char* ks, const char* vs) {
-    f32x16 s[2], dp[2];
+    f32x16 s[KB], dp[KB];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
       for (int t = 0; t < 16; ++t) {
         s[kb][t] = 0.f;
@@ -297,9 +301,9 @@ void dq_kernel(const BwdArgs a) {
     const uint64_t below_lo = lo >= 64 ? ~0ull : (1ull << lo) - 1;
     const uint64_t vis = edge ? (below_hi & ~below_lo) : ~0ull;
     const int w0 = int(uint32_t(vis)), w1 = int(uint32_t(vis >> 32));
-    bf16x8 dsb[2][2];
+    bf16x8 dsb[KB][2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int m = __builtin_amdgcn_sbfe(kb ? w1 : w0, 16 * (r >> 3) + (r & 7), 1);
@@ -312,7 +316,7 @@ void dq_kernel(const BwdArgs a) {
 #pragma unroll
     for (int db = 0; db < ND; ++db)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub) {
           const bf16x8 tf = tr_read8(ks + (32 * kb + 16 * sub) * 256, ktr[db]);
@@ -364,56 +368,78 @@ void dq_kernel(const BwdArgs a) {
 }
 
 // ---------------------------------------------------------------- dK / dV
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+// s_waitcnt immediate for vmcnt(n) and lgkmcnt(0) together.
+constexpr int wait_vmcnt_lgkm0(int n) { return (wait_vmcnt(n) & ~0x0F00); }
+// __builtin_amdgcn_sched_group_barrier instruction classes
+constexpr int kSchedMfma = 0x0008;
+constexpr int kSchedDsRead = 0x0100;
+// A matrix phase of the dK/dV kernel: 8 product MFMAs (two transposing LDS
+// reads each), then 8 score MFMAs (one LDS read each); every MFMA's reads go
+// out kPhaseAhead MFMAs before it.
+constexpr int kPhaseAhead = 4;
+__device__ inline void schedule_matrix_phase() {
+  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * kPhaseAhead, 0);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    if (i + kPhaseAhead < 8)
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+    else if (i + kPhaseAhead < 16)
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+  }
+}
+
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void dkdv_kernel(const BwdArgs a) {
   constexpr int D = 128, NQ = 8, ND = 4, RBK = kBwdRowBlock;
-  constexpr int ROWT = RBK * D * 2;    // bytes of a 32-row Q, dO, Q^T or dO^T tile
-  constexpr int CH = ROWT / 1024 / 4;  // 16-byte LDS-DMA instructions per wave per tile (2)
-  static_assert(kBwdKeyTile == 128 && RBK == 32, "4 waves of 32 keys, 32-row blocks");
+  constexpr int ROWT = RBK * D * 2;    // bytes of a 32-row Q or dO tile
+  constexpr int CH = ROWT / 1024 / 8;  // 16-byte LDS-DMA instructions per wave per tile (1)
+  static_assert(kBwdKeyTile == 128 && RBK == 32 && CH == 1, "4 wave pairs of 32 keys, 32-row blocks");
   // One ring slot: Q | dO | row records (every wave loads 256 B of records;
-  // 512 B are the record, the rest reads as zeros).
+  // the first 512 B are the record, the rest reads as zeros).
   constexpr int OQ = 0, OD = ROWT, OREC = 2 * ROWT;
-  constexpr int STAGE = 2 * ROWT + 1024;
+  constexpr int STAGE = 2 * ROWT + 2048;
   constexpr int REC_BYTES = 4 * RBK * 4;
   constexpr int PER_STAGE = 2 * CH + 1;  // LDS-DMA instructions per wave per slot
+  // P of one step, from the P wave of each pair to its partner: bf16, in the
+  // register order of the P wave (two 16-byte pieces per lane)
+  constexpr int PBUF = 4 * 2 * 1024;
   __shared__ __attribute__((aligned(1024))) char st0[STAGE], st1[STAGE], st2[STAGE], st3[STAGE];
+  __shared__ __attribute__((aligned(1024))) char pb0[PBUF], pb1[PBUF];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int pair = wave & 3;           // waves w and w + 4 share a SIMD and 32 keys
+  const bool pwave = wave < 4;         // S, P, dV; its partner: dP, dS, dK
   const int g = blockIdx.x % a.Hkv;
   const KeyTileRec kt = scalar_load(a.ktiles, blockIdx.x / a.Hkv);
   const const_ptr<int32_t> blk = scalar_view(a.blk);
   const int kl = lane & 31, hh = lane >> 5;
-  const int kw0 = kt.k0 + 32 * wave;  // the wave's first key
+  const int kw0 = kt.k0 + 32 * pair;  // the pair's first key
   const int key = kw0 + kl;           // this lane's key (column of S)
 
-  // K and V rows of the wave's 32 keys as B operands: lane holds key kl,
-  // d = 16 jj + 8 hh + 0..7. Keys >= k1 read as zeros.
-  bf16x8 kf[NQ], vf[NQ];
+  // K (P wave) or V (partner) rows of the pair's 32 keys as B operands:
+  // lane holds key kl, d = 16 jj + 8 hh + 0..7. Keys >= k1 read as zeros.
+  bf16x8 kv[NQ];
   {
     const int tok_bytes = a.Hkv * D * 2;
     const int valid = __builtin_amdgcn_readfirstlane(max(min(kt.k1 - kw0, 32), 0) * tok_bytes);
     const int64_t base = (int64_t(kw0) * a.Hkv + g) * D * 2;
-    const __amdgpu_buffer_rsrc_t kr = make_rsrc(static_cast<const char*>(a.k) + base, valid);
-    const __amdgpu_buffer_rsrc_t vr = make_rsrc(static_cast<const char*>(a.v) + base, valid);
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(static_cast<const char*>(pwave ? a.k : a.v) + base, valid);
 #pragma unroll
     for (int jj = 0; jj < NQ; ++jj) {
       const int off = kl * tok_bytes + (16 * jj + 8 * hh) * 2;
-      kf[jj] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(kr, off, 0, 0));
-      vf[jj] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(vr, off, 0, 0));
+      kv[jj] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
     }
   }
 
   // LDS-DMA offsets. Q and dO row tiles are 32 rows x 256 B, swizzled by
-  // tile_swizzle: instruction i of this wave fills rows 4c..4c+3,
-  // c = 2 wave + i.
+  // tile_swizzle: wave w fills rows 4w..4w+3 of each.
   const int row_bytes = a.H * D * 2;
-  int ngo[CH];
-#pragma unroll
-  for (int i = 0; i < CH; ++i) {
-    const int c = wave * CH + i;
-    const int r = 4 * c + (lane >> 4), p = lane & 15;
-    ngo[i] = r * row_bytes + 16 * (p ^ tile_swizzle(r));
+  int ngo;
+  {
+    const int r = 4 * wave + (lane >> 4), p = lane & 15;
+    ngo = r * row_bytes + 16 * (p ^ tile_swizzle(r));
   }
   // the (row block, head) steps: rb in [rb0, rb1) outer, the query heads of
   // KV head g (a.group of them) inner
@@ -427,61 +453,57 @@ void dkdv_kernel(const BwdArgs a) {
     const __amdgpu_buffer_rsrc_t qr = make_rsrc(static_cast<const char*>(a.qr) + noff, valid);
     const __amdgpu_buffer_rsrc_t dr = make_rsrc(static_cast<const char*>(a.dout) + noff, valid);
     const __amdgpu_buffer_rsrc_t rr = make_rsrc(a.rec + (int64_t(h) * a.nrb + rb) * (4 * RBK), REC_BYTES);
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int slot = (wave * CH + i) * 1024;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(qr, (lds_void*)(st + OQ + slot), 16, ngo[i], 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(dr, (lds_void*)(st + OD + slot), 16, ngo[i], 0, 0, 0);
-    }
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(qr, (lds_void*)(st + OQ + wave * 1024), 16, ngo, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(dr, (lds_void*)(st + OD + wave * 1024), 16, ngo, 0, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (lds_void*)(st + OREC + wave * 256), 4, wave * 256 + 4 * lane,
                                              0, 0, 0);
   };
-  // A operands of S and dP: lane reads row sigma(kl) of the Q / dO tile
+  // A operands of S (Q) and dP (dO): lane reads row sigma(kl) of the tile
   const int srow = (kl & ~12) | ((kl & 4) << 1) | ((kl & 8) >> 1);
   int nro[NQ];
 #pragma unroll
   for (int jj = 0; jj < NQ; ++jj) nro[jj] = srow * 256 + 16 * ((2 * jj + hh) ^ tile_swizzle(srow));
-  // B operands of dV and dK (rows 16 kk + 8 hh + 0..7 at d = 32 db + kl):
-  // transposing reads of the dO and Q tiles
+  // B operands of dV (dO) and dK (Q) -- rows 16 kk + 8 hh + 0..7 at
+  // d = 32 db + kl -- by transposing reads of the same tiles
   int ttr[ND][2];
 #pragma unroll
   for (int db = 0; db < ND; ++db) tr_offsets(lane, 32 * db, ttr[db]);
 
-  f32x16 dk[ND], dv[ND];
+  f32x16 acc[ND];  // dV (P wave) or dK (partner): key 32 pair + (t/4)*8 + 4 hh + t%4, d = 32 db + kl
 #pragma unroll
   for (int db = 0; db < ND; ++db)
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      dk[db][t] = 0.f;
-      dv[db][t] = 0.f;
-    }
+    for (int t = 0; t < 16; ++t) acc[db][t] = 0.f;
   const float c2 = a.scale_log2;
 
-  // one (row block, query head) step. Register t of lane half hh holds row
-  // 32 rb + 16 (t / 8) + 8 hh + t % 8 of the block.
-  // A block step is split in three so that a wave overlaps one step's
-  // softmax arithmetic with the previous step's dV/dK products:
-  //   scores(j):   S = Q K^T and dP = dO V^T (rows of step j's slot);
-  //   softmax(j):  P and dS from S, dP and the slot's row records;
-  //   products:    dV += P^T dO and dK += dS^T Q (Q^T, dO^T of the step's slot).
-  // Register t of lane half hh holds row 32 rb + 16 (t / 8) + 8 hh + t % 8.
-  auto scores = [&](int j, const char* st, f32x16& s, f32x16& dp) {
+  // scores: S = Q K^T (P wave) or dP = dO V^T (partner) of a slot. Register
+  // t of lane half hh holds row 32 rb + 16 (t / 8) + 8 hh + t % 8.
+  auto scores = [&](const char* tile, f32x16& s) {
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      s[t] = 0.f;
-      dp[t] = 0.f;
-    }
+    for (int t = 0; t < 16; ++t) s[t] = 0.f;
 #pragma unroll
     for (int jj = 0; jj < NQ; ++jj) {
-      const bf16x8 qa = *reinterpret_cast<const bf16x8*>(st + OQ + nro[jj]);
-      const bf16x8 da = *reinterpret_cast<const bf16x8*>(st + OD + nro[jj]);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[jj], s, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vf[jj], dp, 0, 0, 0);
+      const bf16x8 x = *reinterpret_cast<const bf16x8*>(tile + nro[jj]);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, kv[jj], s, 0, 0, 0);
     }
-    // every row of the block sees every key of the wave unless the block
+  };
+  // the product acc += A^T B for A in the P wave's register order (pa) and
+  // B the tile read transposed (dO for dV, Q for dK)
+  auto product = [&](const bf16x8 (&pa)[2], const char* tile) {
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[kk], tr_read8(tile + 16 * kk * 256, ttr[db]), acc[db],
+                                                          0, 0, 0);
+  };
+  // P wave, step j in slot st: the mask on S, P = exp2(S c2 - lse log2 e)
+  // (0 for pad rows, whose record holds +inf), P to the partner
+  auto p_softmax = [&](int j, const char* st, f32x16& s, bf16x8 (&pa)[2], char* pbuf) {
+    const int* const rec = reinterpret_cast<const int*>(st + OREC);
+    // every row of the block sees every key of the pair unless the block
     // holds a causal edge or a sample boundary; then S = -inf where the key
     // is outside [sample start, row's global id]
-    const int* const rec = reinterpret_cast<const int*>(st + OREC);
     const int rb = kt.rb0 + j / group;
     if (!(blk[2 * rb] <= kw0 && kw0 + 31 <= blk[2 * rb + 1])) {
 #pragma unroll
@@ -499,116 +521,142 @@ void dkdv_kernel(const BwdArgs a) {
           }
         }
     }
+#pragma unroll
+    for (int run = 0; run < 2; ++run)
+#pragma unroll
+      for (int q4 = 0; q4 < 2; ++q4) {
+        const f32x4 l2 = *reinterpret_cast<const f32x4*>(rec + 16 * run + 8 * hh + 4 * q4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          pa[run][4 * q4 + e] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * run + 4 * q4 + e], c2, -l2[e]));
+      }
+    bf16x8* const pw = reinterpret_cast<bf16x8*>(pbuf + pair * 2048) + lane;
+    pw[0] = pa[0];
+    pw[64] = pa[1];
   };
-  // P = exp2(S c2 - lse log2 e) (0 for pad rows, whose record holds +inf),
-  // dS = P (dP - Delta), both as bf16 A operands
-  auto softmax = [&](const char* st, const f32x16& s, const f32x16& dp, bf16x8 (&pa)[2], bf16x8 (&dsa)[2]) {
+  // partner, the step in slot st: dS = P (dP - Delta) with P from its P wave
+  auto p_ds = [&](const char* st, const char* pbuf, const f32x16& dp, bf16x8 (&dsa)[2]) {
+    const bf16x8* const pr = reinterpret_cast<const bf16x8*>(pbuf + pair * 2048) + lane;
+    const bf16x8 pa[2] = {pr[0], pr[64]};
     const int* const rec = reinterpret_cast<const int*>(st + OREC);
 #pragma unroll
     for (int run = 0; run < 2; ++run)
 #pragma unroll
       for (int q4 = 0; q4 < 2; ++q4) {
-        const int row = 16 * run + 8 * hh + 4 * q4;
-        const f32x4 l2 = *reinterpret_cast<const f32x4*>(rec + row);
-        const f32x4 dl = *reinterpret_cast<const f32x4*>(rec + RBK + row);
+        const f32x4 dl = *reinterpret_cast<const f32x4*>(rec + RBK + 16 * run + 8 * hh + 4 * q4);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int t = 8 * run + 4 * q4 + e;
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t], c2, -l2[e]));
-          pa[run][4 * q4 + e] = (__bf16)p;
-          dsa[run][4 * q4 + e] = (__bf16)(p * (dp[t] - dl[e]));
+          const int i = 4 * q4 + e;
+          dsa[run][i] = (__bf16)(float(pa[run][i]) * (dp[8 * run + i] - dl[e]));
         }
       }
   };
-  auto products = [&](const bf16x8 (&pa)[2], const bf16x8 (&dsa)[2], const char* st) {
-#pragma unroll
-    for (int db = 0; db < ND; ++db)
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const bf16x8 dob = tr_read8(st + OD + 16 * kk * 256, ttr[db]);
-        const bf16x8 qb = tr_read8(st + OQ + 16 * kk * 256, ttr[db]);
-        dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[kk], dob, dv[db], 0, 0, 0);
-        dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dsa[kk], qb, dk[db], 0, 0, 0);
-      }
-  };
 
-  // Ring of four LDS slots: block step j sits in slot j % 4. In iteration j
-  // a wave computes scores(j), then products(j - 1) interleaved with
-  // softmax(j); steps j + 1 and j + 2 are in flight meanwhile. Step j + 2 is
-  // issued into the slot of step j - 2, which every wave finished in
-  // iteration j - 1, before this iteration's barrier. Every iteration issues
-  // one stage (past the end, the last step again, into a free slot), so the
-  // count of loads in flight after step j's is always one stage. The slot of
-  // step -1 (st3) holds zeros so that the first iteration's products add
-  // nothing.
-  {
-    const uint4 z = make_uint4(0, 0, 0, 0);
-    uint4* const z3 = reinterpret_cast<uint4*>(st3 + OQ);
-#pragma unroll
-    for (int i = 0; i < 2 * ROWT / 16 / 256; ++i) z3[i * 256 + tid] = z;
-  }
-  bf16x8 pa[2], dsa[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      pa[i][e] = (__bf16)0.f;
-      dsa[i][e] = (__bf16)0.f;
-    }
+  // Ring of four LDS slots: block step j sits in slot j % 4; steps j + 1
+  // and j + 2 are in flight while step j is consumed. Iteration j has two
+  // phases, each ending at a workgroup barrier, and in each phase one wave
+  // of a pair works on the matrix cores while its partner does vector work:
+  //   phase A: P wave   dV += P(j-1)^T dO(j-1), then S(j) = Q(j) K^T  (MFMA)
+  //            partner  dS(j-1) = P(j-1) (dP(j-1) - Delta)           (VALU)
+  //   phase B: P wave   mask, P(j) = exp2(...), P(j) to LDS          (VALU)
+  //            partner  dK += dS(j-1)^T Q(j-1), then dP(j) = dO(j) V^T (MFMA)
+  // Step j + 2 is issued at the start of iteration j into the slot of step
+  // j - 2, which both waves finished in iteration j - 1. Every iteration
+  // issues one stage (past the end, the last step again, into a free slot),
+  // so the count of loads in flight after step j's is always one stage.
   const int last = n_blocks - 1;
   if (n_blocks > 0) {
     issue(0, st0);
     issue(min(1, last), st1);
   }
-#define DKDV_STEP(J, CUR, PREV, NXT)                            \
+  // The slot of step -1 (st3) and the P buffer of parity -1 (pb1) hold
+  // zeros, so the first iteration's products of step -1 add nothing and the
+  // phases need no branch on the step.
+  {
+    const uint4 z = make_uint4(0, 0, 0, 0);
+    uint4* const z3 = reinterpret_cast<uint4*>(st3);
+#pragma unroll
+    for (int i = 0; i < STAGE / 16 / 512; ++i) z3[i * 512 + tid] = z;
+    if (tid < (STAGE / 16) % 512) z3[(STAGE / 16 / 512) * 512 + tid] = z;
+    uint4* const zp = reinterpret_cast<uint4*>(pb1);
+#pragma unroll
+    for (int i = 0; i < PBUF / 16 / 512; ++i) zp[i * 512 + tid] = z;
+  }
+  f32x16 sdp;        // S(j) (P wave) or dP(j) (partner)
+  bf16x8 pd[2];      // P(j) (P wave) or dS(j - 1) (partner)
+#pragma unroll
+  for (int t = 0; t < 16; ++t) sdp[t] = 0.f;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pd[i][e] = (__bf16)0.f;
+#define DKDV_STEP(J, CUR, PREV, NXT, PC, PP)                    \
   {                                                             \
-    __builtin_amdgcn_s_waitcnt(wait_vmcnt(PER_STAGE));          \
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt_lgkm0(PER_STAGE));    \
     asm volatile("s_barrier" ::: "memory");                     \
     issue(min((J) + 2, last), NXT);                             \
-    f32x16 s, dp;                                               \
-    scores((J), CUR, s, dp);                                    \
-    products(pa, dsa, PREV);                                    \
-    softmax(CUR, s, dp, pa, dsa);                               \
+    if (pwave) {                                                \
+      __builtin_amdgcn_s_setprio(1);                            \
+      product(pd, PREV + OD);                                   \
+      scores(CUR + OQ, sdp);                                    \
+      schedule_matrix_phase();                                  \
+      __builtin_amdgcn_s_setprio(0);                            \
+    } else {                                                    \
+      p_ds(PREV, PP, sdp, pd);                                  \
+    }                                                           \
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt_lgkm0(63));           \
+    asm volatile("s_barrier" ::: "memory");                     \
+    if (pwave) {                                                \
+      p_softmax((J), CUR, sdp, pd, PC);                         \
+    } else {                                                    \
+      __builtin_amdgcn_s_setprio(1);                            \
+      product(pd, PREV + OQ);                                   \
+      scores(CUR + OD, sdp);                                    \
+      schedule_matrix_phase();                                  \
+      __builtin_amdgcn_s_setprio(0);                            \
+    }                                                           \
   }
+  // (guarded steps rather than early exits: one loop exit keeps the
+  // accumulators in place instead of copying them at every exit)
   int i = 0;
   for (; i + 4 <= n_blocks; i += 4) {
-    DKDV_STEP(i, st0, st3, st2);
-    DKDV_STEP(i + 1, st1, st0, st3);
-    DKDV_STEP(i + 2, st2, st1, st0);
-    DKDV_STEP(i + 3, st3, st2, st1);
+    DKDV_STEP(i, st0, st3, st2, pb0, pb1);
+    DKDV_STEP(i + 1, st1, st0, st3, pb1, pb0);
+    DKDV_STEP(i + 2, st2, st1, st0, pb0, pb1);
+    DKDV_STEP(i + 3, st3, st2, st1, pb1, pb0);
   }
-  if (i < n_blocks) DKDV_STEP(i, st0, st3, st2);
-  if (i + 1 < n_blocks) DKDV_STEP(i + 1, st1, st0, st3);
-  if (i + 2 < n_blocks) DKDV_STEP(i + 2, st2, st1, st0);
+  if (i < n_blocks) DKDV_STEP(i, st0, st3, st2, pb0, pb1);
+  if (i + 1 < n_blocks) DKDV_STEP(i + 1, st1, st0, st3, pb1, pb0);
+  if (i + 2 < n_blocks) DKDV_STEP(i + 2, st2, st1, st0, pb0, pb1);
 #undef DKDV_STEP
-  // the last step's products (its slot is (n_blocks - 1) % 4); the stages
-  // issued past the end land before the kernel exits
+  // the last step's remaining work: dV (P wave) and dS then dK (partner) of
+  // step n_blocks - 1 (slot (n_blocks - 1) % 4, P buffer of its parity); the
+  // stages issued past the end land before the kernel exits
+  __builtin_amdgcn_s_waitcnt(wait_vmcnt_lgkm0(0));
+  asm volatile("s_barrier" ::: "memory");
   if (n_blocks > 0) {
+    const char* const pl = (last & 1) ? pb1 : pb0;
     const int slot = last & 3;
-    if (slot == 0)
-      products(pa, dsa, st0);
-    else if (slot == 1)
-      products(pa, dsa, st1);
-    else if (slot == 2)
-      products(pa, dsa, st2);
-    else
-      products(pa, dsa, st3);
+    const char* const sl = slot == 0 ? st0 : slot == 1 ? st1 : slot == 2 ? st2 : st3;
+    if (pwave) {
+      product(pd, sl + OD);
+    } else {
+      p_ds(sl, pl, sdp, pd);
+      product(pd, sl + OQ);
+    }
   }
-  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
-  // accumulator register t of lane half hh: key 32 wave + (t/4)*8 + 4 hh + t%4,
+  // accumulator register t of lane half hh: key 32 pair + (t/4)*8 + 4 hh + t%4,
   // d = 32 db + kl
+  float* const outp = pwave ? a.dv : a.dk;
+  const float sc = pwave ? 1.f : a.scale;
 #pragma unroll
   for (int t = 0; t < 16; ++t) {
     const int k = kw0 + (t >> 2) * 8 + 4 * hh + (t & 3);
     if (k >= kt.k1) continue;
-    float* const dkp = a.dk + (int64_t(k) * a.Hkv + g) * D + kl;
-    float* const dvp = a.dv + (int64_t(k) * a.Hkv + g) * D + kl;
+    float* const op = outp + (int64_t(k) * a.Hkv + g) * D + kl;
 #pragma unroll
-    for (int db = 0; db < ND; ++db) {
-      dkp[32 * db] = dk[db][t] * a.scale;
-      dvp[32 * db] = dv[db][t];
-    }
+    for (int db = 0; db < ND; ++db) op[32 * db] = acc[db][t] * sc;
   }
 }
 
@@ -624,7 +672,7 @@ hipError_t launch_bwd_g(const BwdArgs& a, int n_units, int n_ktiles, hipStream_t
   if (n_ktiles > 0) {
     const int64_t blocks = int64_t(n_ktiles) * a.Hkv;
     if (blocks >= (int64_t(1) << 31)) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(dkdv_kernel, dim3(uint32_t(blocks)), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(dkdv_kernel, dim3(uint32_t(blocks)), dim3(512), 0, stream, a);
   }
   return hipGetLastError();
 }
