@@ -215,3 +215,47 @@ def test_backward_workload_sampled(cp, num):
     worst = float((np.abs(got - want) / bound).max())
     print(f"  sum_keys dv vs sum_rows dout: worst |diff| / bound {worst:.3f}", flush=True)
     assert worst <= 1.0
+
+
+def test_backward_rank_sum_is_the_unsplit_gradient(cp):
+    # The reverse ring / all-reduce over the CP group: summing every rank's
+    # dk, dv (the image keys' gradients included) and scattering every
+    # rank's dq by its index gives the unsplit sequence's gradients. Image
+    # rows are replicated on every rank; their loss gradient is carried by
+    # rank 0's copy here, so the sum counts it once.
+    T_img, T_txt, H, Hkv, D, P = 40, 600, 4, 2, 128, 4
+    T = T_img + T_txt
+    img = np.array([T_img], np.int32)
+    rng = np.random.default_rng(21)
+    q, k, v = (torch.from_numpy(rng.standard_normal((T, h, D), dtype=np.float32)).to(torch.bfloat16)
+               for h in (H, Hkv, Hkv))
+    dfull = torch.from_numpy(rng.standard_normal((T, H, D), dtype=np.float32)).to(torch.bfloat16)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    dq_sum = torch.zeros(T, H, D, dtype=torch.float64)
+    dk_sum = torch.zeros(T, Hkv, D, dtype=torch.float64)
+    dv_sum = torch.zeros(T, Hkv, D, dtype=torch.float64)
+    for r in range(P):
+        idx, _ = oracle.partition_index(T, img, None, P, r)
+        ids = torch.from_numpy(np.maximum(idx, 0).astype(np.int64))
+        dout = dfull[ids].clone()
+        dout[torch.from_numpy(idx < 0)] = 0
+        if r > 0:
+            dout[:T_img] = 0  # image rows: rank 0's copy carries the gradient
+        out, lse = cp.rank_fwd(qd, kd, vd, cp_size=P, cp_rank=r, n_img=img)
+        dq, dk, dv = cp.rank_bwd(qd, kd, vd, out, lse, dout.to(DEV), cp_size=P, cp_rank=r, n_img=img)
+        torch.cuda.synchronize()
+        real = torch.from_numpy(idx >= 0)
+        dq_sum.index_add_(0, ids[real], dq.double().cpu()[real])
+        dk_sum += dk.double().cpu()
+        dv_sum += dv.double().cpu()
+    out1, lse1 = cp.rank_fwd(qd, kd, vd, cp_size=1, cp_rank=0, n_img=img)
+    g1 = cp.rank_bwd(qd, kd, vd, out1, lse1, dfull.to(DEV), cp_size=1, cp_rank=0, n_img=img)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.rank_attention_backward(q, k, v, dfull, img, None, 1, 0)
+    for name, s, one, ref in (("dq", dq_sum, g1[0], rq), ("dk", dk_sum, g1[1], rk), ("dv", dv_sum, g1[2], rv)):
+        e_sum = rel_err(s, ref)
+        e_one = rel_err(one, ref)
+        print(f"  {name}: rank sum vs oracle {e_sum:.2e}, unsplit GPU vs oracle {e_one:.2e}", flush=True)
+        assert e_sum <= BWD_RTOL and e_one <= BWD_RTOL
+    # the image keys' gradients come from every rank's text rows
+    assert float(dk_sum[:T_img].abs().sum()) > 0
