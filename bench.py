@@ -255,6 +255,81 @@ def bench_backward(w, args):
     print(json.dumps(line), flush=True)
 
 
+def bench_hbm(w, args):
+    """A2 (gather) and A5 (merge) are HBM-bound; report GB/s of algorithmic
+    bytes against the 8 TB/s peak and against a plain device copy of about
+    the same size timed in the same process (the MALL is 256 MB, so a
+    working set of this size is not cache-resident)."""
+    import numpy as np
+    import torch
+
+    import context_parallelism_amd as cp
+
+    dev = torch.device("cuda:0")
+    n_img = w.n_img_array if any(w.n_img) else None
+    cu = w.cu_seqlens if w.n_samples > 1 else None
+    index, _ = cp.partition_index(w.seq_len, n_img, cu, cp_size=w.cp_size, cp_rank=w.rank)
+    R, H, D, P = len(index), w.heads, w.head_dim, w.cp_size
+    esize = 2 if w.dtype == "bf16" else 4
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    g = torch.Generator(device="cpu").manual_seed(w.seed)
+    q = torch.randn((w.seq_len, H, D), generator=g).to(dt).to(dev)
+    part = torch.randn((P, R, H, D), generator=g).to(dev)
+    plse = torch.randn((P, H, R), generator=g).to(dev)
+    mask = np.full(R, (1 << P) - 1, dtype=np.uint64).astype(np.uint32)
+
+    def time_ms(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        for a, b in evs:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in evs]))
+
+    gather_bytes = 2 * R * H * D * esize
+    merge_bytes = P * R * H * (D + 1) * 4 + R * H * (D * esize + 4)
+    # buffers made once; the timed calls are the C-ABI calls alone
+    idx_d = torch.as_tensor(index).to(dev)
+    qr = torch.empty((R, H, D), dtype=dt, device=dev)
+    mask_d = torch.as_tensor(mask.view(np.int32)).to(dev)
+    out = torch.empty((R, H, D), dtype=dt, device=dev)
+    lse = torch.empty((H, R), dtype=torch.float32, device=dev)
+    code = cp.CP_DTYPE_BF16 if w.dtype == "bf16" else cp.CP_DTYPE_F32
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def gather():
+        cp.check(cp.cp_gather_rows(q.data_ptr(), code, w.seq_len, H * D, idx_d.data_ptr(), R, qr.data_ptr(),
+                                   stream), "cp_gather_rows")
+
+    def merge():
+        cp.check(cp.cp_lse_merge(part.data_ptr(), plse.data_ptr(), mask_d.data_ptr(), P, R, H, D, code,
+                                 out.data_ptr(), lse.data_ptr(), stream), "cp_lse_merge")
+    t_gather = time_ms(gather)
+    t_merge = time_ms(merge)
+    src = torch.empty(merge_bytes // 2 // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    t_copy = time_ms(lambda: dst.copy_(src))
+    copy_bytes = 2 * src.numel() * 4
+
+    def rate(b, t):
+        return round(b / (t * 1e-3) / 1e9, 1)
+    copy_gbps = rate(copy_bytes, t_copy)
+    line = {"mode": "hbm", "unit": "GB/s", "peak_GBps": 8000.0,
+            "gather": {"kernel": "gather_rows_kernel", "bytes": gather_bytes, "ms": round(t_gather, 4),
+                       "GBps": rate(gather_bytes, t_gather),
+                       "frac_of_copy": round(rate(gather_bytes, t_gather) / copy_gbps, 3)},
+            "merge": {"kernel": "lse_merge_kernel", "bytes": merge_bytes, "ms": round(t_merge, 4),
+                      "GBps": rate(merge_bytes, t_merge), "steps_per_row": P,
+                      "frac_of_copy": round(rate(merge_bytes, t_merge) / copy_gbps, 3)},
+            "copy": {"bytes": copy_bytes, "ms": round(t_copy, 4), "GBps": copy_gbps},
+            "config": {"workload": w.name, "cp_rank": w.rank, "rank_rows": R}}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -278,6 +353,10 @@ def main():
     ap.add_argument("--backward", action="store_true",
                     help="instead of the headline line: time cp_attn_rank_bwd (gradients of the rank "
                          "share) on the workload; one JSON line")
+    ap.add_argument("--hbm", action="store_true",
+                    help="instead of the headline line: the HBM-bound steps on the workload's shape -- "
+                         "the Q gather (cp_gather_rows) and the LSE merge (cp_lse_merge, every row with "
+                         "all P steps) -- in GB/s against the 8 TB/s peak and a device copy; one JSON line")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="instead of the attention, run --steps plain device copies of this many MiB "
                          "(the reference kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -312,6 +391,9 @@ def main():
         return
     if args.backward:
         bench_backward(w, args)
+        return
+    if args.hbm:
+        bench_hbm(w, args)
         return
     rank = w.rank if args.rank is None else args.rank
     if rank != w.rank:
