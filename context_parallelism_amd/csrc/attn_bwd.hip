@@ -445,8 +445,24 @@ void dkdv_kernel(const BwdArgs a) {
   // KV head g (a.group of them) inner
   const int group = a.group;
   const int n_blocks = (kt.rb1 - kt.rb0) * group;
-  auto issue = [&](int j, char* st) {
-    const int rb = kt.rb0 + j / group, h = g * group + j % group;
+  // Position of a block step j = (rb - rb0) * group + hq: its row block and
+  // query head within the group, advanced one step at a time (no division
+  // in the loop); past the last step it stays there.
+  struct StepPos {
+    int rb, hq, j;
+  };
+  const int last = n_blocks - 1;
+  auto next = [&](StepPos& p) {
+    if (p.j < last) {
+      ++p.j;
+      if (++p.hq == group) {
+        p.hq = 0;
+        ++p.rb;
+      }
+    }
+  };
+  auto issue = [&](const StepPos& p, char* st) {
+    const int rb = p.rb, h = g * group + p.hq;
     const int r0 = rb * RBK;
     const int valid = __builtin_amdgcn_readfirstlane(max(min(a.R - r0, RBK), 0) * row_bytes);
     const int64_t noff = (int64_t(r0) * a.H + h) * D * 2;
@@ -499,12 +515,11 @@ void dkdv_kernel(const BwdArgs a) {
   };
   // P wave, step j in slot st: the mask on S, P = exp2(S c2 - lse log2 e)
   // (0 for pad rows, whose record holds +inf), P to the partner
-  auto p_softmax = [&](int j, const char* st, f32x16& s, bf16x8 (&pa)[2], char* pbuf) {
+  auto p_softmax = [&](int rb, const char* st, f32x16& s, bf16x8 (&pa)[2], char* pbuf) {
     const int* const rec = reinterpret_cast<const int*>(st + OREC);
     // every row of the block sees every key of the pair unless the block
     // holds a causal edge or a sample boundary; then S = -inf where the key
     // is outside [sample start, row's global id]
-    const int rb = kt.rb0 + j / group;
     if (!(blk[2 * rb] <= kw0 && kw0 + 31 <= blk[2 * rb + 1])) {
 #pragma unroll
       for (int run = 0; run < 2; ++run)
@@ -564,10 +579,13 @@ void dkdv_kernel(const BwdArgs a) {
   // j - 2, which both waves finished in iteration j - 1. Every iteration
   // issues one stage (past the end, the last step again, into a free slot),
   // so the count of loads in flight after step j's is always one stage.
-  const int last = n_blocks - 1;
+  StepPos ip = {kt.rb0, 0, 0};  // the next step to issue
+  StepPos cp = {kt.rb0, 0, 0};  // the step the P waves compute
   if (n_blocks > 0) {
-    issue(0, st0);
-    issue(min(1, last), st1);
+    issue(ip, st0);
+    next(ip);
+    issue(ip, st1);
+    next(ip);
   }
   // The slot of step -1 (st3) and the P buffer of parity -1 (pb1) hold
   // zeros, so the first iteration's products of step -1 add nothing and the
@@ -594,7 +612,8 @@ void dkdv_kernel(const BwdArgs a) {
   {                                                             \
     __builtin_amdgcn_s_waitcnt(wait_vmcnt_lgkm0(PER_STAGE));    \
     asm volatile("s_barrier" ::: "memory");                     \
-    issue(min((J) + 2, last), NXT);                             \
+    issue(ip, NXT);                                             \
+    next(ip);                                                   \
     if (pwave) {                                                \
       __builtin_amdgcn_s_setprio(1);                            \
       product(pd, PREV + OD);                                   \
@@ -607,7 +626,7 @@ void dkdv_kernel(const BwdArgs a) {
     __builtin_amdgcn_s_waitcnt(wait_vmcnt_lgkm0(63));           \
     asm volatile("s_barrier" ::: "memory");                     \
     if (pwave) {                                                \
-      p_softmax((J), CUR, sdp, pd, PC);                         \
+      p_softmax(cp.rb, CUR, sdp, pd, PC);                       \
     } else {                                                    \
       __builtin_amdgcn_s_setprio(1);                            \
       product(pd, PREV + OQ);                                   \
@@ -615,6 +634,7 @@ void dkdv_kernel(const BwdArgs a) {
       schedule_matrix_phase();                                  \
       __builtin_amdgcn_s_setprio(0);                            \
     }                                                           \
+    next(cp);                                                   \
   }
   // (guarded steps rather than early exits: one loop exit keeps the
   // accumulators in place instead of copying them at every exit)
