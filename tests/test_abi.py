@@ -263,3 +263,59 @@ def test_zero_row_problem(cp):
     a, cu_rows = cp.partition_index(0, None, np.array([0], np.int32), cp_size=4, cp_rank=1)
     assert a.size == 0 and list(cu_rows) == [0]
     assert cp.pair_counts(0, None, np.array([0], np.int32), cp_size=4, cp_rank=1) == (0, 0)
+
+
+def bwd_ws_status(cp, heads=4, kv_heads=4, head_dim=128, dtype=1, seq_len=100, P=2, r=0, split=0):
+    b = ctypes.c_size_t(12345)
+    st = cp.cp_attn_rank_bwd_workspace_size(seq_len, None, None, 1, P, r, split, heads, kv_heads, head_dim,
+                                            dtype, ctypes.byref(b))
+    return st, b.value
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(heads=6, kv_heads=4), "CP_EINVAL"),
+    (dict(head_dim=96), "CP_EUNSUPPORTED"),
+    (dict(head_dim=64), "CP_EUNSUPPORTED"),   # backward: bf16 with head_dim 128 only
+    (dict(dtype=0), "CP_EUNSUPPORTED"),
+    (dict(dtype=2), "CP_EUNSUPPORTED"),
+    (dict(r=2), "CP_EINVAL"),
+    (dict(P=0), "CP_EINVAL"),
+    (dict(split=5), "CP_EUNSUPPORTED"),
+])
+def test_bwd_workspace_size_errors(cp, kw, code):
+    st, b = bwd_ws_status(cp, **kw)
+    assert st == getattr(cp, code) and b == 12345
+
+
+def test_bwd_workspace_size_grows_with_problem(cp):
+    st_a, a = bwd_ws_status(cp, seq_len=1000)
+    st_b, b = bwd_ws_status(cp, seq_len=2000)
+    assert st_a == st_b == cp.CP_OK and 0 < a < b
+
+
+def test_bwd_argument_errors_before_any_device_work(cp):
+    # argument checks run before any HIP call, so these are CPU-safe
+    fake = ctypes.c_void_p(4096)  # never dereferenced: the call must fail first
+    ok_ws = bwd_ws_status(cp)[1]
+
+    def bwd(**kw):
+        a = dict(q=fake, k=fake, v=fake, out=fake, lse=fake, dout=fake, dtype=1, seq_len=100, cu=None, n=1,
+                 P=2, r=0, H=4, Hkv=4, D=128, dq=fake, dk=fake, dv=fake, ws=ctypes.c_void_p(1 << 20), wsb=ok_ws)
+        a.update(kw)
+        return cp.cp_attn_rank_bwd(a["q"], a["k"], a["v"], a["out"], a["lse"], a["dout"], a["dtype"],
+                                   a["seq_len"], None, a["cu"], a["n"], a["P"], a["r"], 0, a["H"], a["Hkv"],
+                                   a["D"], a["dq"], a["dk"], a["dv"], a["ws"], a["wsb"], None)
+    for name in ("q", "k", "v", "out", "lse", "dout", "dq", "dk", "dv", "ws"):
+        assert bwd(**{name: None}) == cp.CP_EINVAL, name
+    assert bwd(ws=ctypes.c_void_p((1 << 20) + 4)) == cp.CP_EINVAL  # workspace alignment
+    assert bwd(dq=ctypes.c_void_p(4100)) == cp.CP_EINVAL  # 16-byte alignment of the gradients
+    assert bwd(wsb=ok_ws - 1) == cp.CP_ENOSPC
+    assert bwd(D=64) == cp.CP_EUNSUPPORTED
+    assert bwd(dtype=0) == cp.CP_EUNSUPPORTED
+    assert bwd(H=6) == cp.CP_EINVAL
+    assert bwd(r=3) == cp.CP_EINVAL
+    assert bwd(seq_len=2 ** 31) == cp.CP_EUNSUPPORTED
+    # an empty packed batch (cu_seqlens = [0]) is a valid problem with nothing to do
+    zero = np.array([0], np.int32)
+    cu0 = zero.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    assert bwd(seq_len=0, cu=cu0, n=0, q=None, out=None, lse=None, dout=None, dq=None) == cp.CP_OK
