@@ -124,15 +124,17 @@ __device__ inline float sum_with_partner16(float x) {
 }
 
 // ---------------------------------------------------------------- prep
-// 16 lanes per (row, head) pair, 8 elements each; 16 pairs per 256 threads;
-// rows up to 32 nrb (rows >= R get pad records).
-__global__ __launch_bounds__(256) void bwd_prep_kernel(const __bf16* __restrict__ out,
-                                                      const __bf16* __restrict__ dout,
+// 16 lanes per (row, head) pair, D/16 elements each; 16 pairs per 256
+// threads; rows up to 32 nrb (rows >= R get pad records). Any input dtype
+// (bf16 or fp32) and head_dim (64 or 128).
+template <typename T, int D>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const T* __restrict__ out, const T* __restrict__ dout,
                                                       const float* __restrict__ lse,
                                                       const int32_t* __restrict__ index,
                                                       const int32_t* __restrict__ row_lo,
                                                       float* __restrict__ delta, int32_t* __restrict__ rec,
                                                       int32_t R, int32_t H, int32_t nrb) {
+  constexpr int E = D / 16;
   const int64_t pair = int64_t(blockIdx.x) * 16 + (threadIdx.x >> 4);
   const int sub = threadIdx.x & 15;
   const bool ok = pair < int64_t(nrb) * kBwdRowBlock * H;
@@ -141,11 +143,9 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const __bf16* __restrict_
   const bool in = r < R;
   float s = 0.f;
   if (in) {
-    const int64_t off = (int64_t(r) * H + h) * 128 + sub * 8;  // [R, H, 128]
-    const bf16x8 o = *reinterpret_cast<const bf16x8*>(out + off);
-    const bf16x8 d = *reinterpret_cast<const bf16x8*>(dout + off);
+    const int64_t off = (int64_t(r) * H + h) * D + sub * E;  // [R, H, D]
 #pragma unroll
-    for (int i = 0; i < 8; ++i) s = __builtin_fmaf(float(o[i]), float(d[i]), s);
+    for (int i = 0; i < E; ++i) s = __builtin_fmaf(float(out[off + i]), float(dout[off + i]), s);
   }
   s = sum_with_partner16(s);
   if (!ok || sub != 0) return;
@@ -701,13 +701,25 @@ hipError_t launch_bwd_g(const BwdArgs& a, int n_units, int n_ktiles, hipStream_t
 
 hipError_t launch_bwd_prep(const void* out, const void* dout, const float* lse, const int32_t* index,
                            const int32_t* row_lo, float* delta, int32_t* rec, int32_t R, int32_t H,
-                           int32_t nrb, hipStream_t stream) {
+                           int32_t nrb, int32_t dtype, int32_t head_dim, hipStream_t stream) {
   if (R == 0) return hipSuccess;
   const int64_t blocks = (int64_t(nrb) * kBwdRowBlock * H + 15) / 16;
   if (blocks >= (int64_t(1) << 31)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(bwd_prep_kernel, dim3(uint32_t(blocks)), dim3(256), 0, stream,
-                     static_cast<const __bf16*>(out), static_cast<const __bf16*>(dout), lse, index, row_lo,
-                     delta, rec, R, H, nrb);
+  const dim3 grid = dim3(uint32_t(blocks)), block = dim3(256);
+#define PREP(T, DD)                                                                                          \
+  hipLaunchKernelGGL((bwd_prep_kernel<T, DD>), grid, block, 0, stream, static_cast<const T*>(out),            \
+                     static_cast<const T*>(dout), lse, index, row_lo, delta, rec, R, H, nrb)
+  if (dtype == 1 && head_dim == 128)
+    PREP(__bf16, 128);
+  else if (dtype == 1 && head_dim == 64)
+    PREP(__bf16, 64);
+  else if (dtype == 0 && head_dim == 128)
+    PREP(float, 128);
+  else if (dtype == 0 && head_dim == 64)
+    PREP(float, 64);
+  else
+    return hipErrorInvalidValue;
+#undef PREP
   return hipGetLastError();
 }
 

@@ -207,19 +207,21 @@ cp_status rank_bwd(const void* q, const void* k, const void* v, const void* out,
     a.scale = float(1.0 / std::sqrt(double(head_dim)));
     a.scale_log2 = float(1.4426950408889634 / std::sqrt(double(head_dim)));
     if (R > 0) {
-      const int64_t row_bytes = int64_t(heads) * head_dim * 2;
+      const int64_t row_bytes = int64_t(heads) * head_dim * (dtype == CP_DTYPE_BF16 ? 2 : 4);
       if (launch_gather(q, a.index, ws + w.off_qr, R, row_bytes, s) != hipSuccess) return CP_EHIP;
       if (launch_bwd_prep(out, dout, lse, a.index, reinterpret_cast<const int32_t*>(ws + w.off_row_lo),
                           reinterpret_cast<float*>(ws + w.off_delta), reinterpret_cast<int32_t*>(ws + w.off_rec),
-                          int32_t(R), heads, w.nrb, s) != hipSuccess)
+                          int32_t(R), heads, w.nrb, dtype, head_dim, s) != hipSuccess)
         return CP_EHIP;
       if (w.plan.rows.pad_rows > 0 &&
           launch_fill_pad_rows(a.index, R, heads, head_dim, CP_DTYPE_F32, dq, nullptr, s) != hipSuccess)
         return CP_EHIP;
     }
     // every key tile of every sample is written (zeros where no rank row sees it)
-    if (launch_bwd(a, w.heads_per_wg, R > 0 ? int(w.plan.rows.units.size()) : 0,
-                   int(w.plan.ktiles.size()), s) != hipSuccess)
+    const int n_units = R > 0 ? int(w.plan.rows.units.size()) : 0;
+    const int n_ktiles = int(w.plan.ktiles.size());
+    if ((w.mfma ? launch_bwd(a, w.heads_per_wg, n_units, n_ktiles, s)
+                : launch_bwd_generic(a, dtype, head_dim, n_units, n_ktiles, s)) != hipSuccess)
       return CP_EHIP;
     return CP_OK;
   } catch (const std::exception&) {

@@ -60,10 +60,15 @@ struct BwdArgs {
 // records (rec, nrb 32-row blocks; row_lo: sample start per row).
 hipError_t launch_bwd_prep(const void* out, const void* dout, const float* lse, const int32_t* index,
                            const int32_t* row_lo, float* delta, int32_t* rec, int32_t R, int32_t H,
-                           int32_t nrb, hipStream_t stream);
+                           int32_t nrb, int32_t dtype, int32_t head_dim, hipStream_t stream);
 // dQ for every unit, then dK/dV for every key tile.
 hipError_t launch_bwd(const BwdArgs& a, int heads_per_wg, int n_units, int n_ktiles,
                       hipStream_t stream);
+// The same gradients with plain fp32 FMA kernels (fp32 inputs, or head_dim
+// 64): one workgroup per (row tile, head) for dQ, per (key tile, KV head)
+// for dK/dV.
+hipError_t launch_bwd_generic(const BwdArgs& a, int32_t dtype, int32_t head_dim, int n_units, int n_ktiles,
+                              hipStream_t stream);
 
 hipError_t launch_gather(const void* src, const int32_t* index, void* dst, int64_t n_rows,
                          int64_t row_bytes, hipStream_t stream);

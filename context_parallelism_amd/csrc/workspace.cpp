@@ -95,15 +95,20 @@ int32_t prepare_bwd_workspace(int64_t seq_len, const int32_t* n_img, const int32
   if (dtype != CP_DTYPE_F32 && dtype != CP_DTYPE_BF16) return CP_EUNSUPPORTED;
   if (heads < 1 || kv_heads < 1 || heads % kv_heads != 0) return CP_EINVAL;
   if (head_dim != 64 && head_dim != 128) return CP_EUNSUPPORTED;
-  if (dtype != CP_DTYPE_BF16 || head_dim != 128) return CP_EUNSUPPORTED;  // backward: bf16, 128
   int32_t st = build_meta(seq_len, n_img, cu_seqlens, n_samples, cp_size, cp_rank, w.meta, split);
   if (st != CP_OK) return st;
   w.heads = heads;
   w.kv_heads = kv_heads;
   w.head_dim = head_dim;
   const int32_t group = heads / kv_heads;
-  w.heads_per_wg = (group % 4 == 0) ? 4 : (group % 2 == 0) ? 2 : 1;
-  w.rows_per_tile = 32 * 4 / w.heads_per_wg;  // dQ: 4 waves of 32 rows
+  w.mfma = dtype == CP_DTYPE_BF16 && head_dim == 128;
+  if (w.mfma) {
+    w.heads_per_wg = (group % 4 == 0) ? 4 : (group % 2 == 0) ? 2 : 1;
+    w.rows_per_tile = 32 * 4 / w.heads_per_wg;  // dQ: 4 waves of 32 rows
+  } else {
+    w.heads_per_wg = 1;
+    w.rows_per_tile = 256 / (head_dim / 32);  // dQ: 256 threads, head_dim / 32 per row
+  }
   w.n_hg = heads / w.heads_per_wg;
   build_bwd_plan(w.meta, w.rows_per_tile, w.plan);
   const Plan& p = w.plan.rows;
@@ -128,7 +133,7 @@ int32_t prepare_bwd_workspace(int64_t seq_len, const int32_t* n_img, const int32
   w.plan_bytes = off;
   w.nrb = int32_t((R + kBwdRowBlock - 1) / kBwdRowBlock);
   w.off_qr = off;
-  off = align256(off + R * size_t(heads) * head_dim * 2);
+  off = align256(off + R * size_t(heads) * head_dim * (dtype == CP_DTYPE_BF16 ? 2 : 4));
   w.off_delta = off;
   off = align256(off + size_t(heads) * R * sizeof(float));
   w.off_rec = off;

@@ -45,17 +45,18 @@ int32_t prepare_workspace(int64_t seq_len, const int32_t* n_img, const int32_t* 
                           int32_t kv_heads, int32_t head_dim, int32_t dtype, Workspace& w,
                           int32_t split = 0);
 
-// Backward workspace (bf16, head_dim 128), each region 256-byte aligned:
+// Backward workspace, each region 256-byte aligned:
 //   plan  : index int32[R], dQ row tiles, spans, step-ordered entries, units,
 //           dK/dV key tiles, sample start per row int32[R], per 32-row
 //           block bounds int32[nrb][2] (uploaded from the host in one copy);
-//   qr    : gathered rank-local Q rows [R, H, 128] bf16;
+//   qr    : gathered rank-local Q rows [R, H, D] in the input dtype;
 //   delta : rowsum(dout * out) fp32 [H, R];
 //   rec   : dK/dV row records [H][nrb][4][32] (nrb = ceil(R / 32)): per row
 //           lse * log2(e), delta, sample start, global id - sample start.
 struct BwdWorkspace {
   Meta meta;
   BwdPlan plan;
+  bool mfma = false;  // bf16 with head_dim 128: the MFMA kernels; otherwise the fp32 FMA kernels
   int32_t heads = 0, kv_heads = 0, head_dim = 0;
   int32_t heads_per_wg = 1, rows_per_tile = 0, n_hg = 0;
   size_t off_index = 0, off_tiles = 0, off_spans = 0, off_tile_entries = 0, off_units = 0,

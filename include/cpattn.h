@@ -280,8 +280,10 @@ cp_status cp_attn_rank_fwd_ex(const void *q, const void *k, const void *v, int32
  *   CP group, and scattering each rank's dq back by its index, gives the
  *   gradients of the whole sequence (the reverse ring / all-reduce).
  * workspace: device, cp_attn_rank_bwd_workspace_size bytes, 256-byte
- *   aligned. Supported: dtype CP_DTYPE_BF16 with head_dim 128; otherwise
- *   CP_EUNSUPPORTED. Deterministic (no atomics).
+ *   aligned. dtype and head_dim as for cp_attn_rank_fwd: bf16 with
+ *   head_dim 128 runs on MFMA (P and dS rounded to bf16 for the products);
+ *   fp32 inputs and head_dim 64 run fp32 FMA kernels (P and dS in fp32).
+ *   Deterministic (no atomics).
  */
 cp_status cp_attn_rank_bwd_workspace_size(int64_t seq_len, const int32_t *n_img,
                                           const int32_t *cu_seqlens, int32_t n_samples,

@@ -275,8 +275,7 @@ def bwd_ws_status(cp, heads=4, kv_heads=4, head_dim=128, dtype=1, seq_len=100, P
 @pytest.mark.parametrize("kw,code", [
     (dict(heads=6, kv_heads=4), "CP_EINVAL"),
     (dict(head_dim=96), "CP_EUNSUPPORTED"),
-    (dict(head_dim=64), "CP_EUNSUPPORTED"),   # backward: bf16 with head_dim 128 only
-    (dict(dtype=0), "CP_EUNSUPPORTED"),
+    (dict(head_dim=256), "CP_EUNSUPPORTED"),
     (dict(dtype=2), "CP_EUNSUPPORTED"),
     (dict(r=2), "CP_EINVAL"),
     (dict(P=0), "CP_EINVAL"),
@@ -291,6 +290,10 @@ def test_bwd_workspace_size_grows_with_problem(cp):
     st_a, a = bwd_ws_status(cp, seq_len=1000)
     st_b, b = bwd_ws_status(cp, seq_len=2000)
     assert st_a == st_b == cp.CP_OK and 0 < a < b
+    # every forward dtype and head_dim has a backward; fp32 holds a wider Q copy
+    st_c, c = bwd_ws_status(cp, seq_len=1000, dtype=0)
+    st_d, d = bwd_ws_status(cp, seq_len=1000, head_dim=64)
+    assert st_c == st_d == cp.CP_OK and c > a and 0 < d
 
 
 def test_bwd_argument_errors_before_any_device_work(cp):
@@ -310,8 +313,8 @@ def test_bwd_argument_errors_before_any_device_work(cp):
     assert bwd(ws=ctypes.c_void_p((1 << 20) + 4)) == cp.CP_EINVAL  # workspace alignment
     assert bwd(dq=ctypes.c_void_p(4100)) == cp.CP_EINVAL  # 16-byte alignment of the gradients
     assert bwd(wsb=ok_ws - 1) == cp.CP_ENOSPC
-    assert bwd(D=64) == cp.CP_EUNSUPPORTED
-    assert bwd(dtype=0) == cp.CP_EUNSUPPORTED
+    assert bwd(D=96) == cp.CP_EUNSUPPORTED
+    assert bwd(dtype=3) == cp.CP_EUNSUPPORTED
     assert bwd(H=6) == cp.CP_EINVAL
     assert bwd(r=3) == cp.CP_EINVAL
     assert bwd(seq_len=2 ** 31) == cp.CP_EUNSUPPORTED
