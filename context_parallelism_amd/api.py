@@ -148,7 +148,7 @@ class RankAttention:
         if events is not None:
             if len(events) != 6:
                 raise ValueError("cp_attn_rank_fwd_ex records exactly six events")
-            ev = (ctypes.c_void_p * 6)(*[ctypes.c_void_p(int(e)) for e in events])
+            ev = (ctypes.c_void_p * 6)(*[ctypes.c_void_p(int(e) if e else None) for e in events])
         check(_lib.cp_attn_rank_fwd_ex(self.q.data_ptr(), self.k.data_ptr(), self.v.data_ptr(), self.dtype,
                                        self.T, self._img_p, self._cu_p, self.n_samples, self.cp_size,
                                        self.cp_rank, self.split, self.H, self.Hkv, self.D,

@@ -67,7 +67,7 @@ hipError_t stage_and_upload(size_t plan_bytes, Pack pack, void* dst, hipStream_t
 inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 inline hipError_t mark(void* const* events, int i, hipStream_t s) {
-  return events ? hipEventRecord(static_cast<hipEvent_t>(events[i]), s) : hipSuccess;
+  return (events && events[i]) ? hipEventRecord(static_cast<hipEvent_t>(events[i]), s) : hipSuccess;
 }
 
 cp_status rank_fwd(const void* q, const void* k, const void* v, int32_t dtype, int64_t seq_len,

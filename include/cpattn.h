@@ -182,8 +182,9 @@ cp_status cp_attn_rank_fwd(const void *q, const void *k, const void *v, int32_t 
  * [3] after the V relayout (bf16, head_dim 128; otherwise right after [2]),
  * [4] after the per-step attention, [5] after the merge. A caller can then
  * time one stage with hipEventElapsedTime, without a profiler. events may
- * be NULL (then this is exactly cp_attn_rank_fwd). The library does not
- * keep the events.
+ * be NULL (then this is exactly cp_attn_rank_fwd), and so may any entry:
+ * that boundary is then not recorded (each record costs a few microseconds
+ * on the stream). The library does not keep the events.
  */
 cp_status cp_attn_rank_fwd_timed(const void *q, const void *k, const void *v, int32_t dtype,
                                  int64_t seq_len, const int32_t *n_img, const int32_t *cu_seqlens,
