@@ -3,8 +3,9 @@
 // exactly by their log-sum-exp). One wavefront covers one rank-local row
 // and 256/D heads; each lane owns four consecutive head_dim elements of
 // one head, loaded as float4, so a wavefront reads contiguous 1 KiB runs
-// of every step's partial. The reduction over steps runs in increasing
-// step order, the same for every lane, so results are deterministic.
+// of every step's partial. Up to 8 steps, every step's loads are issued
+// before the reduction. The reduction over steps runs in increasing step
+// order, the same for every lane, so results are deterministic.
 #include "kernels.h"
 
 namespace cpattn {
@@ -23,7 +24,10 @@ __device__ inline void store_out(__bf16* out, int64_t i4, float4 v) {
   reinterpret_cast<bf16x4*>(out)[i4] = b;
 }
 
-template <int D, typename OutT>
+// NS > 0: at most NS steps (unrolled: every step's lse and partial load is
+// in flight before the reduction); NS = 0: any count up to 32, one step at
+// a time.
+template <int D, int NS, typename OutT>
 __global__ __launch_bounds__(kMergeThreads) void lse_merge_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_lse,
     const uint32_t* __restrict__ mask, uint32_t valid_bits, int32_t n_rows, int32_t H,
@@ -40,34 +44,61 @@ __global__ __launch_bounds__(kMergeThreads) void lse_merge_kernel(
   const int d4 = lane % kLanesPerHead;
   const int64_t out4 = (row * H + h) * kLanesPerHead + d4;
   const uint32_t bits = mask[row] & valid_bits;
-  if (bits == 0) {
+  auto empty_row = [&]() {
     store_out(out, out4, make_float4(0.f, 0.f, 0.f, 0.f));
     if (d4 == 0) lse[int64_t(h) * n_rows + row] = -INFINITY;
+  };
+  if (bits == 0) {
+    empty_row();
     return;
   }
-  float m = -INFINITY;
-  for (uint32_t b = bits; b; b &= b - 1) {
-    const int s = __builtin_ctz(b);
-    m = fmaxf(m, part_lse[(int64_t(s) * H + h) * n_rows + row]);
-  }
-  float wsum = 0.f;
+  const float4* const po = reinterpret_cast<const float4*>(part_o);
+  const int64_t step_stride4 = int64_t(n_rows) * H * kLanesPerHead;
+  const int64_t row4 = (row * H + h) * kLanesPerHead + d4;
+  float m = -INFINITY, wsum = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (uint32_t b = bits; b; b &= b - 1) {
-    const int s = __builtin_ctz(b);
-    const float ls = part_lse[(int64_t(s) * H + h) * n_rows + row];
-    if (ls == -INFINITY) continue;  // an empty partial: its output is not read
-    const float w = expf(ls - m);
-    const float4 o = reinterpret_cast<const float4*>(part_o)[(int64_t(s) * n_rows + row) * H * kLanesPerHead +
-                                                              int64_t(h) * kLanesPerHead + d4];
-    wsum += w;
-    acc.x += w * o.x;
-    acc.y += w * o.y;
-    acc.z += w * o.z;
-    acc.w += w * o.w;
+  if constexpr (NS > 0) {
+    float ls[NS];
+    float4 o[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const bool on = (bits >> s) & 1u;
+      ls[s] = on ? part_lse[(int64_t(s) * H + h) * n_rows + row] : -INFINITY;
+      o[s] = on ? po[int64_t(s) * step_stride4 + row4] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int s = 0; s < NS; ++s) m = fmaxf(m, ls[s]);
+    // steps in increasing order, empty partials (lse -inf) skipped
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      if (ls[s] == -INFINITY) continue;
+      const float w = expf(ls[s] - m);
+      wsum += w;
+      acc.x += w * o[s].x;
+      acc.y += w * o[s].y;
+      acc.z += w * o[s].z;
+      acc.w += w * o[s].w;
+    }
+  } else {
+    for (uint32_t b = bits; b; b &= b - 1) {
+      const int s = __builtin_ctz(b);
+      m = fmaxf(m, part_lse[(int64_t(s) * H + h) * n_rows + row]);
+    }
+    for (uint32_t b = bits; b; b &= b - 1) {
+      const int s = __builtin_ctz(b);
+      const float ls = part_lse[(int64_t(s) * H + h) * n_rows + row];
+      if (ls == -INFINITY) continue;  // an empty partial: its output is not read
+      const float w = expf(ls - m);
+      const float4 o = po[int64_t(s) * step_stride4 + row4];
+      wsum += w;
+      acc.x += w * o.x;
+      acc.y += w * o.y;
+      acc.z += w * o.z;
+      acc.w += w * o.w;
+    }
   }
   if (!(wsum > 0.f)) {  // every partial empty
-    store_out(out, out4, make_float4(0.f, 0.f, 0.f, 0.f));
-    if (d4 == 0) lse[int64_t(h) * n_rows + row] = -INFINITY;
+    empty_row();
     return;
   }
   const float inv = 1.f / wsum;
@@ -85,14 +116,26 @@ hipError_t launch_merge_d(const float* part_o, const float* part_lse, const uint
   const int64_t waves = n_rows * head_groups;
   const int64_t blocks = (waves * 64 + kMergeThreads - 1) / kMergeThreads;
   if (blocks >= (int64_t(1) << 31)) return hipErrorInvalidValue;
-  if (dtype == 1)
-    hipLaunchKernelGGL((lse_merge_kernel<D, __bf16>), dim3(uint32_t(blocks)), dim3(kMergeThreads), 0,
-                       stream, part_o, part_lse, mask, valid, int32_t(n_rows), heads, head_groups,
-                       static_cast<__bf16*>(out), lse);
+#define MERGE(NSV)                                                                                       \
+  {                                                                                                      \
+    if (dtype == 1)                                                                                      \
+      hipLaunchKernelGGL((lse_merge_kernel<D, NSV, __bf16>), dim3(uint32_t(blocks)), dim3(kMergeThreads), 0, \
+                         stream, part_o, part_lse, mask, valid, int32_t(n_rows), heads, head_groups,     \
+                         static_cast<__bf16*>(out), lse);                                                \
+    else                                                                                                 \
+      hipLaunchKernelGGL((lse_merge_kernel<D, NSV, float>), dim3(uint32_t(blocks)), dim3(kMergeThreads), 0,  \
+                         stream, part_o, part_lse, mask, valid, int32_t(n_rows), heads, head_groups,     \
+                         static_cast<float*>(out), lse);                                                 \
+  }
+  if (n_steps <= 2)
+    MERGE(2)
+  else if (n_steps <= 4)
+    MERGE(4)
+  else if (n_steps <= 8)
+    MERGE(8)
   else
-    hipLaunchKernelGGL((lse_merge_kernel<D, float>), dim3(uint32_t(blocks)), dim3(kMergeThreads), 0,
-                       stream, part_o, part_lse, mask, valid, int32_t(n_rows), heads, head_groups,
-                       static_cast<float*>(out), lse);
+    MERGE(0)
+#undef MERGE
   return hipGetLastError();
 }
 
