@@ -20,8 +20,11 @@
 //    walks the tile's key spans over all ring steps, 32 keys at a time,
 //    recomputing S^T = K Q^T and dP^T = V dO^T (K and V rows from LDS, Q and
 //    dO in registers) and accumulating dQ^T += K^T dS^T, the K^T operand
-//    read from the same row-major K tile with transposing LDS reads; K and V
-//    tiles stream through a three-slot LDS ring (48 KiB), two tiles ahead;
+//    read from the same row-major K tile with transposing LDS reads. The
+//    steps are software-pipelined: the scores of tile t + 1 go to the matrix
+//    cores while the vector units turn tile t's scores into dS, then tile
+//    t's dQ product follows. K and V tiles stream through a four-slot LDS
+//    ring (64 KiB), two tiles ahead of the scores;
 //  * dK/dV: one workgroup of 8 waves per (128-key tile, KV head); waves w
 //    and w + 4 share a SIMD and 32 keys, and walk the rank's 32-row blocks
 //    that see the tile, for every query head of the KV head. Wave w keeps
@@ -52,7 +55,6 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kBufferWord3 = 0x00020000;  // raw buffer access, gfx9 family
-constexpr int kWaitVmcnt0 = 0x0F70;       // s_waitcnt vmcnt(0), expcnt and lgkmcnt untouched
 
 // s_waitcnt immediate for vmcnt(n) alone (n < 64: low four bits in [3:0],
 // high two in [15:14]; expcnt 7 and lgkmcnt 15 mean "no wait").
@@ -165,15 +167,40 @@ struct Cursor {
 };
 
 // ---------------------------------------------------------------- dQ
+// __builtin_amdgcn_sched_group_barrier instruction classes
+constexpr int kSchedValu = 0x0002;
+constexpr int kSchedMfma = 0x0008;
+constexpr int kSchedDsRead = 0x0100;
+// One pipelined dQ step: the 16 score MFMAs of the next tile, each with its
+// LDS read issued kDqAhead MFMAs ahead and a share of this tile's dS vector
+// work beside it, then the 8 dQ MFMAs (two transposing reads each).
+constexpr int kDqAhead = 2;
+constexpr int kDqValuPerMfma = 7;
+__device__ inline void schedule_dq_step() {
+  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kDqAhead, 0);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedValu, kDqValuPerMfma, 0);
+    if (i + kDqAhead < 16) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    if (i + 2 < 8) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+  }
+}
+
 template <int G>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void dq_kernel(const BwdArgs a) {
-  constexpr int D = 128, BN = 32, KB = BN / 32, NQ = 8, ND = 4, RB = 4 / G;
+  constexpr int D = 128, BN = 32, NQ = 8, ND = 4, RB = 4 / G;
   constexpr int TILE = BN * D * 2;     // bytes of a K or V tile
   constexpr int CH = TILE / 1024 / 4;  // LDS-DMA instructions per wave per tensor
   constexpr int PER_STAGE = 2 * CH;    // LDS-DMA instructions per wave per tile
-  __shared__ __attribute__((aligned(1024))) char k0s[TILE], k1s[TILE], k2s[TILE];
-  __shared__ __attribute__((aligned(1024))) char v0s[TILE], v1s[TILE], v2s[TILE];
+  // ring slots: K tile, then V tile
+  __shared__ __attribute__((aligned(1024))) char sl0[2 * TILE], sl1[2 * TILE], sl2[2 * TILE], sl3[2 * TILE];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -190,7 +217,6 @@ void dq_kernel(const BwdArgs a) {
   const bool row_ok = rin < tile.nrows;
   const int lrow = tile.local0 + rin;
   const int grow = tile.g0 + rin;
-  const int wave_lo = tile.g0 + rsub * 32;
   static_assert(RB * G == 4, "4 waves");
   const const_ptr<SpanRec> spans = scalar_view(a.spans) + steps[0].span_begin;
   const int n_spans = steps[n_steps - 1].span_end - steps[0].span_begin;
@@ -275,84 +301,99 @@ void dq_kernel(const BwdArgs a) {
 #pragma unroll
     for (int t = 0; t < 16; ++t) acc[db][t] = 0.f;
 
-  auto tile_step = [&](const Cursor& c, const char* ks, const char* vs) {
-    f32x16 s[KB], dp[KB];
+  // Scores of a tile: S^T = K Q^T and dP^T = V dO^T (register r of lane
+  // half hh holds key kt + 16 (r / 8) + 8 hh + r % 8 of row ql).
+  auto scores = [&](const char* ks, const char* vs, f32x16& s, f32x16& dp) {
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-      for (int t = 0; t < 16; ++t) {
-        s[kb][t] = 0.f;
-        dp[kb][t] = 0.f;
-      }
-#pragma unroll
-      for (int jj = 0; jj < NQ; ++jj) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(ks + kb * 32 * 256 + kro[jj]);
-        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vs + kb * 32 * 256 + kro[jj]);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[jj], s[kb], 0, 0, 0);
-        dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, df[jj], dp[kb], 0, 0, 0);
-      }
+    for (int t = 0; t < 16; ++t) {
+      s[t] = 0.f;
+      dp[t] = 0.f;
     }
-    // register r of lane half hh holds key kt + 32 kb + 16 (r / 8) + 8 hh + r % 8
-    const bool edge = c.kt < c.k0 || c.kt + BN > c.k1 || c.kt + BN - 1 > wave_lo;
+#pragma unroll
+    for (int jj = 0; jj < NQ; ++jj) {
+      const bf16x8 kf = *reinterpret_cast<const bf16x8*>(ks + kro[jj]);
+      const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vs + kro[jj]);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[jj], s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, df[jj], dp, 0, 0, 0);
+    }
+  };
+  // dS = P (dP - Delta) of a tile, as the bf16 B operands of dQ^T += K^T dS^T
+  auto dscores = [&](const Cursor& c, const f32x16& s, const f32x16& dp, bf16x8 (&dsb)[2]) {
+    // visible keys of this lane's row, as bits relative to kt + 8 hh (in a
+    // tile inside the span and below the wave's first row this is all ones
+    // on the bits the lane uses)
     const int base = c.kt + 8 * hh;
-    const int lo = min(max(c.k0 - base, 0), 64);
-    const int hi = min(max(min(c.k1, grow + 1) - base, 0), 64);
-    const uint64_t below_hi = hi >= 64 ? ~0ull : (1ull << hi) - 1;
-    const uint64_t below_lo = lo >= 64 ? ~0ull : (1ull << lo) - 1;
-    const uint64_t vis = edge ? (below_hi & ~below_lo) : ~0ull;
-    const int w0 = int(uint32_t(vis)), w1 = int(uint32_t(vis >> 32));
-    bf16x8 dsb[KB][2];
+    const int lo = min(max(c.k0 - base, 0), 32);
+    const int hi = min(max(min(c.k1, grow + 1) - base, 0), 32);
+    const uint32_t below_hi = hi >= 32 ? ~0u : (1u << hi) - 1;
+    const uint32_t below_lo = lo >= 32 ? ~0u : (1u << lo) - 1;
+    const int w0 = int(below_hi & ~below_lo);
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = __builtin_amdgcn_sbfe(kb ? w1 : w0, 16 * (r >> 3) + (r & 7), 1);
-        float arg;
-        asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(arg) : "v"(m), "v"(__builtin_fmaf(s[kb][r], c2, -lse2)),
-            "v"(-INFINITY));
-        const float p = __builtin_amdgcn_exp2f(arg);
-        dsb[kb][r >> 3][r & 7] = (__bf16)(p * (dp[kb][r] - dl));
-      }
+    for (int r = 0; r < 16; ++r) {
+      const int m = __builtin_amdgcn_sbfe(w0, 16 * (r >> 3) + (r & 7), 1);
+      float arg;
+      asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(arg) : "v"(m), "v"(__builtin_fmaf(s[r], c2, -lse2)), "v"(-INFINITY));
+      const float p = __builtin_amdgcn_exp2f(arg);
+      dsb[r >> 3][r & 7] = (__bf16)(p * (dp[r] - dl));
+    }
+  };
+  auto dq_update = [&](const char* ks, const bf16x8 (&dsb)[2]) {
 #pragma unroll
     for (int db = 0; db < ND; ++db)
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int sub = 0; sub < 2; ++sub) {
-          const bf16x8 tf = tr_read8(ks + (32 * kb + 16 * sub) * 256, ktr[db]);
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tf, dsb[kb][sub], acc[db], 0, 0, 0);
-        }
+      for (int sub = 0; sub < 2; ++sub) {
+        const bf16x8 tf = tr_read8(ks + 16 * sub * 256, ktr[db]);
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tf, dsb[sub], acc[db], 0, 0, 0);
+      }
   };
 
-  // Ring of three LDS slots: tile t sits in slot t % 3; while tile t is
-  // consumed, tile t + 1 is in flight and tile t + 2 is issued into the slot
-  // tile t - 1 left (every wave finished it before this step's barrier).
+  // Software pipeline over a ring of four LDS slots (tile t in slot t % 4):
+  // step t computes the scores of tile t + 1 while the vector units turn the
+  // scores of tile t into dS, then adds tile t's dQ product. Tiles t + 2 and
+  // t + 3 are in flight meanwhile; tile t + 3 goes into the slot tile t - 1
+  // left (every wave finished it before this step's barrier). Every step
+  // issues a tile -- past the last one the loads cover no bytes and write
+  // zeros into a slot nobody reads again -- so every step waits for the same
+  // count. On the last step the scores read a slot holding no tile; they are
+  // never used. The main loop runs whole groups of four steps with no
+  // condition inside: where paths with different loads in flight merge, the
+  // compiler's own LDS-DMA tracking falls back to waiting for every load.
   Cursor cs, cl;
   start(cs);
   start(cl);
-  issue(cl, k0s, v0s);
-  if (n_tiles > 1) {
-    advance(cl);
-    issue(cl, k1s, v1s);
+  issue(cl, sl0, (sl0 + TILE));
+  advance(cl);
+  issue(cl, sl1, (sl1 + TILE));
+  advance(cl);
+  issue(cl, sl2, (sl2 + TILE));
+  f32x16 s0, d0, s1, d1;
+  __builtin_amdgcn_s_waitcnt(wait_vmcnt(2 * PER_STAGE));
+  asm volatile("s_barrier" ::: "memory");
+  scores(sl0, (sl0 + TILE), s0, d0);
+#define DQ_STEP(T, KC, KN, VN, KL, VL, SC, DC, SN, DN)                \
+  {                                                                   \
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt(PER_STAGE));                \
+    asm volatile("s_barrier" ::: "memory");                           \
+    advance(cl);                                                      \
+    issue(cl, KL, VL);                                                \
+    scores(KN, VN, SN, DN);                                           \
+    bf16x8 dsb[2];                                                    \
+    dscores(cs, SC, DC, dsb);                                         \
+    dq_update(KC, dsb);                                               \
+    schedule_dq_step();                                               \
+    advance(cs);                                                      \
   }
-#define DQ_STEP(T, KC, VC, KN, VN)                           \
-  {                                                          \
-    if ((T) + 1 < n_tiles)                                   \
-      __builtin_amdgcn_s_waitcnt(wait_vmcnt(PER_STAGE));     \
-    else                                                     \
-      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);               \
-    asm volatile("s_barrier" ::: "memory");                  \
-    if ((T) + 2 < n_tiles) {                                 \
-      advance(cl);                                           \
-      issue(cl, KN, VN);                                     \
-    }                                                        \
-    tile_step(cs, KC, VC);                                   \
-    advance(cs);                                             \
+  int t = 0;
+  for (; t + 4 <= n_tiles; t += 4) {
+    DQ_STEP(t, sl0, sl1, (sl1 + TILE), sl3, (sl3 + TILE), s0, d0, s1, d1);
+    DQ_STEP(t + 1, sl1, sl2, (sl2 + TILE), sl0, (sl0 + TILE), s1, d1, s0, d0);
+    DQ_STEP(t + 2, sl2, sl3, (sl3 + TILE), sl1, (sl1 + TILE), s0, d0, s1, d1);
+    DQ_STEP(t + 3, sl3, sl0, (sl0 + TILE), sl2, (sl2 + TILE), s1, d1, s0, d0);
   }
-  for (int t = 0; t < n_tiles; t += 3) {
-    DQ_STEP(t, k0s, v0s, k2s, v2s);
-    if (t + 1 < n_tiles) DQ_STEP(t + 1, k1s, v1s, k0s, v0s);
-    if (t + 2 < n_tiles) DQ_STEP(t + 2, k2s, v2s, k1s, v1s);
+  if (t < n_tiles) {
+    DQ_STEP(t, sl0, sl1, (sl1 + TILE), sl3, (sl3 + TILE), s0, d0, s1, d1);
+    if (t + 1 < n_tiles) DQ_STEP(t + 1, sl1, sl2, (sl2 + TILE), sl0, (sl0 + TILE), s1, d1, s0, d0);
+    if (t + 2 < n_tiles) DQ_STEP(t + 2, sl2, sl3, (sl3 + TILE), sl1, (sl1 + TILE), s0, d0, s1, d1);
   }
 #undef DQ_STEP
 
@@ -370,9 +411,6 @@ void dq_kernel(const BwdArgs a) {
 // ---------------------------------------------------------------- dK / dV
 // s_waitcnt immediate for vmcnt(n) and lgkmcnt(0) together.
 constexpr int wait_vmcnt_lgkm0(int n) { return (wait_vmcnt(n) & ~0x0F00); }
-// __builtin_amdgcn_sched_group_barrier instruction classes
-constexpr int kSchedMfma = 0x0008;
-constexpr int kSchedDsRead = 0x0100;
 // A matrix phase of the dK/dV kernel: 8 product MFMAs (two transposing LDS
 // reads each), then 8 score MFMAs (one LDS read each); every MFMA's reads go
 // out kPhaseAhead MFMAs before it.
