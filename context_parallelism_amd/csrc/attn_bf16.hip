@@ -37,6 +37,7 @@
 // Output per entry: O_s normalised by its own softmax sum (fp32) and
 // lse_s = m_ref/sqrt(D) + ln(sum) (fp32), combined across steps by the LSE
 // merge.
+#include "device_util.h"
 #include "kernels.h"
 
 namespace cpattn {
@@ -359,9 +360,11 @@ void attn_rank_bf16_d128_kernel(const AttnArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   const int grp = wave >> 2, wg = wave & 3;  // waves w and w+4 share a SIMD
   const int hg = blockIdx.x % a.n_hg;
-  const UnitRec unit = a.units[blockIdx.x / a.n_hg];
-  const TileRec tile = a.tiles[unit.tile];
-  const EntryRec* const steps = a.tile_entries + unit.e0;
+  // plan records through scalar views: their loads are scalar, so a wait
+  // for one never waits for the K/V loads in flight
+  const UnitRec unit = scalar_load(a.units, blockIdx.x / a.n_hg);
+  const TileRec tile = scalar_load(a.tiles, unit.tile);
+  const const_ptr<EntryRec> steps = scalar_view(a.tile_entries) + unit.e0;
   const int n_steps = unit.e1 - unit.e0;
   const int h = hg * G + (wg % G);
   const int rsub = grp * RB + wg / G;
@@ -373,7 +376,7 @@ void attn_rank_bf16_d128_kernel(const AttnArgs a) {
   const int grow = tile.g0 + rin;
   const int wave_lo = tile.g0 + rsub * 32;
   // The unit's key spans: every step's spans, contiguous and in step order.
-  const SpanRec* spans = a.spans + steps[0].span_begin;
+  const const_ptr<SpanRec> spans = scalar_view(a.spans) + steps[0].span_begin;
   const int n_spans = steps[n_steps - 1].span_end - steps[0].span_begin;
   // This wave's per-step partial slots (step i at i * kUnitWaves slots).
   float* const part = a.part_o + (int64_t(blockIdx.x) * a.max_steps * kUnitWaves + wave) *

@@ -40,6 +40,7 @@
 //    (bits 2 and 3 of the row swapped). The row blocks stream through a
 //    four-slot LDS ring, two blocks ahead, so no wave waits on memory
 //    inside a step.
+#include "device_util.h"
 #include "kernels.h"
 
 namespace cpattn {
@@ -89,27 +90,6 @@ __device__ inline bf16x8 tr_read8(const char* base, const int (&off)[2]) {
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// Plan records are read through the constant address space so that the
-// uniform loads become scalar loads (counted by lgkmcnt, not by the vmcnt
-// that tracks the LDS-DMA ring).
-template <typename T>
-using const_ptr = const __attribute__((address_space(4))) T*;
-template <typename T>
-__device__ inline const_ptr<T> scalar_view(const T* p) {
-  return (const_ptr<T>)(p);
-}
-// Copy of plan record i (a struct of int32 words) through a scalar view.
-template <typename T>
-__device__ inline T scalar_load(const T* p, int64_t i) {
-  static_assert(sizeof(T) % 4 == 0, "int32 words");
-  const const_ptr<int32_t> q = (const_ptr<int32_t>)(p + i);
-  int32_t w[sizeof(T) / 4];
-#pragma unroll
-  for (size_t k = 0; k < sizeof(T) / 4; ++k) w[k] = q[k];
-  T r;
-  __builtin_memcpy(&r, w, sizeof(T));
-  return r;
-}
 constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
