@@ -538,7 +538,9 @@ void dkdv_kernel(const BwdArgs a) {
     // every row of the block sees every key of the pair unless the block
     // holds a causal edge or a sample boundary; then S = -inf where the key
     // is outside [sample start, row's global id]
-    if (!(blk[2 * rb] <= kw0 && kw0 + 31 <= blk[2 * rb + 1])) {
+    // (both bounds in one 8-byte scalar load, tested without short-circuit)
+    const int64_t bounds = *(const_ptr<int64_t>)(blk + 2 * rb);
+    if (!((int(bounds) <= kw0) & (kw0 + 31 <= int(bounds >> 32)))) {
 #pragma unroll
       for (int run = 0; run < 2; ++run)
 #pragma unroll
