@@ -177,10 +177,11 @@ cp_status cp_attn_rank_fwd(const void *q, const void *k, const void *v, int32_t 
 /*
  * cp_attn_rank_fwd_timed -- cp_attn_rank_fwd that also records six
  * caller-created hipEvent_t on `stream` at its stage boundaries:
- * events[0] before the plan upload, [1] after it, [2] after the gather
- * (which the attention kernels now do as they load Q: [2] follows [1]),
- * [3] after the V relayout (bf16, head_dim 128; otherwise right after [2]),
- * [4] after the per-step attention, [5] after the merge. A caller can then
+ * events[0] before the plan upload, [1] after it, [2] and [3] right after
+ * [1] (the Q gather is done by the attention kernels as they load Q, and V
+ * is read in its own layout, so those two stages are empty), [4] after the
+ * attention, [5] after the merge (right after [4] where the attention
+ * kernel merges the ring steps itself). A caller can then
  * time one stage with hipEventElapsedTime, without a profiler. events may
  * be NULL (then this is exactly cp_attn_rank_fwd), and so may any entry:
  * that boundary is then not recorded (each record costs a few microseconds
