@@ -24,7 +24,7 @@ from typing import List, Optional
 
 import numpy as np
 
-__all__ = ["Workload", "WORKLOADS", "get", "make_inputs", "random_meta"]
+__all__ = ["Workload", "WORKLOADS", "get", "make_inputs", "random_meta", "draw_on_device"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -152,3 +152,23 @@ def random_meta(rng: np.random.Generator, n_samples: int, max_img: int, max_text
     text = lens - n_img
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     return n_img.astype(np.int32), cu
+
+
+def draw_on_device(shapes, seed: int, dtype: str = "bf16", device: str = "cuda:0"):
+    """I.i.d. N(0, 1) tensors of the given shapes for problems too large to
+    draw on the host (several GB each): drawn on ``device`` by torch's
+    generator seeded with ``seed``, in the order given, in fp32, then
+    rounded to bf16 (or kept fp32). A checker reads back only the slices it
+    needs, so both sides still take the same values from here.
+    """
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    dt = torch.float32 if dtype == "f32" else torch.bfloat16
+    out = []
+    for shape in shapes:
+        t = torch.randn(tuple(shape), generator=g, device=device, dtype=torch.float32)
+        out.append(t.to(dt).contiguous())
+        del t
+    return tuple(out)
