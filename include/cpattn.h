@@ -33,8 +33,12 @@
  *   - n_img: int32[n_samples], image-prefix length of each sample,
  *     0 <= n_img[s] <= cu[s+1] - cu[s]. NULL means no image prefix.
  *   - Host pointers are read during the call only; the library keeps no
- *     pointer and holds no global mutable state (calls on different
- *     streams may run concurrently).
+ *     caller pointer. Its only state is one pinned host staging buffer per
+ *     host thread for the plan upload (hipHostMalloc'd on first use, grown
+ *     when a larger plan comes, kept until the process ends); a call waits
+ *     for the previous upload from that buffer before rewriting it. Calls
+ *     from different threads, or on different streams, may run
+ *     concurrently. The library allocates no device memory.
  *   - Errors: every argument is checked before anything is written or
  *     launched; on error nothing is written and a negative status is
  *     returned. No C++ exception crosses this boundary.
@@ -108,8 +112,9 @@ cp_status cp_pair_counts(int64_t seq_len, const int32_t *n_img, const int32_t *c
 /*
  * cp_attn_rank_workspace_size -- bytes of device workspace that
  * cp_attn_rank_fwd needs for these arguments (host only). The workspace
- * holds the uploaded plan, the V^T copy (bf16, head_dim 128), and the
- * per-step partial outputs (fp32) and log-sum-exps.
+ * holds the uploaded plan and the per-step partial outputs (fp32) and
+ * log-sum-exps (bf16 with head_dim 128: one slot per workgroup, ring step
+ * and wave; other paths: [P, R, heads, head_dim] and [P, heads, R]).
  */
 cp_status cp_attn_rank_workspace_size(int64_t seq_len, const int32_t *n_img,
                                       const int32_t *cu_seqlens, int32_t n_samples,
@@ -225,7 +230,6 @@ cp_status cp_lse_merge(const float *part_out, const float *part_lse, const uint3
                        int32_t n_steps, int64_t n_rows, int32_t heads, int32_t head_dim,
                        int32_t dtype, void *out, float *lse, void *stream);
 
-/* Static English text for a status code. */
 /*
  * The same operations with an explicit split (CP_SPLIT_*). An unknown
  * split returns CP_EUNSUPPORTED and writes nothing. Everything else --
@@ -299,6 +303,7 @@ cp_status cp_attn_rank_bwd(const void *q, const void *k, const void *v, const vo
                            int32_t kv_heads, int32_t head_dim, float *dq, float *dk, float *dv,
                            void *workspace, size_t workspace_bytes, void *stream);
 
+/* Static English text for a status code. */
 const char *cp_status_string(cp_status s);
 
 #ifdef __cplusplus
