@@ -102,6 +102,35 @@ def _stream(t) -> int:
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
+def _check_gpu(named, device=None):
+    """Every tensor a contiguous GPU tensor on one device (the kernels take
+    raw pointers: a mismatch here would be an out-of-bounds read there)."""
+    for name, t in named:
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor (the HIP library has no CPU path)")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if device is None:
+            device = t.device
+        elif t.device != device:
+            raise ValueError(f"{name} is on {t.device}, expected {device}")
+    return device
+
+
+def _check_qkv(q, k, v):
+    """q [T,H,D], k and v [T,Hkv,D], one dtype, one device, contiguous (THD)."""
+    _check_gpu((("q", q), ("k", k), ("v", v)))
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share one dtype")
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+        raise ValueError("q, k, v must be 3-D (THD layout)")
+    T, H, D = q.shape
+    Tk, Hkv, Dk = k.shape
+    if tuple(v.shape) != (Tk, Hkv, Dk) or Tk != T or Dk != D:
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    return _dtype_code(q), int(T), int(H), int(Hkv), int(D)
+
+
 class RankAttention:
     """Reusable per-rank forward: plans the sizes once and keeps the output
     and workspace tensors, so repeated calls (benchmarks) allocate nothing."""
@@ -110,20 +139,8 @@ class RankAttention:
                  split: str = "head_tail"):
         import torch
 
-        for name, t in (("q", q), ("k", k), ("v", v)):
-            if not t.is_cuda:
-                raise ValueError(f"{name} must be a GPU tensor (the HIP library has no CPU path)")
-            if not t.is_contiguous():
-                raise ValueError(f"{name} must be contiguous (THD layout)")
-        if not (q.dtype == k.dtype == v.dtype):
-            raise TypeError("q, k, v must share one dtype")
-        self.dtype = _dtype_code(q)
-        T, H, D = q.shape
-        Tk, Hkv, Dk = k.shape
-        if tuple(v.shape) != (Tk, Hkv, Dk) or Tk != T or Dk != D:
-            raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+        self.dtype, self.T, self.H, self.Hkv, self.D = _check_qkv(q, k, v)
         self.q, self.k, self.v = q, k, v
-        self.T, self.H, self.Hkv, self.D = int(T), int(H), int(Hkv), int(D)
         self.cp_size, self.cp_rank = int(cp_size), int(cp_rank)
         self.split = _split_code(split)
         self._keep, self._cu_p, self._img_p, self.n_samples = _meta(n_img, cu_seqlens)
@@ -173,13 +190,8 @@ class RankAttentionBackward:
                  split: str = "head_tail"):
         import torch
 
-        for name, t in (("q", q), ("k", k), ("v", v)):
-            if not t.is_cuda or not t.is_contiguous():
-                raise ValueError(f"{name} must be a contiguous GPU tensor")
-        self.dtype = _dtype_code(q)
+        self.dtype, self.T, self.H, self.Hkv, self.D = _check_qkv(q, k, v)
         self.q, self.k, self.v = q, k, v
-        self.T, self.H, self.D = (int(x) for x in q.shape)
-        self.Hkv = int(k.shape[1])
         self.cp_size, self.cp_rank, self.split = int(cp_size), int(cp_rank), _split_code(split)
         self._keep, self._cu_p, self._img_p, self.n_samples = _meta(n_img, cu_seqlens)
         rows = ctypes.c_int64(0)
@@ -200,9 +212,13 @@ class RankAttentionBackward:
         self.workspace = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=dev)
 
     def __call__(self, out, lse, dout):
-        for name, t in (("out", out), ("lse", lse), ("dout", dout)):
-            if not t.is_cuda or not t.is_contiguous():
-                raise ValueError(f"{name} must be a contiguous GPU tensor")
+        import torch
+
+        _check_gpu((("out", out), ("lse", lse), ("dout", dout)), self.q.device)
+        if out.dtype != self.q.dtype or dout.dtype != self.q.dtype:
+            raise TypeError(f"out and dout must have q's dtype {self.q.dtype}")
+        if lse.dtype != torch.float32:
+            raise TypeError("lse must be float32")
         if tuple(out.shape) != (self.R, self.H, self.D) or tuple(dout.shape) != (self.R, self.H, self.D):
             raise ValueError("out and dout must be [R, heads, head_dim] of this rank")
         if tuple(lse.shape) != (self.H, self.R):
@@ -227,9 +243,11 @@ def gather_rows(src, index):
     """dst[i] = src[index[i]] (0 where index is -1); src a GPU tensor [N, ...]."""
     import torch
 
-    if not src.is_cuda or not src.is_contiguous():
-        raise ValueError("src must be a contiguous GPU tensor")
-    idx = torch.as_tensor(np.asarray(index, dtype=np.int32)).to(src.device)
+    _check_gpu((("src", src),))
+    index = np.asarray(index)
+    if index.size and (int(index.min()) < -1 or int(index.max()) >= src.shape[0]):
+        raise ValueError(f"index values must be -1 or in [0, {src.shape[0]})")
+    idx = torch.as_tensor(index.astype(np.int32)).to(src.device)
     row_elems = int(np.prod(src.shape[1:])) if src.dim() > 1 else 1
     dst = torch.empty((len(idx),) + tuple(src.shape[1:]), dtype=src.dtype, device=src.device)
     check(_lib.cp_gather_rows(src.data_ptr(), _dtype_code(src), src.shape[0], row_elems, idx.data_ptr(),
@@ -242,7 +260,16 @@ def lse_merge(part_out, part_lse, step_mask, out_dtype):
     step_mask uint32-compatible int [R]. Returns (out [R,H,D], lse [H,R])."""
     import torch
 
+    _check_gpu((("part_out", part_out), ("part_lse", part_lse)))
+    if part_out.dtype != torch.float32 or part_lse.dtype != torch.float32:
+        raise TypeError("part_out and part_lse must be float32")
+    if part_out.dim() != 4:
+        raise ValueError("part_out must be [steps, rows, heads, head_dim]")
     S, R, H, D = part_out.shape
+    if tuple(part_lse.shape) != (S, H, R):
+        raise ValueError(f"part_lse must be [{S}, {H}, {R}], not {tuple(part_lse.shape)}")
+    if len(step_mask) != R:
+        raise ValueError(f"step_mask must have {R} entries")
     mask = torch.as_tensor(np.asarray(step_mask, dtype=np.uint32).view(np.int32)).to(part_out.device)
     out = torch.empty((R, H, D), dtype=out_dtype, device=part_out.device)
     lse = torch.empty((H, R), dtype=torch.float32, device=part_out.device)

@@ -301,3 +301,34 @@ def test_ulysses_share_matches_ring_and_oracle(cp):
         d_o = (out[:, :hq].float() - ou[it].float()).abs().max().item()
         d_l = (lse[:hq] - lu[:, it]).abs().max().item()
         assert d_o <= TOL["bf16"][0] and d_l <= TOL["bf16"][1], (r, d_o, d_l)
+
+
+def test_binding_rejects_mismatched_inputs(cp):
+    # the binding hands raw pointers to the kernels: a dtype or shape that
+    # does not match must be refused on the host, before any launch
+    T, H, Hkv, D, P = 300, 4, 2, 128, 2
+    q = torch.zeros(T, H, D, dtype=torch.bfloat16, device=DEV)
+    k = torch.zeros(T, Hkv, D, dtype=torch.bfloat16, device=DEV)
+    v = torch.zeros(T, Hkv, D, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(TypeError):
+        cp.RankAttentionBackward(q.float(), k, v, cp_size=P, cp_rank=0)
+    with pytest.raises(ValueError):
+        cp.RankAttentionBackward(q, k[:-1].contiguous(), v, cp_size=P, cp_rank=0)
+    with pytest.raises(ValueError):
+        cp.RankAttention(q, k, v[:, :1].contiguous(), cp_size=P, cp_rank=0)
+    bw = cp.RankAttentionBackward(q, k, v, cp_size=P, cp_rank=0)
+    out, lse = cp.rank_fwd(q, k, v, cp_size=P, cp_rank=0)
+    with pytest.raises(TypeError):
+        bw(out.float(), lse, out)
+    with pytest.raises(TypeError):
+        bw(out, lse.double(), out)
+    with pytest.raises(ValueError):
+        cp.gather_rows(q, np.array([0, T], np.int32))
+    with pytest.raises(ValueError):
+        cp.gather_rows(q, np.array([-2], np.int32))
+    po = torch.zeros(2, 8, H, D, device=DEV)
+    with pytest.raises(ValueError):
+        cp.lse_merge(po, torch.zeros(2, 8, H, device=DEV), np.zeros(8, np.uint32), torch.bfloat16)
+    with pytest.raises(ValueError):
+        cp.lse_merge(po, torch.zeros(2, H, 8, device=DEV), np.zeros(7, np.uint32), torch.bfloat16)
+    torch.cuda.synchronize()
