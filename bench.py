@@ -483,7 +483,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic_from_profile(),
-                     "kernel": ("attn_rank_bf16_d128_kernel (all ring steps of a row tile per workgroup, LSE merge in-kernel)" if w.head_dim == 128 else "attn_step_bf16_kernel (per-step attention, all ring steps, one launch)")
+                     "kernel": ("attn_rank_bf16_d128_kernel (all ring steps of a row tile per workgroup, one online softmax across them)" if w.head_dim == 128 else "attn_step_bf16_kernel (per-step attention, all ring steps, one launch)")
                                },
     }
     if not args.no_cpu_baseline:

@@ -349,7 +349,6 @@ void attn_rank_bf16_d128_kernel(const AttnArgs a) {
   constexpr int ND = D / 32, NQ = D / 16;
   constexpr int RB = 4 / G;                  // row blocks per wave group
   static_assert(BN == 64, "tile walk assumes 64-key tiles");
-  static_assert(kUnitWaves == 8 && kUnitSlotFloats == (ND * 16 + 1) * 64, "partial slot layout");
   __shared__ __attribute__((aligned(1024))) char k0s[TILE];
   __shared__ __attribute__((aligned(1024))) char k1s[TILE];
   __shared__ __attribute__((aligned(1024))) char v0s[TILE];
@@ -378,16 +377,7 @@ void attn_rank_bf16_d128_kernel(const AttnArgs a) {
   // The unit's key spans: every step's spans, contiguous and in step order.
   const const_ptr<SpanRec> spans = scalar_view(a.spans) + steps[0].span_begin;
   const int n_spans = steps[n_steps - 1].span_end - steps[0].span_begin;
-  // This wave's per-step partial slots (step i at i * kUnitWaves slots).
-  float* const part = a.part_o + (int64_t(blockIdx.x) * a.max_steps * kUnitWaves + wave) *
-                                     int64_t(kUnitSlotFloats) + lane;
-
   auto span_tiles = [&](int i) { return (spans[i].k1 - (spans[i].k0 & ~7) + BN - 1) / BN; };
-  auto step_tiles = [&](int st) {
-    int n = 0;
-    for (int i = steps[st].span_begin; i < steps[st].span_end; ++i) n += span_tiles(i - steps[0].span_begin);
-    return n;
-  };
   int n_tiles = 0;
   for (int i = 0; i < n_spans; ++i) n_tiles += span_tiles(i);
   auto start = [&](TileCursor& c) {
@@ -528,35 +518,7 @@ void attn_rank_bf16_d128_kernel(const AttnArgs a) {
         pb[kb][r >> 3][r & 7] = (__bf16)p;
       }
   };
-  // Ring-step boundaries: the step that owns softmax tile ts, and the tile
-  // where the next step starts.
-  int ts = 0, cur_step = 0, step_end = step_tiles(0);
-  // Close the current step: its partial (output normalised by its own sum,
-  // and lse = m_ref/sqrt(D) + ln(sum)) goes to this wave's slot for the
-  // step, and the running state restarts for the next step.
-  auto end_step = [&]() {
-    const float lt = sum_with_partner(l);
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    float* const slot = part + int64_t(cur_step) * kUnitWaves * kUnitSlotFloats;
-#pragma unroll
-    for (int db = 0; db < ND; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        slot[(db * 16 + r) * 64] = o[db][r] * inv;
-        o[db][r] = 0.f;
-      }
-    slot[ND * 16 * 64] = lt > 0.f ? m_ref * a.scale + logf(lt) : -INFINITY;
-    l = 0.f;
-    m_ref = -INFINITY;
-  };
   auto softmax = [&](const TileCursor& c) {
-    // The previous matrix phase finished the last PV of a step: close it.
-    if (ts == step_end) {
-      end_step();
-      ++cur_step;
-      step_end += step_tiles(cur_step);
-    }
-    ++ts;
     if (c.kt < c.k0 || c.kt + BN > c.k1 || c.kt + BN - 1 > wave_lo) {
       // Keys of this lane sit at offsets 32kb + 16(r>>3) + (r&7) from
       // kt + 8hh; the visible ones form the range [lo, hi). Build that range
@@ -760,35 +722,10 @@ void attn_rank_bf16_d128_kernel(const AttnArgs a) {
           lt > 0.f ? m_ref * a.scale + logf(lt) : -INFINITY;
     return;
   }
-  // LSE merge of the unit's ring steps (Ring Attention's combination of
-  // blockwise results): the last step is still in registers, the others
-  // are in this wave's slots. m = max over steps of lse_s; w_s =
-  // exp(lse_s - m); out = sum_s w_s O_s / sum_s w_s; lse = m + ln sum_s w_s.
-  const float lse_last = lt > 0.f ? m_ref * a.scale + logf(lt) : -INFINITY;
-  float m = lse_last;
-  for (int st = 0; st < n_steps - 1; ++st)
-    m = fmaxf(m, part[int64_t(st) * kUnitWaves * kUnitSlotFloats + ND * 16 * 64]);
-  const float w_last = m == -INFINITY ? 0.f : __expf(lse_last - m);
-  float den = w_last;
-  {
-    const float c = lt > 0.f ? w_last / lt : 0.f;
-#pragma unroll
-    for (int db = 0; db < ND; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[db][r] *= c;
-  }
-  for (int st = 0; st < n_steps - 1; ++st) {
-    const float* slot = part + int64_t(st) * kUnitWaves * kUnitSlotFloats;
-    const float ls = slot[ND * 16 * 64];
-    const float w = m == -INFINITY ? 0.f : __expf(ls - m);
-    den += w;
-#pragma unroll
-    for (int db = 0; db < ND; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[db][r] = __builtin_fmaf(w, slot[(db * 16 + r) * 64], o[db][r]);
-  }
+  // The online softmax ran across every ring step of the unit, so the
+  // running output, sum and reference already merge all steps' blocks.
   if (!row_ok) return;
-  const float inv = den > 0.f ? 1.f / den : 0.f;
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
   __bf16* const po = static_cast<__bf16*>(a.out) + (int64_t(lrow) * a.H + h) * D + 4 * hh;
 #pragma unroll
   for (int db = 0; db < ND; ++db)
@@ -799,7 +736,7 @@ void attn_rank_bf16_d128_kernel(const AttnArgs a) {
                           (__bf16)(o[db][4 * tq + 2] * inv), (__bf16)(o[db][4 * tq + 3] * inv)};
       *reinterpret_cast<bf16x4*>(po + 32 * db + 8 * tq) = val;
     }
-  if (hh == 0) a.lse[int64_t(h) * a.R + lrow] = den > 0.f ? m + logf(den) : -INFINITY;
+  if (hh == 0) a.lse[int64_t(h) * a.R + lrow] = lt > 0.f ? m_ref * a.scale + logf(lt) : -INFINITY;
 }
 
 template <int G>

@@ -115,7 +115,6 @@ cp_status rank_fwd(const void* q, const void* k, const void* v, int32_t dtype, i
     a.units = reinterpret_cast<const UnitRec*>(ws + w.off_units);
     a.out = out;
     a.lse = lse;
-    a.max_steps = cp_size;
     a.R = int32_t(R);
     a.H = heads;
     a.Hkv = kv_heads;

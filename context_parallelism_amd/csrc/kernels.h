@@ -23,7 +23,6 @@ struct AttnArgs {
   const UnitRec* units;          // unit kernel work list
   void* out;                     // [R, H, D] in the input dtype (unit kernel)
   float* lse;                    // [H, R] fp32 (unit kernel)
-  int32_t max_steps;             // P: per-step partial slots per workgroup (unit kernel)
   int32_t per_step;              // unit kernel: units of one step, partials for the merge pass
   int32_t R, H, Hkv;
   int32_t n_hg;          // head groups (workgroups per entry)

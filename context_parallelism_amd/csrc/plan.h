@@ -36,11 +36,6 @@ constexpr int kBlockN = 64;
 constexpr int kBf16Waves = 4;
 constexpr int kBf16WavesD128 = 8;  // two ping-pong groups of four
 constexpr int kF32RowsPerTile = 64;
-// Unit kernel (bf16, head_dim 128): waves per workgroup, and floats of one
-// wave's per-step partial slot (64 output registers and the log-sum-exp,
-// each for 64 lanes).
-constexpr int kUnitWaves = kBf16WavesD128;
-constexpr int kUnitSlotFloats = 65 * 64;
 
 struct TileShape {
   int32_t rows;          // rows per plan tile (bm)

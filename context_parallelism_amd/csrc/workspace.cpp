@@ -59,9 +59,7 @@ int32_t prepare_workspace(int64_t seq_len, const int32_t* n_img, const int32_t* 
   w.plan_bytes = off;
   w.off_po = off;
   if (w.unit_kernel && !w.unit_per_step) {
-    const size_t n_hg = size_t(heads / w.shape.heads_per_wg);
-    off = align256(off + w.plan.units.size() * n_hg * size_t(cp_size) * kUnitWaves *
-                             kUnitSlotFloats * sizeof(float));
+    // one online softmax across all ring steps of a row tile: no partials
     w.off_pl = off;
   } else {
     off = align256(off + size_t(cp_size) * R * size_t(heads) * head_dim * sizeof(float));

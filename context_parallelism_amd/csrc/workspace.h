@@ -2,10 +2,11 @@
 // workspace holds, each region 256-byte aligned:
 //   plan   : index int32[R], step mask uint32[R], tiles, entries, spans,
 //            step-ordered entries, units (uploaded from the host in one copy);
-//   part_o : per-step partial outputs, fp32. Per-step kernels: [P, R, H, D].
-//            Unit kernel (bf16, head_dim 128): one slot per (workgroup, step,
-//            wave) of kUnitSlotFloats, in the wave's own register order;
-//   part_l : per-step log-sum-exps fp32 [P, H, R] (per-step kernels only).
+//   part_o : per-step partial outputs fp32 [P, R, H, D] and
+//   part_l : per-step log-sum-exps fp32 [P, H, R], for the per-step kernels
+//            and the merge pass. The unit kernel (bf16, head_dim 128, large
+//            grids) carries one online softmax across all ring steps of a
+//            row tile and needs neither.
 #pragma once
 
 #include <cstddef>
@@ -22,7 +23,7 @@ struct Workspace {
   int32_t heads = 0, kv_heads = 0, head_dim = 0, dtype = 0;
   size_t off_index = 0, off_mask = 0, off_tiles = 0, off_entries = 0, off_spans = 0;
   size_t off_tile_entries = 0, off_units = 0;
-  bool unit_kernel = false;  // bf16 head_dim 128: units with the in-kernel merge
+  bool unit_kernel = false;  // bf16 head_dim 128: units, one online softmax across the steps
   bool unit_per_step = false;  // ... but one step per unit and the merge pass (small grids)
   const std::vector<UnitRec>& launch_units() const {
     return unit_per_step ? plan.step_units : plan.units;

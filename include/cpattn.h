@@ -112,9 +112,9 @@ cp_status cp_pair_counts(int64_t seq_len, const int32_t *n_img, const int32_t *c
 /*
  * cp_attn_rank_workspace_size -- bytes of device workspace that
  * cp_attn_rank_fwd needs for these arguments (host only). The workspace
- * holds the uploaded plan and the per-step partial outputs (fp32) and
- * log-sum-exps (bf16 with head_dim 128: one slot per workgroup, ring step
- * and wave; other paths: [P, R, heads, head_dim] and [P, heads, R]).
+ * holds the uploaded plan and, where the ring steps are merged in a
+ * separate pass (fp32, head_dim 64, small bf16 grids), the per-step partial
+ * outputs fp32 [P, R, heads, head_dim] and log-sum-exps [P, heads, R].
  */
 cp_status cp_attn_rank_workspace_size(int64_t seq_len, const int32_t *n_img,
                                       const int32_t *cu_seqlens, int32_t n_samples,
@@ -158,10 +158,12 @@ cp_status cp_attn_rank_plan_stats(int64_t seq_len, const int32_t *n_img, const i
  *   4. merge the partials of each row by their log-sum-exp (Ring
  *      Attention's combination of blockwise results).
  * With bf16 and head_dim 128, steps 3 and 4 run in one kernel: a workgroup
- * takes all ring steps of a row tile in order, keeps each step's partial in
- * its own workspace slot and merges them before it writes out and lse.
- * Other dtypes and head_dim 64 write partials for all rows and merge them
- * in a separate pass (cp_lse_merge's kernel).
+ * takes all ring steps of a row tile in order and merges every key block
+ * into one running output by the online-softmax (log-sum-exp) update,
+ * across step boundaries too, so no partial leaves its registers; the
+ * result equals the per-step partials merged by log-sum-exp up to rounding
+ * order. Other dtypes, head_dim 64 and small grids write per-step partials
+ * for all rows and merge them in a separate pass (cp_lse_merge's kernel).
  *
  * q, k, v: device, dtype CP_DTYPE_BF16 or CP_DTYPE_F32, THD layout.
  * out: device [R, heads, head_dim] in dtype; lse: device fp32 [heads, R],
