@@ -619,7 +619,6 @@ void attn_rank_bf16_d128_kernel(const AttnArgs a) {
   // holds up the matrix work. On the last tile the QK^T reads a stale K
   // slot; those scores are never used.
   auto matrix = [&](const char* vb, const char* kb, bool loads, char* kdst, char* vdst) {
-    __builtin_amdgcn_s_setprio(1);  // favour this wave's MFMA issue
     pv(vb);
     qk(kb);
     // LDS reads per MFMA: two for the 16 PV MFMAs (transposing reads), one
@@ -637,7 +636,6 @@ void attn_rank_bf16_d128_kernel(const AttnArgs a) {
         __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
     }
     fence_s();
-    __builtin_amdgcn_s_setprio(0);
   };
 
   if (grp == 0) {
