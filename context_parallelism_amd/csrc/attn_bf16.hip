@@ -294,8 +294,13 @@ void attn_step_bf16_kernel(const AttnArgs a) {
 // ---------------------------------------------------------------------------
 // head_dim 128: ping-pong variant.
 //
-// Work: one workgroup of 8 waves per (row tile, ring step, head group)
-// entry. Waves w and w+4 share a SIMD; waves 0-3 form group 0 and waves
+// Work: one workgroup of 8 waves per (unit, head group), a unit being one
+// row tile with all of its ring steps in step order (or, for small grids,
+// one (row tile, step) entry). The tiles of all the unit's steps run
+// through one online softmax: the running output, sum and reference carry
+// over step boundaries, so the blocks of every step are merged by the
+// log-sum-exp update as they come and no per-step partial leaves the
+// registers. Waves w and w+4 share a SIMD; waves 0-3 form group 0 and waves
 // 4-7 group 1. Each wave owns 32 query rows of one head; with G query heads
 // per KV head (G = 4, 2, 1) a group covers 4/G row blocks of G heads, so the
 // workgroup's 8 waves share every K/V tile.
@@ -574,7 +579,7 @@ void attn_rank_bf16_d128_kernel(const AttnArgs a) {
   // (phase 2j+1), and both groups read it in M(j) (phases 2j+2, 2j+3).
   // The two groups run separate copies of the loop, so neither carries a
   // branch on its group inside a phase. Tiles run through all ring steps of
-  // the unit without a break; a step boundary only closes the step's partial.
+  // the unit without a break: a step boundary is just the next tile.
   TileCursor cs, ck, cv;   // softmax tile; K and V tiles of the last load group
   start(cs);
   start(ck);
