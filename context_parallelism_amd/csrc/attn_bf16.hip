@@ -53,7 +53,7 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int kBufferWord3 = 0x00020000;  // raw buffer access, gfx9 family
 constexpr float kRescaleLog2 = 8.0f;      // lazy-rescale threshold (exp2 domain)
-constexpr int kLdsAhead = 6;             // LDS operand reads issued ahead of their MFMA
+constexpr int kLdsAhead = 4;             // LDS operand reads issued ahead of their MFMA
 constexpr int kWaitVmcnt0 = 0x0F70;       // s_waitcnt vmcnt(0), expcnt and lgkmcnt untouched
 // __builtin_amdgcn_sched_group_barrier instruction classes
 constexpr int kSchedMfma = 0x0008;
