@@ -334,8 +334,8 @@ void attn_step_bf16_kernel(const AttnArgs a) {
 //    while its partner does the vector work.
 //  * Matrix phases read each MFMA operand from LDS kLdsAhead MFMAs ahead,
 //    which hides LDS latency under load; group 0 spreads the next tile's
-//    LDS-DMA loads over its matrix phase, one every four MFMAs, so the
-//    memory queue never stalls the matrix work.
+//    LDS-DMA loads over the QK^T half of its matrix phase, one every other
+//    MFMA, so the memory queue never stalls the matrix work.
 //  * Masks of diagonal and span-edge tiles are built as a 64-bit lane mask
 //    and applied with bitfield selects, keeping scalar registers free.
 // Scalar walk over an entry's 64-key tiles: up to three key spans, each
@@ -620,8 +620,8 @@ void attn_rank_bf16_d128_kernel(const AttnArgs a) {
   };
   // Matrix phase: PV of tile t and QK^T of tile t+1, 32 MFMAs fed by LDS
   // reads issued kLdsAhead MFMAs ahead. With loads, one
-  // LDS-DMA instruction goes out every four MFMAs, so the memory queue never
-  // holds up the matrix work. On the last tile the QK^T reads a stale K
+  // LDS-DMA instruction goes out beside every other QK^T MFMA, so the memory
+  // queue never holds up the matrix work. On the last tile the QK^T reads a stale K
   // slot; those scores are never used.
   auto matrix = [&](const char* vb, const char* kb, bool loads, char* kdst, char* vdst) {
     pv(vb);
@@ -633,7 +633,10 @@ void attn_rank_bf16_d128_kernel(const AttnArgs a) {
     __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * kLdsAhead, 0);
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
-      if (loads && i % (32 / (2 * CH)) == 0) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
+      // the 2 CH loads go out in the QK^T half, beside every other MFMA (the PV
+      // half's transposing reads keep the LDS busier)
+      static_assert(2 * CH == 8, "eight loads per matrix phase");
+      if (loads && i >= 16 && i % 2 == 0) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
       __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
       if (i + kLdsAhead < 16)
         __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
