@@ -28,7 +28,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0
 METRIC = "useful causal attn TFLOP/s per CP-rank share (1 GPU) + % of bf16 MFMA peak"
-PMC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_text64k_r3_pmc.json")
+PMC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_text64k_rank3_pmc.json")
 ATTN_SRC = os.path.join(ROOT, "context_parallelism_amd", "csrc", "attn_bf16.hip")
 
 
