@@ -128,17 +128,21 @@ def unit_mode(request, monkeypatch):
     return request.param
 
 
-@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
-def test_small_all_ranks(cp, case, unit_mode):
+# bf16 head_dim 128 runs in both modes; the other shapes have per-step
+# kernels only
+SMALL_MODES = [(c, m) for c in SMALL for m in (("units", "steps") if (c[7] == "bf16" and c[5] == 128) else ("units",))]
+
+
+@pytest.mark.parametrize("case,mode", SMALL_MODES, ids=[f"{c[0]}-{m}" for c, m in SMALL_MODES])
+def test_small_all_ranks(cp, case, mode, monkeypatch):
     name, n_img, text, H, Hkv, D, P, dtype = case
-    if unit_mode == "steps" and not (dtype == "bf16" and D == 128):
-        pytest.skip("one mode only: per-step kernels")
+    monkeypatch.setenv("CPATTN_UNIT_MIN_WORKGROUPS", "0" if mode == "units" else "1000000000")
     lens = np.array(n_img) + np.array(text)
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     T = int(cu[-1])
     q, k, v = draw(zlib.crc32(name.encode()) % 1000, T, H, Hkv, D, dtype)
     for r in range(P):
-        run_case(cp, q, k, v, np.array(n_img, np.int32), cu, P, r, dtype, what=f"{name} r={r} {unit_mode}")
+        run_case(cp, q, k, v, np.array(n_img, np.int32), cu, P, r, dtype, what=f"{name} r={r} {mode}")
 
 
 CONTIGUOUS = [
