@@ -15,6 +15,9 @@ from ._lib import (  # noqa: F401
     CP_EUNSUPPORTED,
     CP_MAX_CP_SIZE,
     CP_OK,
+    CP_SCHED_AUTO,
+    CP_SCHED_PER_STEP,
+    CP_SCHED_ROW_TILE,
     CP_SPLIT_CONTIGUOUS,
     CP_SPLIT_HEAD_TAIL,
     LIB_PATH,
@@ -40,6 +43,7 @@ from ._lib import (  # noqa: F401
     load,
 )
 from .api import (  # noqa: F401
+    SCHEDULES,
     SPLITS,
     RankAttention,
     RankAttentionBackward,

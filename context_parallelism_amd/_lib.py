@@ -22,6 +22,9 @@ CP_DTYPE_BF16 = 1
 CP_MAX_CP_SIZE = 32
 CP_SPLIT_HEAD_TAIL = 0
 CP_SPLIT_CONTIGUOUS = 1
+CP_SCHED_AUTO = 0
+CP_SCHED_ROW_TILE = 1
+CP_SCHED_PER_STEP = 2
 
 # (name, restype, argtypes) for every entry point declared in include/cpattn.h
 _P32 = POINTER(c_int32)
@@ -50,13 +53,14 @@ SIGNATURES = [
     ("cp_pair_counts_ex", c_int32, [c_int64, _P32, _P32, c_int32, c_int32, c_int32, c_int32, _P64, _P64]),
     ("cp_attn_rank_workspace_size_ex", c_int32,
      [c_int64, _P32, _P32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32,
-      POINTER(c_size_t)]),
+      c_int32, POINTER(c_size_t)]),
     ("cp_attn_rank_plan_stats_ex", c_int32,
      [c_int64, _P32, _P32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32,
       _P64, _P64, _P64, _P64, _P64]),
     ("cp_attn_rank_fwd_ex", c_int32,
      [c_void_p, c_void_p, c_void_p, c_int32, c_int64, _P32, _P32, c_int32, c_int32, c_int32, c_int32,
-      c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p, POINTER(c_void_p)]),
+      c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p,
+      POINTER(c_void_p)]),
     ("cp_attn_rank_bwd_workspace_size", c_int32,
      [c_int64, _P32, _P32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32,
       POINTER(c_size_t)]),

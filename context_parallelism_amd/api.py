@@ -12,16 +12,24 @@ from typing import Optional, Sequence, Tuple
 import numpy as np
 
 from . import _lib
-from ._lib import CP_DTYPE_BF16, CP_DTYPE_F32, CP_SPLIT_CONTIGUOUS, CP_SPLIT_HEAD_TAIL, check
+from ._lib import (CP_DTYPE_BF16, CP_DTYPE_F32, CP_SCHED_AUTO, CP_SCHED_PER_STEP, CP_SCHED_ROW_TILE,
+                   CP_SPLIT_CONTIGUOUS, CP_SPLIT_HEAD_TAIL, check)
 
 _I32P = ctypes.POINTER(ctypes.c_int32)
 SPLITS = {"head_tail": CP_SPLIT_HEAD_TAIL, "contiguous": CP_SPLIT_CONTIGUOUS}
+SCHEDULES = {"auto": CP_SCHED_AUTO, "row_tile": CP_SCHED_ROW_TILE, "per_step": CP_SCHED_PER_STEP}
 
 
 def _split_code(split) -> int:
     if split not in SPLITS:
         raise ValueError(f"split must be one of {sorted(SPLITS)}, not {split!r}")
     return SPLITS[split]
+
+
+def _schedule_code(schedule) -> int:
+    if schedule not in SCHEDULES:
+        raise ValueError(f"schedule must be one of {sorted(SCHEDULES)}, not {schedule!r}")
+    return SCHEDULES[schedule]
 
 
 def _meta(n_img, cu_seqlens):
@@ -61,12 +69,13 @@ def pair_counts(seq_len: int, n_img=None, cu_seqlens=None, *, cp_size: int, cp_r
 
 
 def workspace_size(seq_len: int, n_img=None, cu_seqlens=None, *, cp_size: int, cp_rank: int,
-                   heads: int, kv_heads: int, head_dim: int, dtype: int, split: str = "head_tail") -> int:
+                   heads: int, kv_heads: int, head_dim: int, dtype: int, split: str = "head_tail",
+                   schedule: str = "auto") -> int:
     keep, cu_p, img_p, n = _meta(n_img, cu_seqlens)
     b = ctypes.c_size_t(0)
     check(_lib.cp_attn_rank_workspace_size_ex(seq_len, img_p, cu_p, n, cp_size, cp_rank,
-                                              _split_code(split), heads, kv_heads, head_dim, dtype,
-                                              ctypes.byref(b)),
+                                              _split_code(split), _schedule_code(schedule), heads,
+                                              kv_heads, head_dim, dtype, ctypes.byref(b)),
           "cp_attn_rank_workspace_size_ex")
     return b.value
 
@@ -132,17 +141,19 @@ def _check_qkv(q, k, v):
 
 
 class RankAttention:
-    """Reusable per-rank forward: plans the sizes once and keeps the output
-    and workspace tensors, so repeated calls (benchmarks) allocate nothing."""
+    """Reusable per-rank forward: sizes the outputs and the workspace once
+    and keeps those tensors, so repeated calls (benchmarks) allocate nothing.
+    ``schedule``: "auto", "row_tile" or "per_step" (CP_SCHED_*)."""
 
     def __init__(self, q, k, v, *, cp_size: int, cp_rank: int, n_img=None, cu_seqlens=None,
-                 split: str = "head_tail"):
+                 split: str = "head_tail", schedule: str = "auto"):
         import torch
 
         self.dtype, self.T, self.H, self.Hkv, self.D = _check_qkv(q, k, v)
         self.q, self.k, self.v = q, k, v
         self.cp_size, self.cp_rank = int(cp_size), int(cp_rank)
         self.split = _split_code(split)
+        self.schedule = _schedule_code(schedule)
         self._keep, self._cu_p, self._img_p, self.n_samples = _meta(n_img, cu_seqlens)
         rows = ctypes.c_int64(0)
         check(_lib.cp_partition_index_ex(self.T, self._img_p, self._cu_p, self.n_samples, self.cp_size,
@@ -151,7 +162,8 @@ class RankAttention:
         self.R = rows.value
         self.ws_bytes = workspace_size(self.T, self._keep[1], self._keep[0], cp_size=self.cp_size,
                                        cp_rank=self.cp_rank, heads=self.H, kv_heads=self.Hkv,
-                                       head_dim=self.D, dtype=self.dtype, split=split)
+                                       head_dim=self.D, dtype=self.dtype, split=split,
+                                       schedule=schedule)
         dev = q.device
         self.out = torch.empty((self.R, self.H, self.D), dtype=q.dtype, device=dev)
         self.lse = torch.empty((self.H, self.R), dtype=torch.float32, device=dev)
@@ -168,17 +180,17 @@ class RankAttention:
             ev = (ctypes.c_void_p * 6)(*[ctypes.c_void_p(int(e) if e else None) for e in events])
         check(_lib.cp_attn_rank_fwd_ex(self.q.data_ptr(), self.k.data_ptr(), self.v.data_ptr(), self.dtype,
                                        self.T, self._img_p, self._cu_p, self.n_samples, self.cp_size,
-                                       self.cp_rank, self.split, self.H, self.Hkv, self.D,
-                                       self.out.data_ptr(), self.lse.data_ptr(), self.workspace.data_ptr(),
+                                       self.cp_rank, self.split, self.schedule, self.H, self.Hkv,
+                                       self.D, self.out.data_ptr(), self.lse.data_ptr(), self.workspace.data_ptr(),
                                        self.ws_bytes, _stream(self.q), ev), "cp_attn_rank_fwd_ex")
         return self.out, self.lse
 
 
 def rank_fwd(q, k, v, *, cp_size: int, cp_rank: int, n_img=None, cu_seqlens=None,
-             split: str = "head_tail"):
+             split: str = "head_tail", schedule: str = "auto"):
     """Per-rank forward attention. Returns (out [R,H,D] in q.dtype, lse fp32 [H,R])."""
     return RankAttention(q, k, v, cp_size=cp_size, cp_rank=cp_rank, n_img=n_img,
-                         cu_seqlens=cu_seqlens, split=split)()
+                         cu_seqlens=cu_seqlens, split=split, schedule=schedule)()
 
 
 class RankAttentionBackward:

@@ -21,7 +21,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libcpattn.so")
 
 # Plain C++ (no HIP headers): the planner and the host-only entry points.
-HOST_SOURCES = ["plan.cpp", "workspace.cpp", "capi_host.cpp"]
+HOST_SOURCES = ["plan.cpp", "workspace.cpp", "capi_host.cpp", "plan_check.cpp"]
 # Compiled as HIP for gfx950.
 DEVICE_SOURCES = ["capi.cpp", "gather.hip", "attn_bf16.hip", "attn_bwd.hip", "attn_bwd_generic.hip", "attn_f32.hip",
                   "lse_merge.hip"]

@@ -72,13 +72,13 @@ inline hipError_t mark(void* const* events, int i, hipStream_t s) {
 
 cp_status rank_fwd(const void* q, const void* k, const void* v, int32_t dtype, int64_t seq_len,
                    const int32_t* n_img, const int32_t* cu_seqlens, int32_t n_samples,
-                   int32_t cp_size, int32_t cp_rank, int32_t split, int32_t heads,
+                   int32_t cp_size, int32_t cp_rank, int32_t split, int32_t schedule, int32_t heads,
                    int32_t kv_heads, int32_t head_dim, void* out, float* lse, void* workspace,
                    size_t workspace_bytes, void* stream, void* const* events) {
   try {
     Workspace w;
     int32_t st = prepare_workspace(seq_len, n_img, cu_seqlens, n_samples, cp_size, cp_rank, heads,
-                                   kv_heads, head_dim, dtype, w, split);
+                                   kv_heads, head_dim, dtype, w, split, schedule);
     if (st != CP_OK) return st;
     const int64_t R = w.meta.rows;
     if (R == 0) return CP_OK;
@@ -250,8 +250,8 @@ cp_status cp_attn_rank_fwd(const void* q, const void* k, const void* v, int32_t 
                            int32_t kv_heads, int32_t head_dim, void* out, float* lse,
                            void* workspace, size_t workspace_bytes, void* stream) {
   return rank_fwd(q, k, v, dtype, seq_len, n_img, cu_seqlens, n_samples, cp_size, cp_rank,
-                  CP_SPLIT_HEAD_TAIL, heads, kv_heads, head_dim, out, lse, workspace, workspace_bytes,
-                  stream, nullptr);
+                  CP_SPLIT_HEAD_TAIL, CP_SCHED_AUTO, heads, kv_heads, head_dim, out, lse, workspace,
+                  workspace_bytes, stream, nullptr);
 }
 
 cp_status cp_attn_rank_fwd_timed(const void* q, const void* k, const void* v, int32_t dtype,
@@ -261,18 +261,19 @@ cp_status cp_attn_rank_fwd_timed(const void* q, const void* k, const void* v, in
                                  float* lse, void* workspace, size_t workspace_bytes,
                                  void* stream, void* const* events) {
   return rank_fwd(q, k, v, dtype, seq_len, n_img, cu_seqlens, n_samples, cp_size, cp_rank,
-                  CP_SPLIT_HEAD_TAIL, heads, kv_heads, head_dim, out, lse, workspace, workspace_bytes,
-                  stream, events);
+                  CP_SPLIT_HEAD_TAIL, CP_SCHED_AUTO, heads, kv_heads, head_dim, out, lse, workspace,
+                  workspace_bytes, stream, events);
 }
 
 cp_status cp_attn_rank_fwd_ex(const void* q, const void* k, const void* v, int32_t dtype,
                               int64_t seq_len, const int32_t* n_img, const int32_t* cu_seqlens,
                               int32_t n_samples, int32_t cp_size, int32_t cp_rank, int32_t split,
-                              int32_t heads, int32_t kv_heads, int32_t head_dim, void* out,
-                              float* lse, void* workspace, size_t workspace_bytes, void* stream,
-                              void* const* events) {
+                              int32_t schedule, int32_t heads, int32_t kv_heads, int32_t head_dim,
+                              void* out, float* lse, void* workspace, size_t workspace_bytes,
+                              void* stream, void* const* events) {
   return rank_fwd(q, k, v, dtype, seq_len, n_img, cu_seqlens, n_samples, cp_size, cp_rank, split,
-                  heads, kv_heads, head_dim, out, lse, workspace, workspace_bytes, stream, events);
+                  schedule, heads, kv_heads, head_dim, out, lse, workspace, workspace_bytes, stream,
+                  events);
 }
 
 cp_status cp_gather_rows(const void* src, int32_t dtype, int64_t src_rows, int64_t row_elems,

@@ -46,13 +46,13 @@ cp_status cp_pair_counts_ex(int64_t seq_len, const int32_t* n_img, const int32_t
 cp_status cp_attn_rank_workspace_size_ex(int64_t seq_len, const int32_t* n_img,
                                          const int32_t* cu_seqlens, int32_t n_samples,
                                          int32_t cp_size, int32_t cp_rank, int32_t split,
-                                         int32_t heads, int32_t kv_heads, int32_t head_dim,
-                                         int32_t dtype, size_t* bytes) {
+                                         int32_t schedule, int32_t heads, int32_t kv_heads,
+                                         int32_t head_dim, int32_t dtype, size_t* bytes) {
   if (bytes == nullptr) return CP_EINVAL;
   try {
     Workspace w;
     int32_t st = prepare_workspace(seq_len, n_img, cu_seqlens, n_samples, cp_size, cp_rank, heads,
-                                   kv_heads, head_dim, dtype, w, split);
+                                   kv_heads, head_dim, dtype, w, split, schedule);
     if (st != CP_OK) return st;
     *bytes = w.total;
     return CP_OK;
@@ -70,7 +70,7 @@ cp_status cp_attn_rank_plan_stats_ex(int64_t seq_len, const int32_t* n_img,
   try {
     Workspace w;
     int32_t st = prepare_workspace(seq_len, n_img, cu_seqlens, n_samples, cp_size, cp_rank, heads,
-                                   kv_heads, head_dim, dtype, w, split);
+                                   kv_heads, head_dim, dtype, w, split, CP_SCHED_AUTO);
     if (st != CP_OK) return st;
     const Plan& p = w.plan;
     std::vector<int64_t> per_step(size_t(cp_size), 0);
@@ -121,7 +121,8 @@ cp_status cp_attn_rank_workspace_size(int64_t seq_len, const int32_t* n_img,
                                       int32_t kv_heads, int32_t head_dim, int32_t dtype,
                                       size_t* bytes) {
   return cp_attn_rank_workspace_size_ex(seq_len, n_img, cu_seqlens, n_samples, cp_size, cp_rank,
-                                        CP_SPLIT_HEAD_TAIL, heads, kv_heads, head_dim, dtype, bytes);
+                                        CP_SPLIT_HEAD_TAIL, CP_SCHED_AUTO, heads, kv_heads, head_dim,
+                                        dtype, bytes);
 }
 
 cp_status cp_attn_rank_plan_stats(int64_t seq_len, const int32_t* n_img, const int32_t* cu_seqlens,

@@ -1,9 +1,11 @@
 #include "workspace.h"
 
-#include <cstdlib>
 #include <cstring>
 
 #include "cpattn.h"
+#ifdef CPATTN_CHECK_PLANS
+#include "plan_check.h"
+#endif
 
 namespace cpattn {
 
@@ -11,22 +13,18 @@ namespace {
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 }  // namespace
 
-int64_t unit_min_workgroups() {
-  const char* env = std::getenv("CPATTN_UNIT_MIN_WORKGROUPS");
-  if (env == nullptr || *env == 0) return kUnitMinWorkgroups;
-  char* end = nullptr;
-  const long long v = std::strtoll(env, &end, 10);
-  return (end != env && v >= 0) ? int64_t(v) : kUnitMinWorkgroups;
-}
-
-
 int32_t prepare_workspace(int64_t seq_len, const int32_t* n_img, const int32_t* cu_seqlens,
                           int32_t n_samples, int32_t cp_size, int32_t cp_rank, int32_t heads,
                           int32_t kv_heads, int32_t head_dim, int32_t dtype, Workspace& w,
-                          int32_t split) {
+                          int32_t split, int32_t schedule) {
   if (dtype != CP_DTYPE_F32 && dtype != CP_DTYPE_BF16) return CP_EUNSUPPORTED;
   if (heads < 1 || kv_heads < 1 || heads % kv_heads != 0) return CP_EINVAL;
   if (head_dim != 64 && head_dim != 128) return CP_EUNSUPPORTED;
+  if (schedule != CP_SCHED_AUTO && schedule != CP_SCHED_ROW_TILE && schedule != CP_SCHED_PER_STEP)
+    return CP_EUNSUPPORTED;
+  // one online softmax across the steps exists for bf16 head_dim 128 only
+  const bool has_row_tile = dtype == CP_DTYPE_BF16 && head_dim == 128;
+  if (schedule == CP_SCHED_ROW_TILE && !has_row_tile) return CP_EUNSUPPORTED;
   int32_t st = build_meta(seq_len, n_img, cu_seqlens, n_samples, cp_size, cp_rank, w.meta, split);
   if (st != CP_OK) return st;
   w.heads = heads;
@@ -35,6 +33,10 @@ int32_t prepare_workspace(int64_t seq_len, const int32_t* n_img, const int32_t* 
   w.dtype = dtype;
   w.shape = tile_shape(dtype, heads / kv_heads, head_dim);
   build_plan(w.meta, w.shape.rows, kBlockN, w.plan);
+#ifdef CPATTN_CHECK_PLANS
+  st = check_plan(w.meta, w.plan);
+  if (st != CP_OK) return st;
+#endif
   const size_t R = size_t(w.meta.rows);
   size_t off = 0;
   w.off_index = off;
@@ -49,10 +51,11 @@ int32_t prepare_workspace(int64_t seq_len, const int32_t* n_img, const int32_t* 
   off = align256(off + w.plan.spans.size() * sizeof(SpanRec));
   w.off_tile_entries = off;
   off = align256(off + w.plan.tile_entries.size() * sizeof(EntryRec));
-  w.unit_kernel = dtype == CP_DTYPE_BF16 && head_dim == 128;
+  w.unit_kernel = has_row_tile;
   if (w.unit_kernel) {
     const int64_t n_hg = heads / w.shape.heads_per_wg;
-    w.unit_per_step = int64_t(w.plan.units.size()) * n_hg < unit_min_workgroups();
+    w.unit_per_step = schedule == CP_SCHED_PER_STEP ||
+                      (schedule == CP_SCHED_AUTO && int64_t(w.plan.units.size()) * n_hg < kUnitMinWorkgroups);
   }
   w.off_units = off;
   off = align256(off + w.launch_units().size() * sizeof(UnitRec));
@@ -109,6 +112,10 @@ int32_t prepare_bwd_workspace(int64_t seq_len, const int32_t* n_img, const int32
   }
   w.n_hg = heads / w.heads_per_wg;
   build_bwd_plan(w.meta, w.rows_per_tile, w.plan);
+#ifdef CPATTN_CHECK_PLANS
+  st = check_bwd_plan(w.meta, w.plan);
+  if (st != CP_OK) return st;
+#endif
   const Plan& p = w.plan.rows;
   const size_t R = size_t(w.meta.rows);
   size_t off = 0;

@@ -32,19 +32,18 @@ struct Workspace {
   size_t off_po = 0, off_pl = 0, total = 0;
 };
 
-// Below this many workgroups the unit kernel takes one ring step per unit
-// (more, smaller workgroups) and the steps are merged in a separate pass:
-// two workgroups per compute unit of a 256-CU MI355X. The environment
-// variable CPATTN_UNIT_MIN_WORKGROUPS overrides it (read at every call; the
-// tests use it to run small problems through both modes).
+// Under CP_SCHED_AUTO, below this many workgroups the unit kernel takes
+// one ring step per unit (more, smaller workgroups) and the steps are
+// merged in a separate pass: two workgroups per compute unit of a 256-CU
+// MI355X.
 constexpr int64_t kUnitMinWorkgroups = 512;
-int64_t unit_min_workgroups();
 
 // Checks every argument, builds the plan and the layout. Returns a cp_status.
+// schedule: CP_SCHED_AUTO, CP_SCHED_ROW_TILE or CP_SCHED_PER_STEP.
 int32_t prepare_workspace(int64_t seq_len, const int32_t* n_img, const int32_t* cu_seqlens,
                           int32_t n_samples, int32_t cp_size, int32_t cp_rank, int32_t heads,
                           int32_t kv_heads, int32_t head_dim, int32_t dtype, Workspace& w,
-                          int32_t split = 0);
+                          int32_t split, int32_t schedule);
 
 // Backward workspace, each region 256-byte aligned:
 //   plan  : index int32[R], dQ row tiles, spans, step-ordered entries, units,

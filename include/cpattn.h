@@ -81,6 +81,25 @@ enum { CP_DTYPE_F32 = 0, CP_DTYPE_BF16 = 1 };
 enum { CP_SPLIT_HEAD_TAIL = 0, CP_SPLIT_CONTIGUOUS = 1 };
 
 /*
+ * How the ring steps of a rank's rows are laid over workgroups (the
+ * schedule argument of cp_attn_rank_workspace_size_ex and
+ * cp_attn_rank_fwd_ex). Both give the same rows up to floating-point
+ * rounding order (the log-sum-exp merge is an exact refactoring of the
+ * softmax, Ring Attention's blockwise combination).
+ *   CP_SCHED_ROW_TILE: one workgroup takes every ring step of a row tile
+ *     in order and carries one online softmax across them; no per-step
+ *     partial is written. bf16 with head_dim 128 only.
+ *   CP_SCHED_PER_STEP: one workgroup per (row tile, ring step); each writes
+ *     its step's partial output and log-sum-exp into the workspace, and a
+ *     second pass merges them. The only schedule of fp32 and head_dim 64.
+ *   CP_SCHED_AUTO: ROW_TILE where it exists and the grid has at least 512
+ *     workgroups (two per compute unit of a 256-CU MI355X), else PER_STEP.
+ * The entry points without the suffix use CP_SCHED_AUTO. ROW_TILE for a
+ * dtype/head_dim that has no such kernel returns CP_EUNSUPPORTED.
+ */
+enum { CP_SCHED_AUTO = 0, CP_SCHED_ROW_TILE = 1, CP_SCHED_PER_STEP = 2 };
+
+/*
  * cp_partition_index -- rows of one CP rank (host only, integer, exact).
  *
  * Page section 1.1 (chunks [cp_rank, 2*cp_size-cp_rank-1]), section 4.1
@@ -233,12 +252,13 @@ cp_status cp_lse_merge(const float *part_out, const float *part_lse, const uint3
                        int32_t dtype, void *out, float *lse, void *stream);
 
 /*
- * The same operations with an explicit split (CP_SPLIT_*). An unknown
- * split returns CP_EUNSUPPORTED and writes nothing. Everything else --
- * arguments, layouts, errors -- is as for the entry point without the
- * suffix; cp_attn_rank_fwd_ex also takes the optional six events of
- * cp_attn_rank_fwd_timed (NULL: none). A workspace sized for one split is
- * not valid for the other.
+ * The same operations with an explicit split (CP_SPLIT_*) and, for the
+ * workspace size and the forward, an explicit schedule (CP_SCHED_*). An
+ * unknown split or schedule returns CP_EUNSUPPORTED and writes nothing.
+ * Everything else -- arguments, layouts, errors -- is as for the entry
+ * point without the suffix; cp_attn_rank_fwd_ex also takes the optional six
+ * events of cp_attn_rank_fwd_timed (NULL: none). A workspace sized for one
+ * (split, schedule) is valid only for that pair.
  */
 cp_status cp_partition_index_ex(int64_t seq_len, const int32_t *n_img, const int32_t *cu_seqlens,
                                 int32_t n_samples, int32_t cp_size, int32_t cp_rank, int32_t split,
@@ -250,7 +270,7 @@ cp_status cp_pair_counts_ex(int64_t seq_len, const int32_t *n_img, const int32_t
 cp_status cp_attn_rank_workspace_size_ex(int64_t seq_len, const int32_t *n_img,
                                          const int32_t *cu_seqlens, int32_t n_samples,
                                          int32_t cp_size, int32_t cp_rank, int32_t split,
-                                         int32_t heads, int32_t kv_heads, int32_t head_dim,
+                                         int32_t schedule, int32_t heads, int32_t kv_heads, int32_t head_dim,
                                          int32_t dtype, size_t *bytes);
 cp_status cp_attn_rank_plan_stats_ex(int64_t seq_len, const int32_t *n_img,
                                      const int32_t *cu_seqlens, int32_t n_samples, int32_t cp_size,
@@ -261,9 +281,9 @@ cp_status cp_attn_rank_plan_stats_ex(int64_t seq_len, const int32_t *n_img,
 cp_status cp_attn_rank_fwd_ex(const void *q, const void *k, const void *v, int32_t dtype,
                               int64_t seq_len, const int32_t *n_img, const int32_t *cu_seqlens,
                               int32_t n_samples, int32_t cp_size, int32_t cp_rank, int32_t split,
-                              int32_t heads, int32_t kv_heads, int32_t head_dim, void *out,
-                              float *lse, void *workspace, size_t workspace_bytes, void *stream,
-                              void *const *events);
+                              int32_t schedule, int32_t heads, int32_t kv_heads, int32_t head_dim,
+                              void *out, float *lse, void *workspace, size_t workspace_bytes,
+                              void *stream, void *const *events);
 
 /*
  * cp_attn_rank_bwd -- gradients of one CP rank's attention share.

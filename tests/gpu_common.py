@@ -53,3 +53,13 @@ def compare(out_gpu, lse_gpu, out_ref, lse_ref, dtype: str, what: str):
 
 def oracle_rows(q, k, v, n_img, cu, P, r, rows=None, split="head_tail"):
     return oracle.rank_attention(q, k, v, n_img, cu, P, r, local_rows=rows, split=split)
+
+
+def pooled_oracle(q, k, v, n_img, cu, P, r, rows=None, heads=None, split="head_tail", stats=None):
+    """The oracle's rank rows (all, or the local rows ``rows``) for the query
+    heads ``heads`` (all if None), computed by threads of this process over
+    (KV group, 128-row) tasks; see oracle.pool."""
+    from oracle.pool import rank_attention_pooled
+
+    return rank_attention_pooled(q, k, v, n_img, cu, P, r, local_rows=rows, split=split, heads=heads,
+                                 executor="thread", row_chunk=128, stats=stats)

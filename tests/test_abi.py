@@ -144,6 +144,34 @@ def test_schedule_covers_every_visible_pair_once(cp, dtype):
     assert st["step_pairs"][1:] == [2 * c * c] * (w.cp_size - 1)
 
 
+def test_schedule_argument(cp):
+    # CP_SCHED_*: the per-step schedule holds the step partials in the
+    # workspace, the row-tile schedule only the plan; row tiles exist for
+    # bf16 head_dim 128 only; unknown values are refused and write nothing
+    kw = dict(cp_size=4, cp_rank=1, heads=8, kv_heads=2, head_dim=128)
+    row = cp.workspace_size(5000, dtype=1, schedule="row_tile", **kw)
+    step = cp.workspace_size(5000, dtype=1, schedule="per_step", **kw)
+    auto = cp.workspace_size(5000, dtype=1, **kw)
+    R, H, D, P = 2 * 625, 8, 128, 4
+    assert step - row >= P * R * H * D * 4 + P * H * R * 4
+    assert auto == step  # 10 row tiles x 4 head groups is below 512 workgroups
+    for dtype, hd in ((0, 128), (1, 64), (0, 64)):
+        with pytest.raises(cp.CpError) as e:
+            cp.workspace_size(5000, dtype=dtype, schedule="row_tile", **dict(kw, head_dim=hd))
+        assert e.value.status == cp.CP_EUNSUPPORTED
+        assert cp.workspace_size(5000, dtype=dtype, schedule="per_step", **dict(kw, head_dim=hd)) == \
+            cp.workspace_size(5000, dtype=dtype, **dict(kw, head_dim=hd))
+    b = ctypes.c_size_t(12345)
+    st = cp.cp_attn_rank_workspace_size_ex(5000, None, None, 1, 4, 1, 0, 3, 8, 2, 128, 1, ctypes.byref(b))
+    assert st == cp.CP_EUNSUPPORTED and b.value == 12345
+    fake = ctypes.c_void_p(4096)
+    st = cp.cp_attn_rank_fwd_ex(fake, fake, fake, 1, 5000, None, None, 1, 4, 1, 0, 3, 8, 2, 128, fake, fake,
+                                ctypes.c_void_p(1 << 20), 1 << 30, None, None)
+    assert st == cp.CP_EUNSUPPORTED
+    with pytest.raises(ValueError):
+        cp.workspace_size(5000, dtype=1, schedule="rows", **kw)
+
+
 def test_workspace_size_grows_with_problem(cp):
     a = cp.workspace_size(1000, cp_size=2, cp_rank=0, heads=4, kv_heads=4, head_dim=128, dtype=1)
     b = cp.workspace_size(2000, cp_size=2, cp_rank=0, heads=4, kv_heads=4, head_dim=128, dtype=1)

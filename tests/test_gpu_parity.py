@@ -1,10 +1,13 @@
 """GPU parity: the HIP library (through the C ABI) against the fp64 oracle.
 
-Small problems are compared on every output; the five workloads at full
-size are compared on sampled rows (both ends of every run of rows, pads,
-random rows) plus whole-output properties (pad rows exact, no NaN,
-determinism, image rows identical across ranks, reassembly over ranks).
+Small problems, and workloads 2, 3 and 5 at full size, are compared on
+every output element. Workload 4 (64K tokens) is compared on every row for
+one query head of each KV group, and on sampled rows (both ends of every
+run of rows, random rows) for all heads. Whole-output properties are
+checked too: pad rows exact, no row left unwritten, determinism, image rows
+identical across ranks, reassembly over ranks.
 """
+import ctypes
 import zlib
 
 import numpy as np
@@ -14,7 +17,7 @@ import torch
 import oracle
 import workloads
 
-from gpu_common import TOL, compare, oracle_rows, sample_rows
+from gpu_common import TOL, compare, oracle_rows, pooled_oracle, sample_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -38,11 +41,12 @@ def draw(seed, T, H, Hkv, D, dtype, q_scale=1.0):
     return [torch.from_numpy(a).to(dt) for a in (q, k, v)]
 
 
-def run_case(cp, q, k, v, n_img, cu, P, r, dtype, rows=None, what="", split="head_tail"):
+def run_case(cp, q, k, v, n_img, cu, P, r, dtype, rows=None, what="", split="head_tail",
+             schedule="auto"):
     print(f"case {what} T={q.shape[0]} H={q.shape[1]} Hkv={k.shape[1]} D={q.shape[2]} P={P} r={r} "
-          f"dtype={dtype} split={split}", flush=True)
+          f"dtype={dtype} split={split} schedule={schedule}", flush=True)
     out, lse = cp.rank_fwd(q.to(DEV), k.to(DEV), v.to(DEV), cp_size=P, cp_rank=r, n_img=n_img,
-                           cu_seqlens=cu, split=split)
+                           cu_seqlens=cu, split=split, schedule=schedule)
     torch.cuda.synchronize()
     if rows is None:
         ro, rl = oracle_rows(q, k, v, n_img, cu, P, r, split=split)
@@ -116,33 +120,39 @@ SMALL = [
     ("bf16-P8-short", [0, 3], [9, 100], 2, 2, 128, 8, "bf16"),
     ("bf16-P32-gqa4", [0], [3000], 4, 1, 128, 32, "bf16"),
     ("bf16-gqa3", [11], [900], 6, 2, 128, 3, "bf16"),
+    # head_dim 64 with 2 and 4 query heads per KV head in one workgroup
+    ("bf16-d64-gqa2-image", [23], [700], 4, 2, 64, 3, "bf16"),
+    ("bf16-d64-gqa4-image", [50], [400], 4, 1, 64, 4, "bf16"),
+    ("bf16-d64-gqa4-packed", [9, 0, 40], [300, 77, 500], 8, 2, 64, 2, "bf16"),
+    ("bf16-d64-gqa2-packed", [0, 17], [130, 260], 8, 4, 64, 3, "bf16"),
 ]
 
 
-@pytest.fixture(params=["units", "steps"])
-def unit_mode(request, monkeypatch):
-    # bf16 head_dim 128 runs whole row tiles per workgroup with the merge in
-    # the kernel, or -- below a workgroup count -- one ring step per
-    # workgroup and a merge pass; small problems are run through both
-    monkeypatch.setenv("CPATTN_UNIT_MIN_WORKGROUPS", "0" if request.param == "units" else "1000000000")
-    return request.param
+def schedules_of(dtype, head_dim):
+    """bf16 head_dim 128 has both schedules (whole row tiles with the merge in
+    the kernel, or one ring step per workgroup and a merge pass); the other
+    shapes have the per-step kernels only."""
+    return ("row_tile", "per_step") if (dtype == "bf16" and head_dim == 128) else ("per_step",)
 
 
-# bf16 head_dim 128 runs in both modes; the other shapes have per-step
-# kernels only
-SMALL_MODES = [(c, m) for c in SMALL for m in (("units", "steps") if (c[7] == "bf16" and c[5] == 128) else ("units",))]
+def with_schedules(cases):
+    pairs = [(c, m) for c in cases for m in schedules_of(c[7], c[5])]
+    return pairs, [f"{c[0]}-{m}" for c, m in pairs]
 
 
-@pytest.mark.parametrize("case,mode", SMALL_MODES, ids=[f"{c[0]}-{m}" for c, m in SMALL_MODES])
-def test_small_all_ranks(cp, case, mode, monkeypatch):
+SMALL_SCHED, SMALL_IDS = with_schedules(SMALL)
+
+
+@pytest.mark.parametrize("case,schedule", SMALL_SCHED, ids=SMALL_IDS)
+def test_small_all_ranks(cp, case, schedule):
     name, n_img, text, H, Hkv, D, P, dtype = case
-    monkeypatch.setenv("CPATTN_UNIT_MIN_WORKGROUPS", "0" if mode == "units" else "1000000000")
     lens = np.array(n_img) + np.array(text)
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     T = int(cu[-1])
     q, k, v = draw(zlib.crc32(name.encode()) % 1000, T, H, Hkv, D, dtype)
     for r in range(P):
-        run_case(cp, q, k, v, np.array(n_img, np.int32), cu, P, r, dtype, what=f"{name} r={r} {mode}")
+        run_case(cp, q, k, v, np.array(n_img, np.int32), cu, P, r, dtype, what=f"{name} r={r}",
+                 schedule=schedule)
 
 
 CONTIGUOUS = [
@@ -150,10 +160,11 @@ CONTIGUOUS = [
     ("contig-bf16-packed", [21, 0, 40], [700, 90, 333], 8, 2, 128, 4, "bf16"),
     ("contig-bf16-d64", [0], [500], 4, 4, 64, 2, "bf16"),
 ]
+CONTIG_SCHED, CONTIG_IDS = with_schedules(CONTIGUOUS)
 
 
-@pytest.mark.parametrize("case", CONTIGUOUS, ids=[c[0] for c in CONTIGUOUS])
-def test_contiguous_split_all_ranks(cp, case, unit_mode):
+@pytest.mark.parametrize("case,schedule", CONTIG_SCHED, ids=CONTIG_IDS)
+def test_contiguous_split_all_ranks(cp, case, schedule):
     # the plain P-way split (section 1.1's unbalanced baseline) through the same kernels
     name, n_img, text, H, Hkv, D, P, dtype = case
     lens = np.array(n_img) + np.array(text)
@@ -161,14 +172,65 @@ def test_contiguous_split_all_ranks(cp, case, unit_mode):
     T = int(cu[-1])
     q, k, v = draw(zlib.crc32(name.encode()) % 1000, T, H, Hkv, D, dtype)
     for r in range(P):
-        run_case(cp, q, k, v, np.array(n_img, np.int32), cu, P, r, dtype, what=f"{name} r={r} {unit_mode}",
-                 split="contiguous")
+        run_case(cp, q, k, v, np.array(n_img, np.int32), cu, P, r, dtype, what=f"{name} r={r}",
+                 split="contiguous", schedule=schedule)
 
 
-def test_peaky_softmax(cp, unit_mode):
+@pytest.mark.parametrize("schedule", ["row_tile", "per_step"])
+def test_peaky_softmax(cp, schedule):
     q, k, v = draw(5, 700, 4, 4, 128, "bf16", q_scale=8.0)
     for r in range(2):
-        run_case(cp, q, k, v, None, None, 2, r, "bf16", what=f"peaky r={r}")
+        run_case(cp, q, k, v, None, None, 2, r, "bf16", what=f"peaky r={r}", schedule=schedule)
+
+
+def test_row_tile_schedule_is_refused_where_it_does_not_exist(cp):
+    q = torch.zeros(64, 2, 64, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(cp.CpError):
+        cp.rank_fwd(q, q, q, cp_size=2, cp_rank=0, schedule="row_tile")
+    q = torch.zeros(64, 2, 128, dtype=torch.float32, device=DEV)
+    with pytest.raises(cp.CpError):
+        cp.rank_fwd(q, q, q, cp_size=2, cp_rank=0, schedule="row_tile")
+
+
+def test_unsuffixed_entry_points_on_device(cp):
+    # cp_attn_rank_fwd and cp_attn_rank_fwd_timed (NULL events) called
+    # directly with device pointers: every rank of an image + packed GQA
+    # problem against the oracle, and bit-identical to the _ex entry point
+    # with the default split and schedule
+    n_img = np.array([31, 0, 12], np.int32)
+    text = [400, 95, 611]
+    cu = np.concatenate([[0], np.cumsum(n_img + np.array(text))]).astype(np.int32)
+    T, H, Hkv, D, P = int(cu[-1]), 8, 2, 128, 3
+    q, k, v = draw(77, T, H, Hkv, D, "bf16")
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    I32 = ctypes.POINTER(ctypes.c_int32)
+    cu_p, img_p = cu.ctypes.data_as(I32), n_img.ctypes.data_as(I32)
+    stream = torch.cuda.current_stream().cuda_stream
+    for r in range(P):
+        rows = ctypes.c_int64(0)
+        cp.check(cp.cp_partition_index(T, img_p, cu_p, 3, P, r, None, 0, ctypes.byref(rows), None),
+                 "cp_partition_index")
+        R = rows.value
+        ws_bytes = ctypes.c_size_t(0)
+        cp.check(cp.cp_attn_rank_workspace_size(T, img_p, cu_p, 3, P, r, H, Hkv, D, cp.CP_DTYPE_BF16,
+                                                ctypes.byref(ws_bytes)), "cp_attn_rank_workspace_size")
+        ws = torch.empty(max(ws_bytes.value, 256), dtype=torch.uint8, device=DEV)
+        outs = []
+        for fn in ("plain", "timed"):
+            out = torch.full((R, H, D), float("nan"), dtype=torch.bfloat16, device=DEV)
+            lse = torch.full((H, R), float("nan"), dtype=torch.float32, device=DEV)
+            args = (qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), cp.CP_DTYPE_BF16, T, img_p, cu_p, 3, P, r,
+                    H, Hkv, D, out.data_ptr(), lse.data_ptr(), ws.data_ptr(), ws_bytes.value, stream)
+            st = cp.cp_attn_rank_fwd(*args) if fn == "plain" else cp.cp_attn_rank_fwd_timed(*args, None)
+            cp.check(st, "cp_attn_rank_fwd")
+            torch.cuda.synchronize()
+            outs.append((out, lse))
+        ro, rl = oracle_rows(q, k, v, n_img, cu, P, r)
+        compare(outs[0][0], outs[0][1], ro, rl, "bf16", f"cp_attn_rank_fwd r={r}")
+        ex_out, ex_lse = cp.rank_fwd(qd, kd, vd, cp_size=P, cp_rank=r, n_img=n_img, cu_seqlens=cu)
+        torch.cuda.synchronize()
+        for out, lse in outs:
+            assert torch.equal(out, ex_out) and torch.equal(lse, ex_lse)
 
 
 def test_empty_input(cp):
@@ -188,15 +250,14 @@ def workload_inputs(num, device=None):
     return w, workloads.make_inputs(w, device=device)
 
 
-def test_workload2_both_unit_modes_agree(cp, monkeypatch):
-    # the two bf16 head_dim-128 modes on one full-size share: same rows to
+def test_workload2_both_schedules_agree(cp):
+    # the two bf16 head_dim-128 schedules on one full-size share: same rows to
     # within the bf16 bound, pads identical
     w, (q, k, v) = workload_inputs(2)
     qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
     res = []
-    for val in ("0", "1000000000"):
-        monkeypatch.setenv("CPATTN_UNIT_MIN_WORKGROUPS", val)
-        out, lse = cp.rank_fwd(qd, kd, vd, cp_size=w.cp_size, cp_rank=1)
+    for schedule in ("row_tile", "per_step"):
+        out, lse = cp.rank_fwd(qd, kd, vd, cp_size=w.cp_size, cp_rank=1, schedule=schedule)
         torch.cuda.synchronize()
         res.append((out.float().cpu(), lse.cpu()))
     assert (res[0][0] - res[1][0]).abs().max().item() <= TOL["bf16"][0]
@@ -209,34 +270,78 @@ def test_workload1_full(cp):
         run_case(cp, q, k, v, None, None, w.cp_size, r, w.dtype, what=f"w1 r={r}")
 
 
-@pytest.mark.parametrize("num", [2, 3, 4, 5])
-def test_workload_sampled(cp, num):
-    w, (q, k, v) = workload_inputs(num)
-    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+def run_workload_share(cp, num, r, q, k, v, qd, kd, vd):
+    """One rank share of a workload in bench's launch configuration (the
+    default split and schedule), with whole-output checks: every row
+    written (NaN canary), pad rows exact, bit-identical on repeat."""
+    w = workloads.get(num)
     cu = w.cu_seqlens if w.n_samples > 1 else None
     n_img = w.n_img_array if any(w.n_img) else None
+    idx, cu_rows = oracle.partition_index(w.seq_len, n_img, cu, w.cp_size, r)
+    ra = cp.RankAttention(qd, kd, vd, cp_size=w.cp_size, cp_rank=r, n_img=n_img, cu_seqlens=cu)
+    ra.out.fill_(float("nan"))  # canary: every row must be overwritten
+    ra.lse.fill_(float("nan"))
+    out, lse = ra()
+    torch.cuda.synchronize()
+    assert not torch.isnan(out).any() and not torch.isnan(lse).any()
+    pads = torch.as_tensor(idx < 0, device=DEV)
+    if pads.any():
+        assert torch.all(out[pads] == 0) and torch.all(torch.isneginf(lse[:, pads]))
+    assert torch.isfinite(lse[:, ~pads]).all()
+    out1, lse1 = out.clone(), lse.clone()
+    out2, lse2 = ra()  # determinism: bit-identical repeat
+    torch.cuda.synchronize()
+    assert torch.equal(out1, out2) and torch.equal(lse1, lse2)
+    return out1, lse1, idx, cu_rows, n_img, cu
+
+
+@pytest.mark.parametrize("num", [2, 3, 5])
+def test_workload_full(cp, num):
+    # every row, every head, every element against the fp64 oracle
+    w, (q, k, v) = workload_inputs(num)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
     for r in w.ranks:
-        idx, cu_rows = oracle.partition_index(w.seq_len, n_img, cu, w.cp_size, r)
-        rows = sample_rows(idx, cu_rows, 96, seed=num * 10 + r)
-        print(f"workload {num} rank {r}: {len(rows)} sampled rows of {len(idx)}", flush=True)
-        ra = cp.RankAttention(qd, kd, vd, cp_size=w.cp_size, cp_rank=r, n_img=n_img, cu_seqlens=cu)
-        ra.out.fill_(float("nan"))  # canary: every row must be overwritten
-        ra.lse.fill_(float("nan"))
-        out, lse = ra()
-        torch.cuda.synchronize()
-        assert not torch.isnan(out).any() and not torch.isnan(lse).any()
-        pads = torch.as_tensor(idx < 0, device=DEV)
-        if pads.any():
-            assert torch.all(out[pads] == 0) and torch.all(torch.isneginf(lse[:, pads]))
-        assert torch.isfinite(lse[:, ~pads]).all()
-        out1, lse1 = out.clone(), lse.clone()
-        out2, lse2 = ra()  # determinism: bit-identical repeat
-        torch.cuda.synchronize()
-        assert torch.equal(out1, out2) and torch.equal(lse1, lse2)
-        ro, rl = oracle_rows(q, k, v, n_img, cu, w.cp_size, r, rows)
-        rt = torch.as_tensor(rows, device=DEV)
-        eo, el = compare(out1[rt], lse1[:, rt], ro, rl, w.dtype, f"workload {num} r={r}")
-        print(f"workload {num} rank {r}: max-abs out {eo:.3e} lse {el:.3e}", flush=True)
+        out, lse, idx, _, n_img, cu = run_workload_share(cp, num, r, q, k, v, qd, kd, vd)
+        print(f"workload {num} rank {r}: GPU done, oracle on all {len(idx)} rows x {w.heads} heads",
+              flush=True)
+        st = {}
+        ro, rl = pooled_oracle(q, k, v, n_img, cu, w.cp_size, r, stats=st)
+        eo, el = compare(out, lse, ro, rl, w.dtype, f"workload {num} r={r}")
+        print(f"workload {num} rank {r}: max-abs out {eo:.3e} lse {el:.3e} "
+              f"(oracle {st['wall_s']:.1f} s on {st['workers']} threads)", flush=True)
+
+
+def test_workload4_every_row_one_head_per_kv_group(cp):
+    # 64K tokens: every row for one query head of each of the 8 KV groups,
+    # at every position inside the group (heads 0, 5, 10, 15, 16, 21, 26, 31)
+    num = 4
+    w, (q, k, v) = workload_inputs(num)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    G = w.heads // w.kv_heads
+    heads = [g * G + (g % G) for g in range(w.kv_heads)]
+    r = w.rank
+    out, lse, idx, _, n_img, cu = run_workload_share(cp, num, r, q, k, v, qd, kd, vd)
+    print(f"workload 4 rank {r}: GPU done, oracle on all {len(idx)} rows of heads {heads}", flush=True)
+    st = {}
+    ro, rl = pooled_oracle(q, k, v, n_img, cu, w.cp_size, r, heads=heads, stats=st)
+    ht = torch.as_tensor(heads, device=DEV)
+    eo, el = compare(out[:, ht], lse[ht], ro, rl, w.dtype, f"workload 4 r={r} heads {heads}")
+    print(f"workload 4 rank {r}: max-abs out {eo:.3e} lse {el:.3e} "
+          f"(oracle {st['wall_s']:.1f} s on {st['workers']} threads)", flush=True)
+
+
+def test_workload4_sampled_rows_all_heads(cp):
+    num = 4
+    w, (q, k, v) = workload_inputs(num)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    r = w.rank
+    out, lse, idx, cu_rows, n_img, cu = run_workload_share(cp, num, r, q, k, v, qd, kd, vd)
+    rows = sample_rows(idx, cu_rows, 96, seed=num * 10 + r)
+    print(f"workload 4 rank {r}: {len(rows)} sampled rows of {len(idx)}, all heads", flush=True)
+    ro, rl = pooled_oracle(q, k, v, n_img, cu, w.cp_size, r, rows=rows)
+    rt = torch.as_tensor(rows, device=DEV)
+    eo, el = compare(out[rt], lse[:, rt], ro, rl, w.dtype, f"workload 4 r={r}")
+    print(f"workload 4 rank {r}: max-abs out {eo:.3e} lse {el:.3e}", flush=True)
 
 
 def test_workload3_image_rows_identical_across_ranks(cp):

@@ -381,6 +381,98 @@ def test_pads_only_at_text_end():
     assert list(idx1) == [0, 1, 5, 6, 7, 8, 9, 10]
 
 
+def owner_partition(seq_len, n_img, cu, P, r):
+    """The rank's rows by a second formulation that does not reshape or
+    select: text offset t of a sample (pads included, t < 2P*c) lies in
+    chunk k = t // c, and head-tail pairing gives chunk k to rank
+    min(k, 2P - 1 - k). Rank r keeps the offsets it owns in increasing
+    order (its chunk r comes before its chunk 2P-1-r), after the image."""
+    ids = []
+    for s in range(len(cu) - 1):
+        a, b, n = int(cu[s]), int(cu[s + 1]), int(n_img[s])
+        T = b - a - n
+        c = -(-T // (2 * P))
+        ids += list(range(a, a + n))
+        for t in range(2 * P * c):
+            k = t // c
+            if min(k, 2 * P - 1 - k) == r:
+                ids.append(a + n + t if t < T else -1)
+    return np.array(ids, dtype=np.int64)
+
+
+def test_partition_equals_owner_formulation():
+    # context-parallel multimodal page, section 1.1 (head-tail pairing) and
+    # 5.3 (per sample): the reshape-and-select partition equals the owner rule
+    rng = np.random.default_rng(17)
+    for trial in range(150):
+        n = int(rng.integers(1, 5))
+        n_img, cu = workloads.random_meta(rng, n, 9, 60)
+        T = int(cu[-1])
+        P = int(rng.integers(1, 7))
+        for r in range(P):
+            idx, _ = oracle.partition_index(T, n_img, cu, P, r)
+            assert np.array_equal(idx, owner_partition(T, n_img, cu, P, r)), (trial, P, r)
+    for w in workloads.WORKLOADS.values():
+        idx, _ = oracle.partition_index(w.seq_len, w.n_img_array, w.cu_seqlens, w.cp_size, w.rank)
+        assert np.array_equal(idx, owner_partition(w.seq_len, w.n_img_array, w.cu_seqlens, w.cp_size, w.rank))
+
+
+def test_real_pairs_are_padded_minus_pad_rows():
+    # pad rows count n_img + t + 1 pairs in the padded total (t its text
+    # offset) and none in the real one; offsets come from the owner rule
+    rng = np.random.default_rng(19)
+    for trial in range(150):
+        n = int(rng.integers(1, 5))
+        n_img, cu = workloads.random_meta(rng, n, 9, 60)
+        T = int(cu[-1])
+        P = int(rng.integers(1, 7))
+        for r in range(P):
+            padded, real = oracle.pair_counts(T, n_img, cu, P, r)
+            pad_terms = 0
+            for s in range(n):
+                a, b, ni = int(cu[s]), int(cu[s + 1]), int(n_img[s])
+                Ts = b - a - ni
+                c = -(-Ts // (2 * P))
+                for t in range(Ts, 2 * P * c):  # the pads sit at the end of the text
+                    k = t // c
+                    if min(k, 2 * P - 1 - k) == r:
+                        pad_terms += ni + t + 1
+            assert real == padded - pad_terms, (trial, P, r)
+
+
+# Per-head pair counts of the five synthetic workloads, written out as
+# integers from the per-sample closed form (image rows n(n+1)/2, text rows
+# against the image 2cn, text rows 2Pc^2 + c) -- not from the oracle.
+#   1: text 256, P=2, c=64:                 2*2*64^2 + 64            = 16,448
+#   2: text 8192, P=4, c=1024:              2*4*1024^2 + 1024        = 8,389,632
+#   3: image 2304 + text 16384, P=4, c=2048:
+#      2304*2305/2 + 2*2048*2304 + 2*4*2048^2 + 2048                 = 45,649,024
+#   4: text 65536, P=8, c=4096:             2*8*4096^2 + 4096        = 268,439,552
+#   5: 8 samples (seed 1005), P=4: the sum of the closed form over samples
+#      = 60,919,305 padded on every rank; rank 0 holds every pad row, so
+#      its real count is lower: 60,648,617.
+PAIR_LITERALS = {1: 16_448, 2: 8_389_632, 3: 45_649_024, 4: 268_439_552, 5: 60_919_305}
+ROW_LITERALS = {1: 128, 2: 2_048, 3: 6_400, 4: 8_192, 5: 23_094}
+
+
+def test_pair_count_literals():
+    for num, want in PAIR_LITERALS.items():
+        w = workloads.get(num)
+        for r in range(w.cp_size):
+            padded, real = oracle.pair_counts(w.seq_len, w.n_img_array, w.cu_seqlens, w.cp_size, r)
+            assert padded == want, (num, r)
+            if num != 5 or r != 0:
+                assert real == padded, (num, r)
+            idx, _ = oracle.partition_index(w.seq_len, w.n_img_array, w.cu_seqlens, w.cp_size, r)
+            assert len(idx) == ROW_LITERALS[num], (num, r)
+    w = workloads.get(5)
+    assert oracle.pair_counts(w.seq_len, w.n_img_array, w.cu_seqlens, w.cp_size, 0)[1] == 60_648_617
+    # the workload-5 lengths these literals were worked out for
+    assert list(w.n_img) == [1320, 2232, 1445, 1306, 2055, 773, 1169, 1916]
+    assert list(w.text_len) == [2553, 7766, 3813, 5971, 7177, 8049, 3044, 5100]
+    assert list(w.cu_seqlens) == [0, 3873, 13871, 19129, 26406, 35638, 44460, 48673, 55689]
+
+
 def test_pair_counts_brute_force_and_closed_form():
     assert pin_pair_counts() == 0
 
