@@ -14,6 +14,7 @@ from ._lib import (  # noqa: F401
     CP_ENOSPC,
     CP_EUNSUPPORTED,
     CP_MAX_CP_SIZE,
+    CP_NOALLOC_SCRATCH_BYTES,
     CP_OK,
     CP_SCHED_AUTO,
     CP_SCHED_PER_STEP,
@@ -28,6 +29,7 @@ from ._lib import (  # noqa: F401
     cp_attn_rank_bwd_workspace_size,
     cp_attn_rank_fwd,
     cp_attn_rank_fwd_ex,
+    cp_attn_rank_fwd_noalloc,
     cp_attn_rank_fwd_timed,
     cp_attn_rank_plan_stats,
     cp_attn_rank_plan_stats_ex,

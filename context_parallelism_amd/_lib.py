@@ -25,6 +25,7 @@ CP_SPLIT_CONTIGUOUS = 1
 CP_SCHED_AUTO = 0
 CP_SCHED_ROW_TILE = 1
 CP_SCHED_PER_STEP = 2
+CP_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 # (name, restype, argtypes) for every entry point declared in include/cpattn.h
 _P32 = POINTER(c_int32)
@@ -45,6 +46,9 @@ SIGNATURES = [
     ("cp_attn_rank_fwd_timed", c_int32,
      [c_void_p, c_void_p, c_void_p, c_int32, c_int64, _P32, _P32, c_int32, c_int32, c_int32,
       c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p, POINTER(c_void_p)]),
+    ("cp_attn_rank_fwd_noalloc", c_int32,
+     [c_void_p, c_void_p, c_void_p, c_int32, c_int64, _P32, _P32, c_int32, c_int32, c_int32,
+      c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p]),
     ("cp_gather_rows", c_int32, [c_void_p, c_int32, c_int64, c_int64, c_void_p, c_int64, c_void_p, c_void_p]),
     ("cp_lse_merge", c_int32,
      [c_void_p, c_void_p, c_void_p, c_int32, c_int64, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p]),
@@ -123,6 +127,7 @@ cp_attn_rank_workspace_size = _fn("cp_attn_rank_workspace_size")
 cp_attn_rank_plan_stats = _fn("cp_attn_rank_plan_stats")
 cp_attn_rank_fwd = _fn("cp_attn_rank_fwd")
 cp_attn_rank_fwd_timed = _fn("cp_attn_rank_fwd_timed")
+cp_attn_rank_fwd_noalloc = _fn("cp_attn_rank_fwd_noalloc")
 cp_gather_rows = _fn("cp_gather_rows")
 cp_lse_merge = _fn("cp_lse_merge")
 cp_partition_index_ex = _fn("cp_partition_index_ex")

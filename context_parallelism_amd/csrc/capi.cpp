@@ -5,6 +5,8 @@
 #include <cmath>
 #include <cstring>
 #include <exception>
+#include <mutex>
+#include <vector>
 
 #include "cpattn.h"
 #include "kernels.h"
@@ -70,6 +72,100 @@ inline hipError_t mark(void* const* events, int i, hipStream_t s) {
   return (events && events[i]) ? hipEventRecord(static_cast<hipEvent_t>(events[i]), s) : hipSuccess;
 }
 
+// How the plan reaches the device workspace.
+enum class Upload {
+  kPinnedStaging,  // the thread's pinned staging buffer, asynchronous
+  kHeapWait,       // ordinary host memory, and the call waits for the copy (allocates no pinned memory)
+};
+
+// Plan on the host, then copy it into the device workspace `ws` on `s`.
+hipError_t upload_plan(const Workspace& w, uint8_t* ws, hipStream_t s, Upload mode) {
+  if (mode == Upload::kPinnedStaging)
+    return stage_and_upload(w.plan_bytes, [&](uint8_t* dst) { pack_plan(w, dst); }, ws, s);
+  std::vector<uint8_t> host(w.plan_bytes);
+  pack_plan(w, host.data());
+  hipError_t e = hipMemcpyAsync(ws, host.data(), w.plan_bytes, hipMemcpyHostToDevice, s);
+  if (e != hipSuccess) return e;
+  // `host` is freed on return: wait until the copy has read it
+  return hipStreamSynchronize(s);
+}
+
+// Argument checks shared by the forward entry points (after the plan is
+// built); the workspace pointer is checked by the caller.
+cp_status check_fwd_pointers(const void* q, const void* k, const void* v, const void* out, const float* lse) {
+  if (!q || !k || !v || !out || !lse) return CP_EINVAL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(lse, 4))
+    return CP_EINVAL;
+  return CP_OK;
+}
+
+// Upload the plan of `w` into `ws` and launch the forward's kernels on `s`.
+cp_status run_fwd(const Workspace& w, const void* q, const void* k, const void* v, int32_t dtype,
+                  int32_t cp_size, int32_t heads, int32_t kv_heads, int32_t head_dim, void* out,
+                  float* lse, uint8_t* ws, hipStream_t s, void* const* events, Upload mode) {
+  const int64_t R = w.meta.rows;
+  if (mark(events, 0, s) != hipSuccess) return CP_EHIP;
+  if (upload_plan(w, ws, s, mode) != hipSuccess) return CP_EHIP;
+  if (mark(events, 1, s) != hipSuccess) return CP_EHIP;
+  // The attention kernels read each row tile's Q rows in place (a tile is
+  // a run of consecutive global ids), so the gather has no pass of its own.
+  const int32_t* index = reinterpret_cast<const int32_t*>(ws + w.off_index);
+  if (mark(events, 2, s) != hipSuccess) return CP_EHIP;
+
+  AttnArgs a;
+  // (no V relayout: the bf16 head_dim-128 kernel reads V tiles row-major
+  // and transposes them in its LDS reads)
+  if (mark(events, 3, s) != hipSuccess) return CP_EHIP;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.part_o = reinterpret_cast<float*>(ws + w.off_po);
+  a.part_lse = reinterpret_cast<float*>(ws + w.off_pl);
+  a.tiles = reinterpret_cast<const TileRec*>(ws + w.off_tiles);
+  a.entries = reinterpret_cast<const EntryRec*>(ws + w.off_entries);
+  a.spans = reinterpret_cast<const SpanRec*>(ws + w.off_spans);
+  a.tile_entries = reinterpret_cast<const EntryRec*>(ws + w.off_tile_entries);
+  a.units = reinterpret_cast<const UnitRec*>(ws + w.off_units);
+  a.out = out;
+  a.lse = lse;
+  a.R = int32_t(R);
+  a.H = heads;
+  a.Hkv = kv_heads;
+  a.group = heads / kv_heads;
+  a.n_hg = heads / w.shape.heads_per_wg;
+  a.scale = float(1.0 / std::sqrt(double(head_dim)));
+  a.scale_log2 = float(1.4426950408889634 / std::sqrt(double(head_dim)));
+  const int n_entries = int(w.plan.entries.size());
+  a.per_step = w.unit_per_step ? 1 : 0;
+  if (w.unit_kernel && !w.unit_per_step) {
+    // all ring steps of a row tile in one workgroup, merged in the kernel
+    if (launch_attn_bf16_units(a, w.shape.heads_per_wg, int(w.plan.units.size()), s) != hipSuccess)
+      return CP_EHIP;
+    if (w.plan.pad_rows > 0 &&
+        launch_fill_pad_rows(index, R, heads, head_dim, dtype, out, lse, s) != hipSuccess)
+      return CP_EHIP;
+    if (mark(events, 4, s) != hipSuccess) return CP_EHIP;
+    if (mark(events, 5, s) != hipSuccess) return CP_EHIP;
+    return CP_OK;
+  }
+  // per-step partials for the merge pass: small bf16 head_dim-128 grids
+  // (unit kernel, one step per unit), head_dim 64, fp32
+  hipError_t e = w.unit_kernel
+                     ? launch_attn_bf16_units(a, w.shape.heads_per_wg, int(w.plan.step_units.size()), s)
+                 : dtype == CP_DTYPE_BF16
+                     ? launch_attn_bf16(a, head_dim, w.shape.heads_per_wg, n_entries, s)
+                     : launch_attn_f32(a, head_dim, n_entries, s);
+  if (e != hipSuccess) return CP_EHIP;
+  if (mark(events, 4, s) != hipSuccess) return CP_EHIP;
+
+  const uint32_t* mask = reinterpret_cast<const uint32_t*>(ws + w.off_mask);
+  if (launch_lse_merge(a.part_o, a.part_lse, mask, cp_size, R, heads, head_dim, dtype, out, lse, s) !=
+      hipSuccess)
+    return CP_EHIP;
+  if (mark(events, 5, s) != hipSuccess) return CP_EHIP;
+  return CP_OK;
+}
+
 cp_status rank_fwd(const void* q, const void* k, const void* v, int32_t dtype, int64_t seq_len,
                    const int32_t* n_img, const int32_t* cu_seqlens, int32_t n_samples,
                    int32_t cp_size, int32_t cp_rank, int32_t split, int32_t schedule, int32_t heads,
@@ -80,77 +176,69 @@ cp_status rank_fwd(const void* q, const void* k, const void* v, int32_t dtype, i
     int32_t st = prepare_workspace(seq_len, n_img, cu_seqlens, n_samples, cp_size, cp_rank, heads,
                                    kv_heads, head_dim, dtype, w, split, schedule);
     if (st != CP_OK) return st;
-    const int64_t R = w.meta.rows;
-    if (R == 0) return CP_OK;
-    if (!q || !k || !v || !out || !lse || !workspace) return CP_EINVAL;
-    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
-        !aligned(lse, 4) || !aligned(workspace, 256))
-      return CP_EINVAL;
+    if (w.meta.rows == 0) return CP_OK;
+    st = check_fwd_pointers(q, k, v, out, lse);
+    if (st != CP_OK) return st;
+    if (!workspace || !aligned(workspace, 256)) return CP_EINVAL;
     if (workspace_bytes < w.total) return CP_ENOSPC;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    return run_fwd(w, q, k, v, dtype, cp_size, heads, kv_heads, head_dim, out, lse,
+                   static_cast<uint8_t*>(workspace), static_cast<hipStream_t>(stream), events,
+                   Upload::kPinnedStaging);
+  } catch (const std::exception&) {
+    return CP_EINVAL;
+  }
+}
 
-    if (mark(events, 0, s) != hipSuccess) return CP_EHIP;
-    if (stage_and_upload(w.plan_bytes, [&](uint8_t* dst) { pack_plan(w, dst); }, ws, s) != hipSuccess)
-      return CP_EHIP;
-    if (mark(events, 1, s) != hipSuccess) return CP_EHIP;
-    // The attention kernels read each row tile's Q rows in place (a tile is
-    // a run of consecutive global ids), so the gather has no pass of its own.
-    const int32_t* index = reinterpret_cast<const int32_t*>(ws + w.off_index);
-    if (mark(events, 2, s) != hipSuccess) return CP_EHIP;
+// ------------------------------------------------ entry point without allocation
+// The scratch of cp_attn_rank_fwd_noalloc: one array per GPU, in the code
+// object's device memory, held until the process ends. Host code never uses
+// its name as an address (on the host it only stands for the symbol): the
+// device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) uint8_t scratch[CP_NOALLOC_SCRATCH_BYTES];
 
-    AttnArgs a;
-    // (no V relayout: the bf16 head_dim-128 kernel reads V tiles row-major
-    // and transposes them in its LDS reads)
-    if (mark(events, 3, s) != hipSuccess) return CP_EHIP;
-    a.q = q;
-    a.k = k;
-    a.v = v;
-    a.part_o = reinterpret_cast<float*>(ws + w.off_po);
-    a.part_lse = reinterpret_cast<float*>(ws + w.off_pl);
-    a.tiles = reinterpret_cast<const TileRec*>(ws + w.off_tiles);
-    a.entries = reinterpret_cast<const EntryRec*>(ws + w.off_entries);
-    a.spans = reinterpret_cast<const SpanRec*>(ws + w.off_spans);
-    a.tile_entries = reinterpret_cast<const EntryRec*>(ws + w.off_tile_entries);
-    a.units = reinterpret_cast<const UnitRec*>(ws + w.off_units);
-    a.out = out;
-    a.lse = lse;
-    a.R = int32_t(R);
-    a.H = heads;
-    a.Hkv = kv_heads;
-    a.group = heads / kv_heads;
-    a.n_hg = heads / w.shape.heads_per_wg;
-    a.scale = float(1.0 / std::sqrt(double(head_dim)));
-    a.scale_log2 = float(1.4426950408889634 / std::sqrt(double(head_dim)));
-    const int n_entries = int(w.plan.entries.size());
-    a.per_step = w.unit_per_step ? 1 : 0;
-    if (w.unit_kernel && !w.unit_per_step) {
-      // all ring steps of a row tile in one workgroup, merged in the kernel
-      if (launch_attn_bf16_units(a, w.shape.heads_per_wg, int(w.plan.units.size()), s) != hipSuccess)
-        return CP_EHIP;
-      if (w.plan.pad_rows > 0 &&
-          launch_fill_pad_rows(index, R, heads, head_dim, dtype, out, lse, s) != hipSuccess)
-        return CP_EHIP;
-      if (mark(events, 4, s) != hipSuccess) return CP_EHIP;
-      if (mark(events, 5, s) != hipSuccess) return CP_EHIP;
-      return CP_OK;
-    }
-    // per-step partials for the merge pass: small bf16 head_dim-128 grids
-    // (unit kernel, one step per unit), head_dim 64, fp32
-    hipError_t e = w.unit_kernel
-                       ? launch_attn_bf16_units(a, w.shape.heads_per_wg, int(w.plan.step_units.size()), s)
-                   : dtype == CP_DTYPE_BF16
-                       ? launch_attn_bf16(a, head_dim, w.shape.heads_per_wg, n_entries, s)
-                       : launch_attn_f32(a, head_dim, n_entries, s);
-    if (e != hipSuccess) return CP_EHIP;
-    if (mark(events, 4, s) != hipSuccess) return CP_EHIP;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
 
-    const uint32_t* mask = reinterpret_cast<const uint32_t*>(ws + w.off_mask);
-    if (launch_lse_merge(a.part_o, a.part_lse, mask, cp_size, R, heads, head_dim, dtype, out, lse, s) !=
-        hipSuccess)
-      return CP_EHIP;
-    if (mark(events, 5, s) != hipSuccess) return CP_EHIP;
-    return CP_OK;
+// Device address of the current device's scratch, looked up on its first use.
+hipError_t scratch_on_current_device(uint8_t** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = static_cast<uint8_t*>(g_scratch_ptr[dev]);
+  return hipSuccess;
+}
+
+cp_status rank_fwd_noalloc(const void* q, const void* k, const void* v, int32_t dtype, int64_t seq_len,
+                           const int32_t* n_img, const int32_t* cu_seqlens, int32_t n_samples,
+                           int32_t cp_size, int32_t cp_rank, int32_t heads, int32_t kv_heads,
+                           int32_t head_dim, void* out, float* lse, void* stream) {
+  try {
+    // bf16 head_dim 128 carries one online softmax across the steps: the
+    // scratch holds the plan only; the other paths also hold the per-step
+    // partials
+    const int32_t schedule = (dtype == CP_DTYPE_BF16 && head_dim == 128) ? CP_SCHED_ROW_TILE : CP_SCHED_AUTO;
+    Workspace w;
+    int32_t st = prepare_workspace(seq_len, n_img, cu_seqlens, n_samples, cp_size, cp_rank, heads,
+                                   kv_heads, head_dim, dtype, w, CP_SPLIT_HEAD_TAIL, schedule);
+    if (st != CP_OK) return st;
+    if (w.meta.rows == 0) return CP_OK;
+    st = check_fwd_pointers(q, k, v, out, lse);
+    if (st != CP_OK) return st;
+    if (w.total > CP_NOALLOC_SCRATCH_BYTES) return CP_ENOSPC;
+    uint8_t* ws = nullptr;
+    if (scratch_on_current_device(&ws) != hipSuccess) return CP_EHIP;
+    return run_fwd(w, q, k, v, dtype, cp_size, heads, kv_heads, head_dim, out, lse, ws,
+                   static_cast<hipStream_t>(stream), nullptr, Upload::kHeapWait);
   } catch (const std::exception&) {
     return CP_EINVAL;
   }
@@ -252,6 +340,15 @@ cp_status cp_attn_rank_fwd(const void* q, const void* k, const void* v, int32_t 
   return rank_fwd(q, k, v, dtype, seq_len, n_img, cu_seqlens, n_samples, cp_size, cp_rank,
                   CP_SPLIT_HEAD_TAIL, CP_SCHED_AUTO, heads, kv_heads, head_dim, out, lse, workspace,
                   workspace_bytes, stream, nullptr);
+}
+
+cp_status cp_attn_rank_fwd_noalloc(const void* q, const void* k, const void* v, int32_t dtype,
+                                   int64_t seq_len, const int32_t* n_img, const int32_t* cu_seqlens,
+                                   int32_t n_samples, int32_t cp_size, int32_t cp_rank, int32_t heads,
+                                   int32_t kv_heads, int32_t head_dim, void* out, float* lse,
+                                   void* stream) {
+  return rank_fwd_noalloc(q, k, v, dtype, seq_len, n_img, cu_seqlens, n_samples, cp_size, cp_rank, heads,
+                          kv_heads, head_dim, out, lse, stream);
 }
 
 cp_status cp_attn_rank_fwd_timed(const void* q, const void* k, const void* v, int32_t dtype,

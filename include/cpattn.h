@@ -221,6 +221,38 @@ cp_status cp_attn_rank_fwd_timed(const void *q, const void *k, const void *v, in
                                  void *stream, void *const *events);
 
 /*
+ * cp_attn_rank_fwd_noalloc -- cp_attn_rank_fwd for callers that cannot
+ * allocate device memory or hand over a workspace: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * Same arguments, results and errors as cp_attn_rank_fwd, without the
+ * workspace. Its scratch (the uploaded plan; on the fp32 and head_dim-64
+ * paths also the per-step partials) is a static device array of
+ * CP_NOALLOC_SCRATCH_BYTES per GPU, held from the library's first use on
+ * that GPU until the process ends. A problem whose scratch would exceed it
+ * returns CP_ENOSPC before any device work. bf16 with head_dim 128 always
+ * takes the row-tile schedule (CP_SCHED_ROW_TILE: no partials), so there
+ * the limit is the plan alone: 8 bytes per rank-local row plus about 50 per
+ * (row tile, ring step), e.g. about a million rank rows at P = 8 with 64-row
+ * tiles. The exact need is what cp_attn_rank_workspace_size_ex returns for
+ * CP_SPLIT_HEAD_TAIL with that schedule (CP_SCHED_AUTO on the other paths).
+ *
+ * It calls no hipMalloc, hipHostMalloc or hipFree: the plan is copied from
+ * ordinary host memory, so the call returns only after that copy has run,
+ * i.e. after `stream` has finished the work queued on it before this call
+ * (the kernels themselves are enqueued asynchronously). Every call on one
+ * GPU uses the same array and overwrites it: calls that overlap on one GPU
+ * (other streams, other host threads) race; calls on one stream are
+ * ordered. Nothing in the array needs to start at zero.
+ */
+#define CP_NOALLOC_SCRATCH_BYTES (16u << 20)
+cp_status cp_attn_rank_fwd_noalloc(const void *q, const void *k, const void *v, int32_t dtype,
+                                   int64_t seq_len, const int32_t *n_img, const int32_t *cu_seqlens,
+                                   int32_t n_samples, int32_t cp_size, int32_t cp_rank,
+                                   int32_t heads, int32_t kv_heads, int32_t head_dim, void *out,
+                                   float *lse, void *stream);
+
+/*
  * cp_gather_rows -- the chunk-index gather alone (page section 1.1,
  * index_select on the sequence dimension): dst[i, :] = src[index[i], :]
  * for index[i] >= 0 and 0 for index[i] == -1.

@@ -350,3 +350,20 @@ def test_bwd_argument_errors_before_any_device_work(cp):
     zero = np.array([0], np.int32)
     cu0 = zero.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
     assert bwd(seq_len=0, cu=cu0, n=0, q=None, out=None, lse=None, dout=None, dq=None) == cp.CP_OK
+
+
+def test_noalloc_refuses_a_plan_beyond_its_scratch_before_device_work(cp):
+    # cp_attn_rank_fwd_noalloc: 3M rank rows need 24 MB of row index and step
+    # masks, beyond its 16 MiB scratch; refused before any HIP call (the fake
+    # pointers are never read), and argument errors as for cp_attn_rank_fwd
+    fake = ctypes.c_void_p(4096)
+    assert cp.CP_NOALLOC_SCRATCH_BYTES == 16 << 20
+    st = cp.cp_attn_rank_fwd_noalloc(fake, fake, fake, 1, 3_000_000, None, None, 1, 1, 0, 2, 2, 128, fake,
+                                     fake, None)
+    assert st == cp.CP_ENOSPC
+    assert cp.cp_attn_rank_fwd_noalloc(None, fake, fake, 1, 100, None, None, 1, 2, 0, 4, 4, 128, fake, fake,
+                                       None) == cp.CP_EINVAL
+    assert cp.cp_attn_rank_fwd_noalloc(fake, fake, fake, 1, 100, None, None, 1, 2, 0, 4, 4, 96, fake, fake,
+                                       None) == cp.CP_EUNSUPPORTED
+    assert cp.cp_attn_rank_fwd_noalloc(fake, fake, fake, 1, 100, None, None, 1, 2, 2, 4, 4, 128, fake, fake,
+                                       None) == cp.CP_EINVAL
