@@ -10,7 +10,9 @@ Prints one JSON line. ``roofline`` covers the dominant kernel (the per-step
 attention): achieved = useful FLOPs per launch / its average duration, timed
 with HIP events recorded by the library on the launch stream.
 ``cpu_baseline`` times the fp64 oracle on a bounded sample of the same
-rank's rows on this host's cores.
+rank's rows on this host's cores (worker processes, spawned before the GPU
+is touched), and, on the default workload, the literal form of the oracle
+(whole sequence, then select) beside its rows-only form on workload 2.
 """
 from __future__ import annotations
 
@@ -58,36 +60,73 @@ def traffic_from_profile():
 
 
 def cpu_baseline(w, q, k, v, n_img, cu, target_s: float, split: str = "head_tail"):
-    """The fp64 oracle, as it stands, on a bounded sample of the rank's rows."""
+    """The fp64 oracle, as it stands, on a bounded sample of the rank's rows,
+    its (KV group, 256-row block) tasks spread over worker processes (one per
+    core of this process's affinity set, at most 16; BLAS one thread each).
+    Must run before this process touches the GPU: the workers are spawned.
+    A small calibration pass sizes the sample to about ``target_s`` seconds."""
     import numpy as np
 
     import oracle
+    from oracle.pool import default_workers, rank_attention_pooled
 
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        threads = 1
+    workers = default_workers()
     index, _ = oracle.partition_index(w.seq_len, n_img, cu, w.cp_size, w.rank, split)
     R = len(index)
-    n = 32
-    while True:
-        rows = np.linspace(0, R - 1, n).astype(np.int64)
-        t0 = time.perf_counter()
-        oracle.rank_attention(q, k, v, n_img, cu, w.cp_size, w.rank, local_rows=rows, split=split)
-        dt = time.perf_counter() - t0
-        if dt >= target_s / 3 or n >= R:
-            break
-        n = min(R, int(n * max(2.0, target_s / max(dt, 1e-3))))
+
+    def run(n):
+        rows = np.unique(np.linspace(0, R - 1, n).astype(np.int64))
+        st = {}
+        rank_attention_pooled(q, k, v, n_img, cu, w.cp_size, w.rank, local_rows=rows, split=split,
+                              workers=workers, row_chunk=256, executor="process", stats=st)
+        return rows, st["wall_s"]
+
+    n0 = min(R, 32 * workers)
+    rows, dt = run(n0)
+    if dt < target_s / 2 and n0 < R:
+        rows, dt = run(min(R, int(n0 * target_s / max(dt, 1e-3))))
     # a real row at position p of its sample sees p + 1 keys; pads see none
     ids = index[rows].astype(np.int64)
     ids = ids[ids >= 0]
     starts = w.cu_seqlens.astype(np.int64)
     pairs = int(np.sum(ids - starts[np.searchsorted(starts, ids, side="right") - 1] + 1))
     flops = 4.0 * w.head_dim * w.heads * pairs
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{n} of {R} rank-local rows (evenly spaced), all {w.heads} heads, "
-                      f"{pairs} useful pairs/head, {dt:.1f} s, fp64 numpy"}
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(workers), "kind": "oracle",
+            "sample": f"{len(rows)} of {R} rank-local rows (evenly spaced), all {w.heads} heads, "
+                      f"{pairs} useful pairs/head, {dt:.1f} s on {workers} worker processes "
+                      f"(affinity set of this process, at most 16; one BLAS thread each), fp64 numpy, "
+                      f"rows-only form"}
+
+
+def cpu_literal_workload2(target_workers=None):
+    """The literal oracle -- whole-sequence causal attention, then the rank's
+    rows selected -- on workload 2 (text 8192, P=4, rank 0, 16 heads), one
+    head per worker process, timed beside its rows-only form."""
+    import numpy as np
+
+    import oracle
+    import workloads
+    from oracle.pool import default_workers, rank_attention_pooled
+
+    w = workloads.get(2)
+    q, k, v = workloads.make_inputs(w)
+    workers = target_workers or default_workers()
+    res = {}
+    for form, literal in (("literal", True), ("rows_only", False)):
+        st = {}
+        rank_attention_pooled(q, k, v, None, None, w.cp_size, 0, literal=literal, workers=workers,
+                              executor="process", stats=st)
+        res[form] = st["wall_s"]
+    _, pairs = oracle.pair_counts(w.seq_len, None, None, w.cp_size, 0)
+    useful = 4.0 * w.head_dim * w.heads * pairs
+    L = w.seq_len
+    full = 4.0 * w.head_dim * w.heads * L * (L + 1) // 2
+    return {"workload": w.name, "cores": int(workers),
+            "literal_s": round(res["literal"], 2), "rows_only_s": round(res["rows_only"], 2),
+            "literal_useful_TFLOPs": round(useful / res["literal"] / 1e12, 4),
+            "literal_computed_TFLOPs": round(full / res["literal"] / 1e12, 4),
+            "rows_only_TFLOPs": round(useful / res["rows_only"] / 1e12, 4),
+            "note": "literal computes all 8192 rows (4x the rank's useful work) before selecting the rank's 2048"}
 
 
 def timed_calls(ra, hip, steps, warmup):
@@ -258,8 +297,9 @@ def bench_backward(w, args):
 def bench_hbm(w, args):
     """A2 (gather) and A5 (merge) are HBM-bound; report GB/s of algorithmic
     bytes against the 8 TB/s peak and against a plain device copy of about
-    the same size timed in the same process (the MALL is 256 MB, so a
-    working set of this size is not cache-resident)."""
+    the same size timed in the same process. A 512 MiB fill before each
+    timed call evicts the 256 MB MALL, so no call finds its inputs (or the
+    previous call's output) in cache."""
     import numpy as np
     import torch
 
@@ -278,12 +318,17 @@ def bench_hbm(w, args):
     plse = torch.randn((P, H, R), generator=g).to(dev)
     mask = np.full(R, (1 << P) - 1, dtype=np.uint64).astype(np.uint32)
 
+    # between timed calls, a 512 MiB fill evicts the 256 MB MALL (last-level
+    # cache), so every call reads its inputs from HBM
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+
     def time_ms(fn):
         for _ in range(args.warmup):
             fn()
         torch.cuda.synchronize()
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
         for a, b in evs:
+            flush.fill_(1)
             a.record()
             fn()
             b.record()
@@ -318,7 +363,7 @@ def bench_hbm(w, args):
     def rate(b, t):
         return round(b / (t * 1e-3) / 1e9, 1)
     copy_gbps = rate(copy_bytes, t_copy)
-    line = {"mode": "hbm", "unit": "GB/s", "peak_GBps": 8000.0,
+    line = {"mode": "hbm", "unit": "GB/s", "peak_GBps": 8000.0, "cache": "MALL flushed before every timed call",
             "gather": {"kernel": "gather_rows_kernel", "bytes": gather_bytes, "ms": round(t_gather, 4),
                        "GBps": rate(gather_bytes, t_gather),
                        "frac_of_copy": round(rate(gather_bytes, t_gather) / copy_gbps, 3)},
@@ -338,8 +383,8 @@ def main():
     ap.add_argument("--workload", type=int, default=4, help="synthetic workload number (1-5)")
     ap.add_argument("--rank", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=36.0,
-                    help="CPU-baseline budget; the oracle sample grows until it takes a third of this")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="CPU-baseline budget: the oracle sample is sized to take about this long")
     ap.add_argument("--split", choices=["head_tail", "contiguous"], default="head_tail",
                     help="text split over the CP group (contiguous: the plain P-way split)")
     ap.add_argument("--compare-splits", action="store_true",
@@ -399,11 +444,23 @@ def main():
     if rank != w.rank:
         import dataclasses
         w = dataclasses.replace(w, ranks=(rank,))
-    dev = torch.device("cuda:0")
     q, k, v = workloads.make_inputs(w)
-    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
     n_img = w.n_img_array if any(w.n_img) else None
     cu = w.cu_seqlens if w.n_samples > 1 else None
+    # the CPU baseline first: its worker processes are spawned, which this
+    # process does before it touches the GPU
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("cpu baseline (fp64 oracle, worker processes) ...", file=sys.stderr, flush=True)
+        try:
+            cpu = cpu_baseline(w, q, k, v, n_img, cu, args.cpu_seconds, args.split)
+            if args.workload == 4:
+                cpu["literal_vs_rows_only"] = cpu_literal_workload2()
+        except Exception as e:  # the baseline is reported, never the product: keep the GPU line
+            cpu = {"error": f"{type(e).__name__}: {e}"}
+        print(f"cpu baseline: {json.dumps(cpu)}", file=sys.stderr, flush=True)
+    dev = torch.device("cuda:0")
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
     ra = cp.RankAttention(qd, kd, vd, cp_size=w.cp_size, cp_rank=rank, n_img=n_img, cu_seqlens=cu,
                           split=args.split)
     _, pairs = cp.pair_counts(w.seq_len, n_img, cu, cp_size=w.cp_size, cp_rank=rank, split=args.split)
@@ -486,8 +543,8 @@ def main():
                      "kernel": ("attn_rank_bf16_d128_kernel (all ring steps of a row tile per workgroup, one online softmax across them)" if w.head_dim == 128 else "attn_step_bf16_kernel (per-step attention, all ring steps, one launch)")
                                },
     }
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, q, k, v, n_img, cu, args.cpu_seconds, args.split)
+    if cpu is not None:
+        line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)
 
 

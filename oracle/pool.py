@@ -10,8 +10,8 @@ on that head and its KV head, so the assembled result is the single-process
 one (up to the BLAS library's own summation order, ~1e-16 relative).
 
 Process workers are started with the "spawn" method (fresh interpreters
-that never touch a GPU) and read the inputs from memory-mapped files under
-/dev/shm, so nothing large is pickled. Thread workers share this process's
+that never touch a GPU) and read the inputs from memory-mapped files (under
+/dev/shm when it has room), so nothing large is pickled. Thread workers share this process's
 arrays. Either way BLAS is limited to one thread per worker; the worker
 count is the parallelism.
 """
@@ -160,8 +160,19 @@ def _run_threads(q, k, v, jobs, n_workers, timeout_s):
     return results, wall
 
 
+def _scratch_dir(nbytes: int) -> Optional[str]:
+    """/dev/shm (memory) when it has room for the inputs twice over, else
+    the default temporary directory."""
+    try:
+        if os.path.isdir("/dev/shm") and shutil.disk_usage("/dev/shm").free > 2 * nbytes:
+            return "/dev/shm"
+    except OSError:  # pragma: no cover
+        pass
+    return None
+
+
 def _run_processes(q, k, v, jobs, n_workers, timeout_s):
-    folder = tempfile.mkdtemp(prefix="cp_oracle_", dir="/dev/shm" if os.path.isdir("/dev/shm") else None)
+    folder = tempfile.mkdtemp(prefix="cp_oracle_", dir=_scratch_dir(q.nbytes + k.nbytes + v.nbytes))
     try:
         for name, arr in (("q", q), ("k", k), ("v", v)):
             np.save(os.path.join(folder, name + ".npy"), arr)
