@@ -628,63 +628,84 @@ void dkdv_kernel(const BwdArgs a) {
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int e = 0; e < 8; ++e) pd[i][e] = (__bf16)0.f;
-#define DKDV_STEP(J, CUR, PREV, NXT, PC, PP)                    \
-  {                                                             \
-    __builtin_amdgcn_s_waitcnt(wait_vmcnt_lgkm0(PER_STAGE));    \
-    asm volatile("s_barrier" ::: "memory");                     \
-    issue(ip, NXT);                                             \
-    next(ip);                                                   \
-    if (pwave) {                                                \
-      __builtin_amdgcn_s_setprio(1);                            \
-      product(pd, PREV + OD);                                   \
-      scores(CUR + OQ, sdp);                                    \
-      schedule_matrix_phase();                                  \
-      __builtin_amdgcn_s_setprio(0);                            \
-    } else {                                                    \
-      p_ds(PREV, PP, sdp, pd);                                  \
-    }                                                           \
-    __builtin_amdgcn_s_waitcnt(wait_vmcnt_lgkm0(63));           \
-    asm volatile("s_barrier" ::: "memory");                     \
-    if (pwave) {                                                \
-      p_softmax(cp.rb, CUR, sdp, pd, PC);                       \
-    } else {                                                    \
-      __builtin_amdgcn_s_setprio(1);                            \
-      product(pd, PREV + OQ);                                   \
-      scores(CUR + OD, sdp);                                    \
-      schedule_matrix_phase();                                  \
-      __builtin_amdgcn_s_setprio(0);                            \
-    }                                                           \
-    next(cp);                                                   \
+  // Each role runs its own copy of the loop: with one loop and a branch on
+  // the role inside every phase, the two roles' accumulators met at every
+  // phase end and the compiler copied them between registers there (about
+  // 40 64-bit moves per step in the vector phase). The barrier sequence is
+  // the same in both loops: two per step, the same step count.
+#define DKDV_HEAD(NXT)                                        \
+  __builtin_amdgcn_s_waitcnt(wait_vmcnt_lgkm0(PER_STAGE));    \
+  asm volatile("s_barrier" ::: "memory");                     \
+  issue(ip, NXT);                                             \
+  next(ip);
+#define DKDV_MID                                              \
+  __builtin_amdgcn_s_waitcnt(wait_vmcnt_lgkm0(63));           \
+  asm volatile("s_barrier" ::: "memory");
+  // P wave: phase A products of step j-1 and scores of step j (MFMA),
+  // phase B the softmax of step j (VALU)
+#define DKDV_STEP_P(CUR, PREV, NXT, PC, PP)                   \
+  {                                                           \
+    DKDV_HEAD(NXT)                                            \
+    __builtin_amdgcn_s_setprio(1);                            \
+    product(pd, PREV + OD);                                   \
+    scores(CUR + OQ, sdp);                                    \
+    schedule_matrix_phase();                                  \
+    __builtin_amdgcn_s_setprio(0);                            \
+    DKDV_MID                                                  \
+    p_softmax(cp.rb, CUR, sdp, pd, PC);                       \
+    next(cp);                                                 \
+  }
+  // partner: phase A dS of step j-1 (VALU), phase B its products and the
+  // dP scores of step j (MFMA)
+#define DKDV_STEP_D(CUR, PREV, NXT, PC, PP)                   \
+  {                                                           \
+    DKDV_HEAD(NXT)                                            \
+    p_ds(PREV, PP, sdp, pd);                                  \
+    DKDV_MID                                                  \
+    __builtin_amdgcn_s_setprio(1);                            \
+    product(pd, PREV + OQ);                                   \
+    scores(CUR + OD, sdp);                                    \
+    schedule_matrix_phase();                                  \
+    __builtin_amdgcn_s_setprio(0);                            \
   }
   // (guarded steps rather than early exits: one loop exit keeps the
   // accumulators in place instead of copying them at every exit)
-  int i = 0;
-  for (; i + 4 <= n_blocks; i += 4) {
-    DKDV_STEP(i, st0, st3, st2, pb0, pb1);
-    DKDV_STEP(i + 1, st1, st0, st3, pb1, pb0);
-    DKDV_STEP(i + 2, st2, st1, st0, pb0, pb1);
-    DKDV_STEP(i + 3, st3, st2, st1, pb1, pb0);
+#define DKDV_LOOP(STEP)                                       \
+  {                                                           \
+    int i = 0;                                                \
+    for (; i + 4 <= n_blocks; i += 4) {                       \
+      STEP(st0, st3, st2, pb0, pb1);                          \
+      STEP(st1, st0, st3, pb1, pb0);                          \
+      STEP(st2, st1, st0, pb0, pb1);                          \
+      STEP(st3, st2, st1, pb1, pb0);                          \
+    }                                                         \
+    if (i < n_blocks) STEP(st0, st3, st2, pb0, pb1);          \
+    if (i + 1 < n_blocks) STEP(st1, st0, st3, pb1, pb0);      \
+    if (i + 2 < n_blocks) STEP(st2, st1, st0, pb0, pb1);      \
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt_lgkm0(0));          \
+    asm volatile("s_barrier" ::: "memory");                   \
   }
-  if (i < n_blocks) DKDV_STEP(i, st0, st3, st2, pb0, pb1);
-  if (i + 1 < n_blocks) DKDV_STEP(i + 1, st1, st0, st3, pb1, pb0);
-  if (i + 2 < n_blocks) DKDV_STEP(i + 2, st2, st1, st0, pb0, pb1);
-#undef DKDV_STEP
   // the last step's remaining work: dV (P wave) and dS then dK (partner) of
   // step n_blocks - 1 (slot (n_blocks - 1) % 4, P buffer of its parity); the
   // stages issued past the end land before the kernel exits
-  __builtin_amdgcn_s_waitcnt(wait_vmcnt_lgkm0(0));
-  asm volatile("s_barrier" ::: "memory");
-  if (n_blocks > 0) {
-    const char* const pl = (last & 1) ? pb1 : pb0;
-    const int slot = last & 3;
-    const char* const sl = slot == 0 ? st0 : slot == 1 ? st1 : slot == 2 ? st2 : st3;
-    if (pwave) {
-      product(pd, sl + OD);
-    } else {
+  const char* const pl = (last & 1) ? pb1 : pb0;
+  const int slot = last & 3;
+  const char* const sl = slot == 0 ? st0 : slot == 1 ? st1 : slot == 2 ? st2 : st3;
+  if (pwave) {
+    DKDV_LOOP(DKDV_STEP_P)
+    if (n_blocks > 0) product(pd, sl + OD);
+  } else {
+    DKDV_LOOP(DKDV_STEP_D)
+    if (n_blocks > 0) {
       p_ds(sl, pl, sdp, pd);
       product(pd, sl + OQ);
     }
   }
+#undef DKDV_LOOP
+#undef DKDV_STEP_D
+#undef DKDV_STEP_P
+#undef DKDV_MID
+#undef DKDV_HEAD
 
   // accumulator register t of lane half hh: key 32 pair + (t/4)*8 + 4 hh + t%4,
   // d = 32 db + kl

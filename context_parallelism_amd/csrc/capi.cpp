@@ -16,21 +16,28 @@ using namespace cpattn;
 
 namespace {
 
-// Pinned host staging for the plan upload, one per host thread. The copy of
-// call n must have left the buffer before call n + 1 rewrites it; an event
-// recorded after the copy guards that. Never freed (process lifetime).
-struct Staging {
+// Pinned host staging for the plan upload: a ring of kStagingSlots buffers
+// per host thread. A slot's copy must have left it before a later call
+// rewrites it; an event recorded after each copy guards that, so the host
+// waits only when it is kStagingSlots uploads ahead of the device. Never
+// freed (process lifetime).
+constexpr int kStagingSlots = 4;
+struct StagingSlot {
   void* host = nullptr;
   size_t cap = 0;
   hipEvent_t copied = nullptr;
   int device = -1;
   bool pending = false;
 };
+struct Staging {
+  StagingSlot slot[kStagingSlots];
+  int next = 0;
+};
 thread_local Staging t_stage;
 
 template <typename Pack>
 hipError_t stage_and_upload(size_t plan_bytes, Pack pack, void* dst, hipStream_t stream) {
-  Staging& s = t_stage;
+  StagingSlot& s = t_stage.slot[t_stage.next];
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
@@ -63,6 +70,7 @@ hipError_t stage_and_upload(size_t plan_bytes, Pack pack, void* dst, hipStream_t
   e = hipEventRecord(s.copied, stream);
   if (e != hipSuccess) return e;
   s.pending = true;
+  t_stage.next = (t_stage.next + 1) % kStagingSlots;
   return hipSuccess;
 }
 

@@ -33,12 +33,14 @@
  *   - n_img: int32[n_samples], image-prefix length of each sample,
  *     0 <= n_img[s] <= cu[s+1] - cu[s]. NULL means no image prefix.
  *   - Host pointers are read during the call only; the library keeps no
- *     caller pointer. Its only state is one pinned host staging buffer per
- *     host thread for the plan upload (hipHostMalloc'd on first use, grown
- *     when a larger plan comes, kept until the process ends); a call waits
- *     for the previous upload from that buffer before rewriting it. Calls
- *     from different threads, or on different streams, may run
- *     concurrently. The library allocates no device memory.
+ *     caller pointer. Its only state is a ring of four pinned host staging
+ *     buffers per host thread for the plan upload (each hipHostMalloc'd on
+ *     first use, grown when a larger plan comes, kept until the process
+ *     ends); a call waits for the upload made four calls earlier from the
+ *     same buffer before rewriting it, so the host can run up to four calls
+ *     ahead of the device. Calls from different threads, or on different
+ *     streams, may run concurrently. Apart from the static scratch of
+ *     cp_attn_rank_fwd_noalloc, the library holds no device memory.
  *   - Errors: every argument is checked before anything is written or
  *     launched; on error nothing is written and a negative status is
  *     returned. No C++ exception crosses this boundary.
