@@ -407,6 +407,21 @@ __device__ inline void schedule_matrix_phase() {
   }
 }
 
+// A matrix phase of two steps: 16 product MFMAs (two transposing LDS reads
+// each), then 16 score MFMAs (one LDS read each); reads kPhaseAhead MFMAs
+// ahead.
+__device__ inline void schedule_matrix_phase2() {
+  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * kPhaseAhead, 0);
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    if (i + kPhaseAhead < 16)
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+    else if (i + kPhaseAhead < 32)
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+  }
+}
+
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void dkdv_kernel(const BwdArgs a) {
   constexpr int D = 128, NQ = 8, ND = 4, RBK = kBwdRowBlock;
@@ -422,8 +437,16 @@ void dkdv_kernel(const BwdArgs a) {
   // P of one step, from the P wave of each pair to its partner: bf16, in the
   // register order of the P wave (two 16-byte pieces per lane)
   constexpr int PBUF = 4 * 2 * 1024;
-  __shared__ __attribute__((aligned(1024))) char st0[STAGE], st1[STAGE], st2[STAGE], st3[STAGE];
-  __shared__ __attribute__((aligned(1024))) char pb0[PBUF], pb1[PBUF];
+  // Each loop iteration takes two consecutive steps (a double step), so a
+  // matrix phase holds 32 MFMAs: a ring of four slot pairs (two steps
+  // each), and one P buffer with a half per step of the pair -- the P waves
+  // write it in phase B, the partners read it in the next phase A, and the
+  // barrier between the two phases orders the next write after those reads.
+  // 8 x 18 KiB + 16 KiB = the 160 KiB of LDS of a compute unit.
+  __shared__ __attribute__((aligned(1024))) char s0[STAGE], s1[STAGE], s2[STAGE], s3[STAGE];
+  __shared__ __attribute__((aligned(1024))) char s4[STAGE], s5[STAGE], s6[STAGE], s7[STAGE];
+  __shared__ __attribute__((aligned(1024))) char pbf[2 * PBUF];
+  static_assert(8 * STAGE + 2 * PBUF <= 160 * 1024, "LDS of one compute unit");
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -533,7 +556,7 @@ void dkdv_kernel(const BwdArgs a) {
   };
   // P wave, step j in slot st: the mask on S, P = exp2(S c2 - lse log2 e)
   // (0 for pad rows, whose record holds +inf), P to the partner
-  auto p_softmax = [&](int rb, const char* st, f32x16& s, bf16x8 (&pa)[2], char* pbuf) {
+  auto p_softmax = [&](int rb, const char* st, f32x16& s, bf16x8 (&pa)[2], char* pbuf, bool valid) {
     const int* const rec = reinterpret_cast<const int*>(st + OREC);
     // every row of the block sees every key of the pair unless the block
     // holds a causal edge or a sample boundary; then S = -inf where the key
@@ -565,6 +588,12 @@ void dkdv_kernel(const BwdArgs a) {
         for (int e = 0; e < 4; ++e)
           pa[run][4 * q4 + e] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * run + 4 * q4 + e], c2, -l2[e]));
       }
+    if (!valid) {  // the step past the end of an odd count: it adds nothing
+#pragma unroll
+      for (int run = 0; run < 2; ++run)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pa[run][e] = (__bf16)0.f;
+    }
     bf16x8* const pw = reinterpret_cast<bf16x8*>(pbuf + pair * 2048) + lane;
     pw[0] = pa[0];
     pw[64] = pa[1];
@@ -587,118 +616,149 @@ void dkdv_kernel(const BwdArgs a) {
       }
   };
 
-  // Ring of four LDS slots: block step j sits in slot j % 4; steps j + 1
-  // and j + 2 are in flight while step j is consumed. Iteration j has two
-  // phases, each ending at a workgroup barrier, and in each phase one wave
-  // of a pair works on the matrix cores while its partner does vector work:
-  //   phase A: P wave   dV += P(j-1)^T dO(j-1), then S(j) = Q(j) K^T  (MFMA)
-  //            partner  dS(j-1) = P(j-1) (dP(j-1) - Delta)           (VALU)
-  //   phase B: P wave   mask, P(j) = exp2(...), P(j) to LDS          (VALU)
-  //            partner  dK += dS(j-1)^T Q(j-1), then dP(j) = dO(j) V^T (MFMA)
-  // Step j + 2 is issued at the start of iteration j into the slot of step
-  // j - 2, which both waves finished in iteration j - 1. Every iteration
-  // issues one stage (past the end, the last step again, into a free slot),
-  // so the count of loads in flight after step j's is always one stage.
+  // Double steps J = 0 .. n_pairs - 1 take steps 2J and 2J + 1 (the second
+  // past the end when n_blocks is odd). Double step J sits in slot pair
+  // J % 4; pairs J + 1 and J + 2 are in flight while J is consumed.
+  // Iteration J has two phases, each ending at a workgroup barrier, and in
+  // each phase one wave of a pair works on the matrix cores while its
+  // partner does vector work:
+  //   phase A: P wave   dV += P(J-1)^T dO(J-1), then S(J) = Q(J) K^T  (MFMA)
+  //            partner  dS(J-1) = P(J-1) (dP(J-1) - Delta)           (VALU)
+  //   phase B: P wave   mask, P(J) = exp2(...), P(J) to LDS          (VALU)
+  //            partner  dK += dS(J-1)^T Q(J-1), then dP(J) = dO(J) V^T (MFMA)
+  // (each for both steps of the pair). Pair J + 2 is issued at the start of
+  // iteration J into the slots of pair J - 2, which both waves finished in
+  // iteration J - 1. Every iteration issues one pair (past the end, the last
+  // step again), so the count of loads in flight after pair J's is always
+  // one pair's.
+  const int n_pairs = (n_blocks + 1) / 2;
   StepPos ip = {kt.rb0, 0, 0};  // the next step to issue
   StepPos cp = {kt.rb0, 0, 0};  // the step the P waves compute
   if (n_blocks > 0) {
-    issue(ip, st0);
+    issue(ip, s0);
     next(ip);
-    issue(ip, st1);
+    issue(ip, s1);
+    next(ip);
+    issue(ip, s2);
+    next(ip);
+    issue(ip, s3);
     next(ip);
   }
-  // The slot of step -1 (st3) and the P buffer of parity -1 (pb1) hold
-  // zeros, so the first iteration's products of step -1 add nothing and the
-  // phases need no branch on the step.
+  // The slots of pair -1 (s6, s7) and the P buffer hold zeros, so the first
+  // iteration's products of pair -1 add nothing and the phases need no
+  // branch on the step.
   {
     const uint4 z = make_uint4(0, 0, 0, 0);
-    uint4* const z3 = reinterpret_cast<uint4*>(st3);
 #pragma unroll
-    for (int i = 0; i < STAGE / 16 / 512; ++i) z3[i * 512 + tid] = z;
-    if (tid < (STAGE / 16) % 512) z3[(STAGE / 16 / 512) * 512 + tid] = z;
-    uint4* const zp = reinterpret_cast<uint4*>(pb1);
+    for (int t = 0; t < 2; ++t) {
+      uint4* const zs = reinterpret_cast<uint4*>(t == 0 ? s6 : s7);
 #pragma unroll
-    for (int i = 0; i < PBUF / 16 / 512; ++i) zp[i * 512 + tid] = z;
+      for (int i = 0; i < STAGE / 16 / 512; ++i) zs[i * 512 + tid] = z;
+      if (tid < (STAGE / 16) % 512) zs[(STAGE / 16 / 512) * 512 + tid] = z;
+    }
+    uint4* const zp = reinterpret_cast<uint4*>(pbf);
+#pragma unroll
+    for (int i = 0; i < 2 * PBUF / 16 / 512; ++i) zp[i * 512 + tid] = z;
   }
-  f32x16 sdp;        // S(j) (P wave) or dP(j) (partner)
-  bf16x8 pd[2];      // P(j) (P wave) or dS(j - 1) (partner)
+  f32x16 sdp[2];    // S (P wave) or dP (partner) of the two steps
+  bf16x8 pd[2][2];  // P (P wave) or dS (partner) of the two steps
 #pragma unroll
-  for (int t = 0; t < 16; ++t) sdp[t] = 0.f;
+  for (int h = 0; h < 2; ++h) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+    for (int t = 0; t < 16; ++t) sdp[h][t] = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) pd[i][e] = (__bf16)0.f;
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pd[h][i][e] = (__bf16)0.f;
+  }
+  int j2 = 0;  // first step of the current double step
+
   // Each role runs its own copy of the loop: with one loop and a branch on
   // the role inside every phase, the two roles' accumulators met at every
-  // phase end and the compiler copied them between registers there (about
-  // 40 64-bit moves per step in the vector phase). The barrier sequence is
-  // the same in both loops: two per step, the same step count.
-#define DKDV_HEAD(NXT)                                        \
-  __builtin_amdgcn_s_waitcnt(wait_vmcnt_lgkm0(PER_STAGE));    \
+  // phase end and the compiler copied them between registers there. The
+  // barrier sequence is the same in both loops: two per iteration, the
+  // same iteration count.
+#define DKDV_HEAD(NA, NB)                                     \
+  __builtin_amdgcn_s_waitcnt(wait_vmcnt_lgkm0(2 * PER_STAGE)); \
   asm volatile("s_barrier" ::: "memory");                     \
-  issue(ip, NXT);                                             \
+  issue(ip, NA);                                              \
+  next(ip);                                                   \
+  issue(ip, NB);                                              \
   next(ip);
 #define DKDV_MID                                              \
   __builtin_amdgcn_s_waitcnt(wait_vmcnt_lgkm0(63));           \
   asm volatile("s_barrier" ::: "memory");
-  // P wave: phase A products of step j-1 and scores of step j (MFMA),
-  // phase B the softmax of step j (VALU)
-#define DKDV_STEP_P(CUR, PREV, NXT, PC, PP)                   \
+  // P wave: phase A products of pair J-1 and scores of pair J (MFMA),
+  // phase B the softmax of pair J (VALU)
+#define DKDV_STEP_P(CA, CB, PA, PB, NA, NB)                   \
   {                                                           \
-    DKDV_HEAD(NXT)                                            \
+    DKDV_HEAD(NA, NB)                                         \
     __builtin_amdgcn_s_setprio(1);                            \
-    product(pd, PREV + OD);                                   \
-    scores(CUR + OQ, sdp);                                    \
-    schedule_matrix_phase();                                  \
+    product(pd[0], PA + OD);                                  \
+    product(pd[1], PB + OD);                                  \
+    scores(CA + OQ, sdp[0]);                                  \
+    scores(CB + OQ, sdp[1]);                                  \
+    schedule_matrix_phase2();                                 \
     __builtin_amdgcn_s_setprio(0);                            \
     DKDV_MID                                                  \
-    p_softmax(cp.rb, CUR, sdp, pd, PC);                       \
+    p_softmax(cp.rb, CA, sdp[0], pd[0], pbf, true);           \
     next(cp);                                                 \
+    p_softmax(cp.rb, CB, sdp[1], pd[1], pbf + PBUF, j2 + 1 < n_blocks); \
+    next(cp);                                                 \
+    j2 += 2;                                                  \
   }
-  // partner: phase A dS of step j-1 (VALU), phase B its products and the
-  // dP scores of step j (MFMA)
-#define DKDV_STEP_D(CUR, PREV, NXT, PC, PP)                   \
+  // partner: phase A dS of pair J-1 (VALU), phase B its products and the
+  // dP scores of pair J (MFMA)
+#define DKDV_STEP_D(CA, CB, PA, PB, NA, NB)                   \
   {                                                           \
-    DKDV_HEAD(NXT)                                            \
-    p_ds(PREV, PP, sdp, pd);                                  \
+    DKDV_HEAD(NA, NB)                                         \
+    p_ds(PA, pbf, sdp[0], pd[0]);                             \
+    p_ds(PB, pbf + PBUF, sdp[1], pd[1]);                      \
     DKDV_MID                                                  \
     __builtin_amdgcn_s_setprio(1);                            \
-    product(pd, PREV + OQ);                                   \
-    scores(CUR + OD, sdp);                                    \
-    schedule_matrix_phase();                                  \
+    product(pd[0], PA + OQ);                                  \
+    product(pd[1], PB + OQ);                                  \
+    scores(CA + OD, sdp[0]);                                  \
+    scores(CB + OD, sdp[1]);                                  \
+    schedule_matrix_phase2();                                 \
     __builtin_amdgcn_s_setprio(0);                            \
   }
   // (guarded steps rather than early exits: one loop exit keeps the
   // accumulators in place instead of copying them at every exit)
 #define DKDV_LOOP(STEP)                                       \
   {                                                           \
-    int i = 0;                                                \
-    for (; i + 4 <= n_blocks; i += 4) {                       \
-      STEP(st0, st3, st2, pb0, pb1);                          \
-      STEP(st1, st0, st3, pb1, pb0);                          \
-      STEP(st2, st1, st0, pb0, pb1);                          \
-      STEP(st3, st2, st1, pb1, pb0);                          \
+    int jj = 0;                                               \
+    for (; jj + 4 <= n_pairs; jj += 4) {                      \
+      STEP(s0, s1, s6, s7, s4, s5);                           \
+      STEP(s2, s3, s0, s1, s6, s7);                           \
+      STEP(s4, s5, s2, s3, s0, s1);                           \
+      STEP(s6, s7, s4, s5, s2, s3);                           \
     }                                                         \
-    if (i < n_blocks) STEP(st0, st3, st2, pb0, pb1);          \
-    if (i + 1 < n_blocks) STEP(st1, st0, st3, pb1, pb0);      \
-    if (i + 2 < n_blocks) STEP(st2, st1, st0, pb0, pb1);      \
+    if (jj < n_pairs) STEP(s0, s1, s6, s7, s4, s5);           \
+    if (jj + 1 < n_pairs) STEP(s2, s3, s0, s1, s6, s7);       \
+    if (jj + 2 < n_pairs) STEP(s4, s5, s2, s3, s0, s1);       \
     __builtin_amdgcn_s_waitcnt(wait_vmcnt_lgkm0(0));          \
     asm volatile("s_barrier" ::: "memory");                   \
   }
-  // the last step's remaining work: dV (P wave) and dS then dK (partner) of
-  // step n_blocks - 1 (slot (n_blocks - 1) % 4, P buffer of its parity); the
-  // stages issued past the end land before the kernel exits
-  const char* const pl = (last & 1) ? pb1 : pb0;
-  const int slot = last & 3;
-  const char* const sl = slot == 0 ? st0 : slot == 1 ? st1 : slot == 2 ? st2 : st3;
+  // the last pair's remaining work: dV (P wave) and dS then dK (partner) of
+  // pair n_pairs - 1 (slot pair (n_pairs - 1) % 4); the loads issued past
+  // the end land before the kernel exits
+  const int lp = (n_pairs - 1) & 3;
+  const char* const la = lp == 0 ? s0 : lp == 1 ? s2 : lp == 2 ? s4 : s6;
+  const char* const lb = lp == 0 ? s1 : lp == 1 ? s3 : lp == 2 ? s5 : s7;
   if (pwave) {
     DKDV_LOOP(DKDV_STEP_P)
-    if (n_blocks > 0) product(pd, sl + OD);
+    if (n_blocks > 0) {
+      product(pd[0], la + OD);
+      product(pd[1], lb + OD);
+    }
   } else {
     DKDV_LOOP(DKDV_STEP_D)
     if (n_blocks > 0) {
-      p_ds(sl, pl, sdp, pd);
-      product(pd, sl + OQ);
+      p_ds(la, pbf, sdp[0], pd[0]);
+      p_ds(lb, pbf + PBUF, sdp[1], pd[1]);
+      product(pd[0], la + OQ);
+      product(pd[1], lb + OQ);
     }
   }
 #undef DKDV_LOOP
