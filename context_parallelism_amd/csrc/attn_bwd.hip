@@ -433,7 +433,10 @@ void dkdv_kernel(const BwdArgs a) {
   constexpr int OQ = 0, OD = ROWT, OREC = 2 * ROWT;
   constexpr int STAGE = 2 * ROWT + 2048;
   constexpr int REC_BYTES = 4 * RBK * 4;
-  constexpr int PER_STAGE = 2 * CH + 1;  // LDS-DMA instructions per wave per slot
+  // LDS-DMA instructions per partner wave per slot: the four partner waves
+  // issue every load (two 1-KiB pieces of Q and of dO, and a record piece);
+  // the P waves, whose matrix phase starts right after the barrier, issue none
+  constexpr int PER_STAGE = 4 * CH + 1;
   // P of one step, from the P wave of each pair to its partner: bf16, in the
   // register order of the P wave (two 16-byte pieces per lane)
   constexpr int PBUF = 4 * 2 * 1024;
@@ -477,10 +480,11 @@ void dkdv_kernel(const BwdArgs a) {
   // LDS-DMA offsets. Q and dO row tiles are 32 rows x 256 B, swizzled by
   // tile_swizzle: wave w fills rows 4w..4w+3 of each.
   const int row_bytes = a.H * D * 2;
-  int ngo;
-  {
-    const int r = 4 * wave + (lane >> 4), p = lane & 15;
-    ngo = r * row_bytes + 16 * (p ^ tile_swizzle(r));
+  int ngo[2];  // partner wave of pair p: rows 4 (p + 4 i) .. + 3, i = 0, 1
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = 4 * (pair + 4 * i) + (lane >> 4), p = lane & 15;
+    ngo[i] = r * row_bytes + 16 * (p ^ tile_swizzle(r));
   }
   // the (row block, head) steps: rb in [rb0, rb1) outer, the query heads of
   // KV head g (a.group of them) inner
@@ -510,9 +514,15 @@ void dkdv_kernel(const BwdArgs a) {
     const __amdgpu_buffer_rsrc_t qr = make_rsrc(static_cast<const char*>(a.qr) + noff, valid);
     const __amdgpu_buffer_rsrc_t dr = make_rsrc(static_cast<const char*>(a.dout) + noff, valid);
     const __amdgpu_buffer_rsrc_t rr = make_rsrc(a.rec + (int64_t(h) * a.nrb + rb) * (4 * RBK), REC_BYTES);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(qr, (lds_void*)(st + OQ + wave * 1024), 16, ngo, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(dr, (lds_void*)(st + OD + wave * 1024), 16, ngo, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (lds_void*)(st + OREC + wave * 256), 4, wave * 256 + 4 * lane,
+    if (pwave) return;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(qr, (lds_void*)(st + OQ + (pair + 4 * i) * 1024), 16, ngo[i], 0, 0,
+                                               0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(dr, (lds_void*)(st + OD + (pair + 4 * i) * 1024), 16, ngo[i], 0, 0,
+                                               0);
+    }
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (lds_void*)(st + OREC + pair * 256), 4, pair * 256 + 4 * lane,
                                              0, 0, 0);
   };
   // A operands of S (Q) and dP (dO): lane reads row sigma(kl) of the tile
@@ -556,13 +566,29 @@ void dkdv_kernel(const BwdArgs a) {
   };
   // P wave, step j in slot st: the mask on S, P = exp2(S c2 - lse log2 e)
   // (0 for pad rows, whose record holds +inf), P to the partner
-  auto p_softmax = [&](int rb, const char* st, f32x16& s, bf16x8 (&pa)[2], char* pbuf, bool valid) {
+  // The softmax inputs that do not depend on S: the row block's bounds (an
+  // 8-byte scalar load) and the rows' lse log2 e from the slot's record,
+  // loaded at the end of the P wave's matrix phase so that their latency
+  // passes under the phase barrier.
+  struct SoftIn {
+    int64_t bounds;
+    f32x4 l2[2][2];
+  };
+  auto p_softmax_in = [&](int rb, const char* st, SoftIn& in) {
+    const int* const rec = reinterpret_cast<const int*>(st + OREC);
+    in.bounds = *(const_ptr<int64_t>)(blk + 2 * rb);
+#pragma unroll
+    for (int run = 0; run < 2; ++run)
+#pragma unroll
+      for (int q4 = 0; q4 < 2; ++q4)
+        in.l2[run][q4] = *reinterpret_cast<const f32x4*>(rec + 16 * run + 8 * hh + 4 * q4);
+  };
+  auto p_softmax = [&](const SoftIn& in, const char* st, f32x16& s, bf16x8 (&pa)[2], char* pbuf, bool valid) {
     const int* const rec = reinterpret_cast<const int*>(st + OREC);
     // every row of the block sees every key of the pair unless the block
     // holds a causal edge or a sample boundary; then S = -inf where the key
     // is outside [sample start, row's global id]
-    // (both bounds in one 8-byte scalar load, tested without short-circuit)
-    const int64_t bounds = *(const_ptr<int64_t>)(blk + 2 * rb);
+    const int64_t bounds = in.bounds;
     if (!((int(bounds) <= kw0) & (kw0 + 31 <= int(bounds >> 32)))) {
 #pragma unroll
       for (int run = 0; run < 2; ++run)
@@ -583,7 +609,7 @@ void dkdv_kernel(const BwdArgs a) {
     for (int run = 0; run < 2; ++run)
 #pragma unroll
       for (int q4 = 0; q4 < 2; ++q4) {
-        const f32x4 l2 = *reinterpret_cast<const f32x4*>(rec + 16 * run + 8 * hh + 4 * q4);
+        const f32x4 l2 = in.l2[run][q4];
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           pa[run][4 * q4 + e] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * run + 4 * q4 + e], c2, -l2[e]));
@@ -672,14 +698,15 @@ void dkdv_kernel(const BwdArgs a) {
       for (int e = 0; e < 8; ++e) pd[h][i][e] = (__bf16)0.f;
   }
   int j2 = 0;  // first step of the current double step
+  SoftIn sin[2];  // the P wave's softmax inputs of the two steps
 
   // Each role runs its own copy of the loop: with one loop and a branch on
   // the role inside every phase, the two roles' accumulators met at every
   // phase end and the compiler copied them between registers there. The
   // barrier sequence is the same in both loops: two per iteration, the
   // same iteration count.
-#define DKDV_HEAD(NA, NB)                                     \
-  __builtin_amdgcn_s_waitcnt(wait_vmcnt_lgkm0(2 * PER_STAGE)); \
+#define DKDV_HEAD(NA, NB, VM)                                 \
+  __builtin_amdgcn_s_waitcnt(wait_vmcnt_lgkm0(VM));           \
   asm volatile("s_barrier" ::: "memory");                     \
   issue(ip, NA);                                              \
   next(ip);                                                   \
@@ -692,26 +719,29 @@ void dkdv_kernel(const BwdArgs a) {
   // phase B the softmax of pair J (VALU)
 #define DKDV_STEP_P(CA, CB, PA, PB, NA, NB)                   \
   {                                                           \
-    DKDV_HEAD(NA, NB)                                         \
+    DKDV_HEAD(NA, NB, 0)                                      \
     __builtin_amdgcn_s_setprio(1);                            \
     product(pd[0], PA + OD);                                  \
     product(pd[1], PB + OD);                                  \
     scores(CA + OQ, sdp[0]);                                  \
     scores(CB + OQ, sdp[1]);                                  \
     schedule_matrix_phase2();                                 \
+    __builtin_amdgcn_sched_barrier(0);                        \
+    p_softmax_in(cp.rb, CA, sin[0]);                          \
+    next(cp);                                                 \
+    p_softmax_in(cp.rb, CB, sin[1]);                          \
+    next(cp);                                                 \
     __builtin_amdgcn_s_setprio(0);                            \
     DKDV_MID                                                  \
-    p_softmax(cp.rb, CA, sdp[0], pd[0], pbf, true);           \
-    next(cp);                                                 \
-    p_softmax(cp.rb, CB, sdp[1], pd[1], pbf + PBUF, j2 + 1 < n_blocks); \
-    next(cp);                                                 \
+    p_softmax(sin[0], CA, sdp[0], pd[0], pbf, true);          \
+    p_softmax(sin[1], CB, sdp[1], pd[1], pbf + PBUF, j2 + 1 < n_blocks); \
     j2 += 2;                                                  \
   }
   // partner: phase A dS of pair J-1 (VALU), phase B its products and the
   // dP scores of pair J (MFMA)
 #define DKDV_STEP_D(CA, CB, PA, PB, NA, NB)                   \
   {                                                           \
-    DKDV_HEAD(NA, NB)                                         \
+    DKDV_HEAD(NA, NB, 2 * PER_STAGE)                          \
     p_ds(PA, pbf, sdp[0], pd[0]);                             \
     p_ds(PB, pbf + PBUF, sdp[1], pd[1]);                      \
     DKDV_MID                                                  \
