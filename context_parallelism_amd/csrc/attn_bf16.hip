@@ -382,9 +382,7 @@ void attn_rank_bf16_d128_kernel(const AttnArgs a) {
   // The unit's key spans: every step's spans, contiguous and in step order.
   const const_ptr<SpanRec> spans = scalar_view(a.spans) + steps[0].span_begin;
   const int n_spans = steps[n_steps - 1].span_end - steps[0].span_begin;
-  auto span_tiles = [&](int i) { return (spans[i].k1 - (spans[i].k0 & ~7) + BN - 1) / BN; };
-  int n_tiles = 0;
-  for (int i = 0; i < n_spans; ++i) n_tiles += span_tiles(i);
+  const int n_tiles = unit.n_tiles;  // the planner counted the unit's 64-key tiles
   auto start = [&](TileCursor& c) {
     c.span = 0;
     c.k0 = spans[0].k0;

@@ -200,8 +200,8 @@ void dq_kernel(const BwdArgs a) {
   static_assert(RB * G == 4, "4 waves");
   const const_ptr<SpanRec> spans = scalar_view(a.spans) + steps[0].span_begin;
   const int n_spans = steps[n_steps - 1].span_end - steps[0].span_begin;
-  int n_tiles = 0;
-  for (int i = 0; i < n_spans; ++i) n_tiles += (spans[i].k1 - (spans[i].k0 & ~7) + BN - 1) / BN;
+  static_assert(BN == kDqBlockN, "the backward plan counts dQ key tiles");
+  const int n_tiles = unit.n_tiles;  // the planner counted the unit's BN-key tiles
   auto start = [&](Cursor& c) {
     c.span = 0;
     c.k0 = spans[0].k0;

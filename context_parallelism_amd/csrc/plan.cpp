@@ -202,13 +202,16 @@ void build_plan(const Meta& m, int32_t bm, int32_t bn, Plan& p) {
   std::stable_sort(units.begin(), units.end(),
                    [](const PendingUnit& x, const PendingUnit& y) { return x.cost > y.cost; });
   p.units.reserve(units.size());
-  for (const PendingUnit& u : units) p.units.push_back(u.u);
+  for (PendingUnit& u : units) {
+    u.u.n_tiles = int32_t(u.cost);
+    p.units.push_back(u.u);
+  }
   // step units: every entry alone, same order as the entries below
   {
     std::vector<PendingUnit> su;
     su.reserve(pend.size());
     for (size_t i = 0; i < pend.size(); ++i)
-      su.push_back({UnitRec{pend[i].e.tile, int32_t(i), int32_t(i) + 1, 0}, pend[i].cost});
+      su.push_back({UnitRec{pend[i].e.tile, int32_t(i), int32_t(i) + 1, int32_t(pend[i].cost)}, pend[i].cost});
     std::stable_sort(su.begin(), su.end(),
                      [](const PendingUnit& x, const PendingUnit& y) { return x.cost > y.cost; });
     p.step_units.reserve(su.size());
@@ -223,7 +226,7 @@ void build_plan(const Meta& m, int32_t bm, int32_t bn, Plan& p) {
 
 void build_bwd_plan(const Meta& m, int32_t rows_bm, BwdPlan& b) {
   b = BwdPlan();
-  build_plan(m, rows_bm, kBlockN, b.rows);
+  build_plan(m, rows_bm, kDqBlockN, b.rows);
   const std::vector<int32_t>& index = b.rows.index;
   struct Pending { KeyTileRec k; int64_t cost; };
   std::vector<Pending> pend;

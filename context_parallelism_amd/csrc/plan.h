@@ -81,8 +81,10 @@ struct TileRec { int32_t local0, nrows, g0, pad; };          // a row tile
 struct EntryRec { int32_t tile, step, span_begin, span_end; };  // (tile, step) work
 struct SpanRec { int32_t k0, k1; };                          // global keys [k0, k1)
 // All ring steps of one row tile: tile_entries[e0, e1), in step order; their
-// key spans are contiguous in the span list.
-struct UnitRec { int32_t tile, e0, e1, pad; };
+// key spans are contiguous in the span list. n_tiles: the key tiles of the
+// plan's bn keys a kernel walks over those spans, each span from its start
+// rounded down to 8 keys (counted here so the kernel need not walk the spans).
+struct UnitRec { int32_t tile, e0, e1, n_tiles; };
 
 struct Plan {
   int32_t bm = 0, bn = 0;
@@ -114,6 +116,7 @@ void build_plan(const Meta& m, int32_t bm, int32_t bn, Plan& p);
 // of that sample with a global id >= k0 (other rows of those blocks are
 // masked by their index).
 constexpr int kBwdRowBlock = 32;   // rank-local rows per dK/dV row block
+constexpr int kDqBlockN = 32;      // keys per dQ key tile (the backward plan's bn)
 constexpr int kBwdKeyTile = 128;   // keys per dK/dV workgroup (4 waves x 32)
 struct KeyTileRec { int32_t k0, k1, rb0, rb1, s0, s1, pad0, pad1; };
 

@@ -136,10 +136,18 @@ int32_t check_plan(const Meta& m, const Plan& p) {
   // units: one per tile that has entries, its entries contiguous, all of
   // that tile, spans contiguous across the unit's steps
   std::vector<uint8_t> unit_seen(p.tiles.size(), 0);
+  // key tiles of p.bn keys over a unit's spans, each from its start rounded down to 8
+  auto walk_tiles = [&](int32_t e0, int32_t e1) {
+    int64_t n = 0;
+    for (int32_t i = p.tile_entries[size_t(e0)].span_begin; i < p.tile_entries[size_t(e1 - 1)].span_end; ++i)
+      n += (int64_t(p.spans[size_t(i)].k1) - (p.spans[size_t(i)].k0 & ~7) + p.bn - 1) / p.bn;
+    return n;
+  };
   for (const UnitRec& u : p.units) {
     if (u.tile < 0 || size_t(u.tile) >= p.tiles.size() || unit_seen[size_t(u.tile)]) return CP_EINVAL;
     unit_seen[size_t(u.tile)] = 1;
     if (u.e0 < 0 || u.e0 >= u.e1 || size_t(u.e1) > p.tile_entries.size()) return CP_EINVAL;
+    if (int64_t(u.n_tiles) != walk_tiles(u.e0, u.e1)) return CP_EINVAL;
     for (int32_t e = u.e0; e < u.e1; ++e) {
       if (p.tile_entries[size_t(e)].tile != u.tile) return CP_EINVAL;
       if (e > u.e0 && p.tile_entries[size_t(e)].span_begin != p.tile_entries[size_t(e - 1)].span_end)
@@ -156,6 +164,7 @@ int32_t check_plan(const Meta& m, const Plan& p) {
       return CP_EINVAL;
     su_seen[size_t(u.e0)] = 1;
     if (p.tile_entries[size_t(u.e0)].tile != u.tile) return CP_EINVAL;
+    if (int64_t(u.n_tiles) != walk_tiles(u.e0, u.e1)) return CP_EINVAL;
   }
 
   // the spans expose every visible pair once: the rank's real pair count
