@@ -682,6 +682,10 @@ void attn_rank_bf16_d128_kernel(const AttnArgs a) {
       matrix(v1s, k1s, true, k0s, v0s);
       sync();
     }
+    // The last matrix phase's loads (past the end of the keys) still write
+    // their slots; they land before the barrier, as the epilogue reuses the
+    // slots.
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     sync();  // group 1's last matrix phase
   } else {
     sync();  // prologue loads
@@ -728,9 +732,16 @@ void attn_rank_bf16_d128_kernel(const AttnArgs a) {
   }
   // The online softmax ran across every ring step of the unit, so the
   // running output, sum and reference already merge all steps' blocks.
-  if (!row_ok) return;
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
-  __bf16* const po = static_cast<__bf16*>(a.out) + (int64_t(lrow) * a.H + h) * D + 4 * hh;
+  if (row_ok && hh == 0) a.lse[int64_t(h) * a.R + lrow] = lt > 0.f ? m_ref * a.scale + logf(lt) : -INFINITY;
+  // The output goes out through LDS: a lane holds 4 consecutive d of one
+  // row per (db, tq), so a direct store writes 16 bytes into each of 32 rows
+  // 8 KiB apart. Each wave writes its 32 rows x 256 bytes into its own 8 KiB
+  // of the K/V slots (16-byte granules XOR-swizzled by row), reads them
+  // back as whole rows and stores 256-byte rows, 16 lanes each, four rows
+  // per instruction. After the last barrier no LDS read of a matrix phase
+  // and no LDS-DMA load is outstanding, so the slots are free.
+  char* const stg = (wave < 2 ? k0s : wave < 4 ? k1s : wave < 6 ? v0s : v1s) + (wave & 1) * 8192;
 #pragma unroll
   for (int db = 0; db < ND; ++db)
 #pragma unroll
@@ -738,9 +749,18 @@ void attn_rank_bf16_d128_kernel(const AttnArgs a) {
       typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
       const bf16x4 val = {(__bf16)(o[db][4 * tq] * inv), (__bf16)(o[db][4 * tq + 1] * inv),
                           (__bf16)(o[db][4 * tq + 2] * inv), (__bf16)(o[db][4 * tq + 3] * inv)};
-      *reinterpret_cast<bf16x4*>(po + 32 * db + 8 * tq) = val;
+      *reinterpret_cast<bf16x4*>(stg + ql * 256 + 16 * ((4 * db + tq) ^ (ql & 15)) + 8 * hh) = val;
     }
-  if (hh == 0) a.lse[int64_t(h) * a.R + lrow] = lt > 0.f ? m_ref * a.scale + logf(lt) : -INFINITY;
+  const int gran = lane & 15;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int r = 4 * k + (lane >> 4);  // row of the wave's 32
+    const uint4 val = *reinterpret_cast<const uint4*>(stg + r * 256 + 16 * (gran ^ (r & 15)));
+    if (rsub * 32 + r < tile.nrows) {
+      char* const dst = static_cast<char*>(a.out) + ((int64_t(tile.local0 + rsub * 32 + r) * a.H + h) * D) * 2;
+      *reinterpret_cast<uint4*>(dst + 16 * gran) = val;
+    }
+  }
 }
 
 template <int G>

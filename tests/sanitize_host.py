@@ -126,7 +126,8 @@ def drive(lib_path: str) -> int:
                                                        ctypes.byref(b)) == 0, (cu, P, r, H, Hkv, D, dtype)
         checked += 1
 
-    shapes = [(32, 8, 128, 1), (4, 4, 64, 1), (6, 2, 128, 0), (8, 2, 64, 1)]
+    # (64 MHA heads: one head per workgroup, 64 head groups per row tile)
+    shapes = [(32, 8, 128, 1), (4, 4, 64, 1), (6, 2, 128, 0), (8, 2, 64, 1), (64, 64, 128, 1)]
     # the five workloads' metadata (rank shares only: plans are validated,
     # so the sizes are kept to what runs in seconds)
     workloads = [
