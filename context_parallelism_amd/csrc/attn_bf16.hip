@@ -644,6 +644,12 @@ void attn_rank_bf16_d128_kernel(const AttnArgs a) {
     fence_s();
   };
 
+  // A wave with no rows (in a row tile's tail) runs only the phase
+  // barriers, and in group 0 its share of the K/V loads: no matrix or
+  // softmax work. The kernel is power-bound, so work skipped on some waves
+  // raises the clock of all.
+  const bool idle = tile.nrows <= rsub * 32;
+
   if (grp == 0) {
     // prologue: K(0) into the slot of group -1 (k1s), group 0 into slot 0
     load_group(krsrc(ck), vrsrc(cv), k1s, v0s);  // V(0) and, harmlessly, K(0) twice
@@ -657,10 +663,25 @@ void attn_rank_bf16_d128_kernel(const AttnArgs a) {
     }
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     sync();
-    qk(k1s);  // phase 0
+    if (!idle) qk(k1s);  // phase 0
     fence_s();
     sync();
-    for (int t = 0; t < n_tiles; t += 2) {
+    for (int t = 0; idle && t < n_tiles; t += 2) {  // (idle wave: loads only)
+      advance(ck);
+      advance(cv);
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      sync();
+      load_group(krsrc(ck), vrsrc(cv), k1s, v1s);
+      sync();
+      if (t + 1 >= n_tiles) break;
+      advance(ck);
+      advance(cv);
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      sync();
+      load_group(krsrc(ck), vrsrc(cv), k0s, v0s);
+      sync();
+    }
+    for (int t = 0; !idle && t < n_tiles; t += 2) {
       // phase 2t+1: S(t); prepare load group t+1
       advance(ck);
       advance(cv);
@@ -690,10 +711,17 @@ void attn_rank_bf16_d128_kernel(const AttnArgs a) {
   } else {
     sync();  // prologue loads
     sync();  // phase 0
-    qk(k1s);  // phase 1
+    if (!idle) qk(k1s);  // phase 1
     fence_s();
     sync();
-    for (int t = 0; t < n_tiles; t += 2) {
+    for (int t = 0; idle && t < n_tiles; t += 2) {  // (idle wave: barriers only)
+      sync();
+      sync();
+      if (t + 1 >= n_tiles) break;
+      sync();
+      sync();
+    }
+    for (int t = 0; !idle && t < n_tiles; t += 2) {
       softmax(cs);
       advance(cs);
       fence_p();
