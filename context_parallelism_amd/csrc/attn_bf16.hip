@@ -363,10 +363,21 @@ void attn_rank_bf16_d128_kernel(const AttnArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   const int grp = wave >> 2, wg = wave & 3;  // waves w and w+4 share a SIMD
-  const int hg = blockIdx.x % a.n_hg;
+  // Workgroup order: unit-major (unit b / n_hg, head group b % n_hg), or
+  // XCD-major: workgroups go to the XCDs round-robin (b % 8), and XCD x runs
+  // head groups x, x + 8, ... one after another, each over all units.
+  int hg, unit_id;
+  if (a.xcd_major) {
+    const int x = blockIdx.x % 8, slot = blockIdx.x / 8;
+    hg = x + 8 * (slot / a.n_units);
+    unit_id = slot % a.n_units;
+  } else {
+    hg = blockIdx.x % a.n_hg;
+    unit_id = blockIdx.x / a.n_hg;
+  }
   // plan records through scalar views: their loads are scalar, so a wait
   // for one never waits for the K/V loads in flight
-  const UnitRec unit = scalar_load(a.units, blockIdx.x / a.n_hg);
+  const UnitRec unit = scalar_load(a.units, unit_id);
   const TileRec tile = scalar_load(a.tiles, unit.tile);
   const const_ptr<EntryRec> steps = scalar_view(a.tile_entries) + unit.e0;
   const int n_steps = unit.e1 - unit.e0;

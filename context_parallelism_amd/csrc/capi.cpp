@@ -145,6 +145,8 @@ cp_status run_fwd(const Workspace& w, const void* q, const void* k, const void* 
   a.scale_log2 = float(1.4426950408889634 / std::sqrt(double(head_dim)));
   const int n_entries = int(w.plan.entries.size());
   a.per_step = w.unit_per_step ? 1 : 0;
+  a.xcd_major = w.xcd_major ? 1 : 0;
+  a.n_units = int32_t(w.launch_units().size());
   if (w.unit_kernel && !w.unit_per_step) {
     // all ring steps of a row tile in one workgroup, merged in the kernel
     if (launch_attn_bf16_units(a, w.shape.heads_per_wg, int(w.plan.units.size()), s) != hipSuccess)

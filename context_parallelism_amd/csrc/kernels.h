@@ -24,6 +24,8 @@ struct AttnArgs {
   void* out;                     // [R, H, D] in the input dtype (unit kernel)
   float* lse;                    // [H, R] fp32 (unit kernel)
   int32_t per_step;              // unit kernel: units of one step, partials for the merge pass
+  int32_t xcd_major;             // unit kernel: XCD-major workgroup order (see xcd_major_pays)
+  int32_t n_units;               // unit kernel: units in the launch
   int32_t R, H, Hkv;
   int32_t n_hg;          // head groups (workgroups per entry)
   int32_t group;         // heads / kv_heads

@@ -110,6 +110,25 @@ void step_ranges(const Meta& m, int32_t sample, int32_t step, std::vector<SpanRe
 // descending key-tile count (`bn` keys per tile).
 void build_plan(const Meta& m, int32_t bm, int32_t bn, Plan& p);
 
+// Workgroup order of the row-tile kernel. Unit-major: workgroup b takes
+// unit b / n_hg (units longest first) and head group b % n_hg. XCD-major:
+// workgroups are dealt round-robin to the 8 XCDs (b % 8), and XCD x takes
+// head groups x, x + 8, ... one after another, each over all units, with the
+// units grouped by sample (samples with the most key tiles first, each
+// sample's units longest first). An XCD's compute units then work on one
+// head and a few samples at a time, whose K/V its L2 can share, where
+// unit-major mixes n_hg / 8 heads and, in cost order, many samples.
+// choose_xcd_major takes XCD-major (and reorders p.units) if n_hg is a
+// multiple of 8 above 8 and its modelled end, on 8 XCDs of 32 compute units
+// (each workgroup its key tiles plus a fixed overhead, dispatched in order
+// to the compute unit of its XCD that frees first), is within
+// kXcdMajorSlack of unit-major's: with few units per head, XCD-major starts
+// the later heads' long units late.
+constexpr int32_t kXcds = 8;
+constexpr int32_t kCusPerXcd = 32;
+constexpr double kXcdMajorSlack = 1.05;
+bool choose_xcd_major(const Meta& m, Plan& p, int32_t n_hg);
+
 // ---------------------------------------------------------------- backward
 // dK/dV work: keys [k0, k1) of one sample [s0, s1) (k1 <= s1), and the
 // 32-row blocks of rank-local rows [32 rb0, 32 rb1) that hold every rank row

@@ -56,6 +56,7 @@ int32_t prepare_workspace(int64_t seq_len, const int32_t* n_img, const int32_t* 
     const int64_t n_hg = heads / w.shape.heads_per_wg;
     w.unit_per_step = schedule == CP_SCHED_PER_STEP ||
                       (schedule == CP_SCHED_AUTO && int64_t(w.plan.units.size()) * n_hg < kUnitMinWorkgroups);
+    w.xcd_major = !w.unit_per_step && choose_xcd_major(w.meta, w.plan, int32_t(n_hg));
   }
   w.off_units = off;
   off = align256(off + w.launch_units().size() * sizeof(UnitRec));

@@ -25,6 +25,7 @@ struct Workspace {
   size_t off_tile_entries = 0, off_units = 0;
   bool unit_kernel = false;  // bf16 head_dim 128: units, one online softmax across the steps
   bool unit_per_step = false;  // ... but one step per unit and the merge pass (small grids)
+  bool xcd_major = false;      // unit kernel, row-tile schedule: XCD-major workgroup order
   const std::vector<UnitRec>& launch_units() const {
     return unit_per_step ? plan.step_units : plan.units;
   }
