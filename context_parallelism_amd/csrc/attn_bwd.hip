@@ -184,8 +184,17 @@ void dq_kernel(const BwdArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int hg = blockIdx.x % a.n_hg;
-  const UnitRec unit = scalar_load(a.units, blockIdx.x / a.n_hg);
+  // unit-major (unit b / n_hg, head group b % n_hg) or XCD-major order
+  int hg, unit_id;
+  if (a.q_xcd_major) {
+    const int x = blockIdx.x % 8, slot = blockIdx.x / 8;
+    hg = x + 8 * (slot / a.n_units);
+    unit_id = slot % a.n_units;
+  } else {
+    hg = blockIdx.x % a.n_hg;
+    unit_id = blockIdx.x / a.n_hg;
+  }
+  const UnitRec unit = scalar_load(a.units, unit_id);
   const TileRec tile = scalar_load(a.tiles, unit.tile);
   const const_ptr<EntryRec> steps = scalar_view(a.tile_entries) + unit.e0;
   const int n_steps = unit.e1 - unit.e0;
@@ -455,8 +464,17 @@ void dkdv_kernel(const BwdArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int pair = wave & 3;           // waves w and w + 4 share a SIMD and 32 keys
   const bool pwave = wave < 4;         // S, P, dV; its partner: dP, dS, dK
-  const int g = blockIdx.x % a.Hkv;
-  const KeyTileRec kt = scalar_load(a.ktiles, blockIdx.x / a.Hkv);
+  // tile-major (key tile b / Hkv, KV head b % Hkv) or XCD-major order
+  int g, kt_id;
+  if (a.kv_xcd_major) {
+    const int x = blockIdx.x % 8, slot = blockIdx.x / 8;
+    g = x + 8 * (slot / a.n_ktiles);
+    kt_id = slot % a.n_ktiles;
+  } else {
+    g = blockIdx.x % a.Hkv;
+    kt_id = blockIdx.x / a.Hkv;
+  }
+  const KeyTileRec kt = scalar_load(a.ktiles, kt_id);
   const const_ptr<int32_t> blk = scalar_view(a.blk);
   const int kl = lane & 31, hh = lane >> 5;
   const int kw0 = kt.k0 + 32 * pair;  // the pair's first key

@@ -303,6 +303,10 @@ cp_status rank_bwd(const void* q, const void* k, const void* v, const void* out,
     a.nrb = w.nrb;
     a.scale = float(1.0 / std::sqrt(double(head_dim)));
     a.scale_log2 = float(1.4426950408889634 / std::sqrt(double(head_dim)));
+    a.q_xcd_major = w.q_xcd_major ? 1 : 0;
+    a.n_units = int32_t(w.plan.rows.units.size());
+    a.kv_xcd_major = w.kv_xcd_major ? 1 : 0;
+    a.n_ktiles = int32_t(w.plan.ktiles.size());
     if (R > 0) {
       const int64_t row_bytes = int64_t(heads) * head_dim * (dtype == CP_DTYPE_BF16 ? 2 : 4);
       if (launch_gather(q, a.index, ws + w.off_qr, R, row_bytes, s) != hipSuccess) return CP_EHIP;

@@ -55,6 +55,8 @@ struct BwdArgs {
   const KeyTileRec* ktiles;
   int32_t R, H, Hkv, n_hg, group, nrb;
   float scale, scale_log2;
+  int32_t q_xcd_major, n_units;     // dQ workgroup order (MFMA kernel; see xcd_major_order)
+  int32_t kv_xcd_major, n_ktiles;   // dK/dV workgroup order (MFMA kernel)
 };
 
 // delta[h][r] = rowsum(dout * out) for every rank row, and the dK/dV row

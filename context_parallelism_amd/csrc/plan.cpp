@@ -7,6 +7,7 @@
 
 #include <algorithm>
 #include <functional>
+#include <map>
 #include <queue>
 
 #include "cpattn.h"
@@ -226,19 +227,20 @@ void build_plan(const Meta& m, int32_t bm, int32_t bn, Plan& p) {
   for (int32_t g : p.index) p.pad_rows += g < 0;
 }
 
-bool choose_xcd_major(const Meta& m, Plan& p, int32_t n_hg) {
-  if (n_hg <= kXcds || n_hg % kXcds != 0 || p.units.empty()) return false;
-  constexpr double kWorkgroupTiles = 4.5;  // a workgroup's fill and drain, in key tiles
-  const int64_t nu = int64_t(p.units.size());
-  // modelled end of a launch of `order`
-  auto finish = [&](const std::vector<UnitRec>& order, bool xcd_major) {
+bool xcd_major_order(const std::vector<int64_t>& cost, const std::vector<int32_t>& sample,
+                     int32_t n_groups, int32_t slots, std::vector<int64_t>& order) {
+  const int64_t n = int64_t(cost.size());
+  if (n_groups <= kXcds || n_groups % kXcds != 0 || n == 0 || slots < 1) return false;
+  constexpr double kWorkgroupCost = 4.5;  // a workgroup's fill and drain, in cost units
+  // modelled end of a launch of the items in `ord`
+  auto finish = [&](const std::vector<int64_t>& ord, bool xcd_major) {
     double end = 0.0;
     for (int32_t x = 0; x < kXcds; ++x) {
       std::priority_queue<double, std::vector<double>, std::greater<double>> free_at;
-      for (int32_t c = 0; c < kCusPerXcd; ++c) free_at.push(0.0);
-      for (int64_t b = x; b < nu * n_hg; b += kXcds) {
-        const int64_t u = xcd_major ? (b / kXcds) % nu : b / n_hg;
-        const double t = free_at.top() + order[size_t(u)].n_tiles + kWorkgroupTiles;
+      for (int32_t c = 0; c < slots; ++c) free_at.push(0.0);
+      for (int64_t b = x; b < n * n_groups; b += kXcds) {
+        const int64_t i = xcd_major ? (b / kXcds) % n : b / n_groups;
+        const double t = free_at.top() + double(cost[size_t(ord[size_t(i)])]) + kWorkgroupCost;
         free_at.pop();
         free_at.push(t);
         end = std::max(end, t);
@@ -246,33 +248,44 @@ bool choose_xcd_major(const Meta& m, Plan& p, int32_t n_hg) {
     }
     return end;
   };
-  // units grouped by sample: samples with the most key tiles first, each
-  // sample's units in their (longest first) order
-  std::vector<int32_t> sample(static_cast<size_t>(nu));
-  std::vector<int64_t> total(m.samples.size(), 0);
-  for (int64_t i = 0; i < nu; ++i) {
-    const int64_t g = p.tiles[size_t(p.units[size_t(i)].tile)].g0;
+  std::vector<int64_t> given(static_cast<size_t>(n));
+  for (int64_t i = 0; i < n; ++i) given[size_t(i)] = i;
+  // grouped by sample: samples with the most work first, then the items'
+  // own order
+  std::map<int32_t, int64_t> total;
+  for (int64_t i = 0; i < n; ++i) total[sample[size_t(i)]] += cost[size_t(i)];
+  std::vector<int64_t> grouped = given;
+  std::stable_sort(grouped.begin(), grouped.end(), [&](int64_t x, int64_t y) {
+    const int32_t a = sample[size_t(x)], b = sample[size_t(y)];
+    if (a == b) return false;
+    const int64_t ta = total[a], tb = total[b];
+    return ta != tb ? ta > tb : a < b;
+  });
+  if (finish(grouped, true) > kXcdMajorSlack * finish(given, false)) return false;
+  order.swap(grouped);
+  return true;
+}
+
+bool choose_xcd_major(const Meta& m, Plan& p, int32_t n_groups, int32_t slots) {
+  const size_t n = p.units.size();
+  std::vector<int64_t> cost(n);
+  std::vector<int32_t> sample(n);
+  for (size_t i = 0; i < n; ++i) {
+    cost[i] = p.units[i].n_tiles;
+    const int64_t g = p.tiles[size_t(p.units[i].tile)].g0;
     int32_t lo = 0, hi = int32_t(m.samples.size()) - 1;
     while (lo < hi) {
       const int32_t mid = (lo + hi + 1) / 2;
       if (m.samples[size_t(mid)].a <= g) lo = mid; else hi = mid - 1;
     }
-    sample[size_t(i)] = lo;
-    total[size_t(lo)] += p.units[size_t(i)].n_tiles;
+    sample[i] = lo;
   }
-  std::vector<int64_t> idx(static_cast<size_t>(nu));
-  for (int64_t i = 0; i < nu; ++i) idx[size_t(i)] = i;
-  std::stable_sort(idx.begin(), idx.end(), [&](int64_t x, int64_t y) {
-    const int32_t a = sample[size_t(x)], b = sample[size_t(y)];
-    if (a == b) return false;  // keep the units' own order
-    if (total[size_t(a)] != total[size_t(b)]) return total[size_t(a)] > total[size_t(b)];
-    return a < b;
-  });
-  std::vector<UnitRec> grouped;
-  grouped.reserve(size_t(nu));
-  for (int64_t i : idx) grouped.push_back(p.units[size_t(i)]);
-  if (finish(grouped, true) > kXcdMajorSlack * finish(p.units, false)) return false;
-  p.units.swap(grouped);
+  std::vector<int64_t> order;
+  if (!xcd_major_order(cost, sample, n_groups, slots, order)) return false;
+  std::vector<UnitRec> units;
+  units.reserve(n);
+  for (int64_t i : order) units.push_back(p.units[size_t(i)]);
+  p.units.swap(units);
   return true;
 }
 

@@ -110,24 +110,29 @@ void step_ranges(const Meta& m, int32_t sample, int32_t step, std::vector<SpanRe
 // descending key-tile count (`bn` keys per tile).
 void build_plan(const Meta& m, int32_t bm, int32_t bn, Plan& p);
 
-// Workgroup order of the row-tile kernel. Unit-major: workgroup b takes
-// unit b / n_hg (units longest first) and head group b % n_hg. XCD-major:
+// Workgroup order of the row-tile kernel (and of the backward's dQ and
+// dK/dV kernels). Item-major: workgroup b takes item b / n_groups (items
+// longest first) and group b % n_groups (head group, or KV head). XCD-major:
 // workgroups are dealt round-robin to the 8 XCDs (b % 8), and XCD x takes
-// head groups x, x + 8, ... one after another, each over all units, with the
-// units grouped by sample (samples with the most key tiles first, each
-// sample's units longest first). An XCD's compute units then work on one
-// head and a few samples at a time, whose K/V its L2 can share, where
-// unit-major mixes n_hg / 8 heads and, in cost order, many samples.
-// choose_xcd_major takes XCD-major (and reorders p.units) if n_hg is a
-// multiple of 8 above 8 and its modelled end, on 8 XCDs of 32 compute units
-// (each workgroup its key tiles plus a fixed overhead, dispatched in order
-// to the compute unit of its XCD that frees first), is within
-// kXcdMajorSlack of unit-major's: with few units per head, XCD-major starts
-// the later heads' long units late.
+// groups x, x + 8, ... one after another, each over all items, with the
+// items grouped by sample (samples with the most work first, each sample's
+// items longest first). An XCD's compute units then work on one head and a
+// few samples at a time, whose K/V (or Q and dO rows) its L2 can share,
+// where item-major mixes n_groups / 8 heads and, in cost order, many
+// samples. xcd_major_order chooses XCD-major if n_groups is a multiple of 8
+// above 8 and its modelled end, on 8 XCDs running `slots` workgroups each
+// (every workgroup its cost plus a fixed overhead, dispatched in order to
+// the slot of its XCD that frees first), is within kXcdMajorSlack of
+// item-major's: with few items per head, XCD-major starts the later heads'
+// long items late. It then returns true and the grouped order of the items
+// (indices into `cost`).
 constexpr int32_t kXcds = 8;
-constexpr int32_t kCusPerXcd = 32;
 constexpr double kXcdMajorSlack = 1.05;
-bool choose_xcd_major(const Meta& m, Plan& p, int32_t n_hg);
+bool xcd_major_order(const std::vector<int64_t>& cost, const std::vector<int32_t>& sample,
+                     int32_t n_groups, int32_t slots, std::vector<int64_t>& order);
+// The same for a plan's units (sample of a unit: that of its tile), which it
+// reorders when it chooses XCD-major.
+bool choose_xcd_major(const Meta& m, Plan& p, int32_t n_groups, int32_t slots);
 
 // ---------------------------------------------------------------- backward
 // dK/dV work: keys [k0, k1) of one sample [s0, s1) (k1 <= s1), and the

@@ -56,7 +56,8 @@ int32_t prepare_workspace(int64_t seq_len, const int32_t* n_img, const int32_t* 
     const int64_t n_hg = heads / w.shape.heads_per_wg;
     w.unit_per_step = schedule == CP_SCHED_PER_STEP ||
                       (schedule == CP_SCHED_AUTO && int64_t(w.plan.units.size()) * n_hg < kUnitMinWorkgroups);
-    w.xcd_major = !w.unit_per_step && choose_xcd_major(w.meta, w.plan, int32_t(n_hg));
+    // one workgroup of the row-tile kernel per compute unit: 32 per XCD
+    w.xcd_major = !w.unit_per_step && choose_xcd_major(w.meta, w.plan, int32_t(n_hg), 32);
   }
   w.off_units = off;
   off = align256(off + w.launch_units().size() * sizeof(UnitRec));
@@ -117,6 +118,25 @@ int32_t prepare_bwd_workspace(int64_t seq_len, const int32_t* n_img, const int32
   st = check_bwd_plan(w.meta, w.plan);
   if (st != CP_OK) return st;
 #endif
+  if (w.mfma) {
+    // workgroup orders of the MFMA kernels: dQ runs two workgroups per
+    // compute unit (64 per XCD), dK/dV one (32)
+    w.q_xcd_major = choose_xcd_major(w.meta, w.plan.rows, w.n_hg, 64);
+    std::vector<int64_t> cost(w.plan.ktiles.size());
+    std::vector<int32_t> sample(w.plan.ktiles.size());
+    for (size_t i = 0; i < cost.size(); ++i) {
+      cost[i] = w.plan.ktiles[i].rb1 - w.plan.ktiles[i].rb0;
+      sample[i] = w.plan.ktiles[i].s0;  // the sample's first token identifies it
+    }
+    std::vector<int64_t> order;
+    w.kv_xcd_major = xcd_major_order(cost, sample, kv_heads, 32, order);
+    if (w.kv_xcd_major) {
+      std::vector<KeyTileRec> kt;
+      kt.reserve(order.size());
+      for (int64_t i : order) kt.push_back(w.plan.ktiles[size_t(i)]);
+      w.plan.ktiles.swap(kt);
+    }
+  }
   const Plan& p = w.plan.rows;
   const size_t R = size_t(w.meta.rows);
   size_t off = 0;

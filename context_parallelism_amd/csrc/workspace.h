@@ -58,6 +58,7 @@ struct BwdWorkspace {
   Meta meta;
   BwdPlan plan;
   bool mfma = false;  // bf16 with head_dim 128: the MFMA kernels; otherwise the fp32 FMA kernels
+  bool q_xcd_major = false, kv_xcd_major = false;  // XCD-major orders of dQ and dK/dV (MFMA kernels)
   int32_t heads = 0, kv_heads = 0, head_dim = 0;
   int32_t heads_per_wg = 1, rows_per_tile = 0, n_hg = 0;
   size_t off_index = 0, off_tiles = 0, off_spans = 0, off_tile_entries = 0, off_units = 0,
