@@ -231,6 +231,9 @@ bool xcd_major_order(const std::vector<int64_t>& cost, const std::vector<int32_t
                      int32_t n_groups, int32_t slots, std::vector<int64_t>& order) {
   const int64_t n = int64_t(cost.size());
   if (n_groups <= kXcds || n_groups % kXcds != 0 || n == 0 || slots < 1) return false;
+  // the model costs a heap operation per workgroup on every call: beyond
+  // kXcdModelMaxWorkgroups the order stays item-major
+  if (n * n_groups > kXcdModelMaxWorkgroups) return false;
   constexpr double kWorkgroupCost = 4.5;  // a workgroup's fill and drain, in cost units
   // modelled end of a launch of the items in `ord`
   auto finish = [&](const std::vector<int64_t>& ord, bool xcd_major) {

@@ -125,9 +125,11 @@ void build_plan(const Meta& m, int32_t bm, int32_t bn, Plan& p);
 // the slot of its XCD that frees first), is within kXcdMajorSlack of
 // item-major's: with few items per head, XCD-major starts the later heads'
 // long items late. It then returns true and the grouped order of the items
-// (indices into `cost`).
+// (indices into `cost`). Launches above kXcdModelMaxWorkgroups workgroups
+// are not modelled and keep the item-major order.
 constexpr int32_t kXcds = 8;
 constexpr double kXcdMajorSlack = 1.05;
+constexpr int64_t kXcdModelMaxWorkgroups = int64_t(1) << 18;
 bool xcd_major_order(const std::vector<int64_t>& cost, const std::vector<int32_t>& sample,
                      int32_t n_groups, int32_t slots, std::vector<int64_t>& order);
 // The same for a plan's units (sample of a unit: that of its tile), which it

@@ -33,10 +33,6 @@ int32_t prepare_workspace(int64_t seq_len, const int32_t* n_img, const int32_t* 
   w.dtype = dtype;
   w.shape = tile_shape(dtype, heads / kv_heads, head_dim);
   build_plan(w.meta, w.shape.rows, kBlockN, w.plan);
-#ifdef CPATTN_CHECK_PLANS
-  st = check_plan(w.meta, w.plan);
-  if (st != CP_OK) return st;
-#endif
   const size_t R = size_t(w.meta.rows);
   size_t off = 0;
   w.off_index = off;
@@ -59,6 +55,10 @@ int32_t prepare_workspace(int64_t seq_len, const int32_t* n_img, const int32_t* 
     // one workgroup of the row-tile kernel per compute unit: 32 per XCD
     w.xcd_major = !w.unit_per_step && choose_xcd_major(w.meta, w.plan, int32_t(n_hg), 32);
   }
+#ifdef CPATTN_CHECK_PLANS
+  st = check_plan(w.meta, w.plan);  // the plan as launched (units in their final order)
+  if (st != CP_OK) return st;
+#endif
   w.off_units = off;
   off = align256(off + w.launch_units().size() * sizeof(UnitRec));
   w.plan_bytes = off;
@@ -114,10 +114,6 @@ int32_t prepare_bwd_workspace(int64_t seq_len, const int32_t* n_img, const int32
   }
   w.n_hg = heads / w.heads_per_wg;
   build_bwd_plan(w.meta, w.rows_per_tile, w.plan);
-#ifdef CPATTN_CHECK_PLANS
-  st = check_bwd_plan(w.meta, w.plan);
-  if (st != CP_OK) return st;
-#endif
   if (w.mfma) {
     // workgroup orders of the MFMA kernels: dQ runs two workgroups per
     // compute unit (64 per XCD), dK/dV one (32)
@@ -137,6 +133,10 @@ int32_t prepare_bwd_workspace(int64_t seq_len, const int32_t* n_img, const int32
       w.plan.ktiles.swap(kt);
     }
   }
+#ifdef CPATTN_CHECK_PLANS
+  st = check_bwd_plan(w.meta, w.plan);  // the plan as launched
+  if (st != CP_OK) return st;
+#endif
   const Plan& p = w.plan.rows;
   const size_t R = size_t(w.meta.rows);
   size_t off = 0;
