@@ -295,10 +295,10 @@ void attn_step_bf16_kernel(const AttnArgs a) {
 // head_dim 128: ping-pong variant.
 //
 // Work: one workgroup of 8 waves per (unit, head group), a unit being one
-// row tile with all of its ring steps in step order (or, for small grids,
-// one (row tile, step) entry). The tiles of all the unit's steps run
-// through one online softmax: the running output, sum and reference carry
-// over step boundaries, so the blocks of every step are merged by the
+// row tile over the union of its ring steps' key ranges, in key order (or,
+// for small grids, one (row tile, step) entry). All of the unit's key tiles
+// run through one online softmax: the running output, sum and reference
+// carry over span boundaries, so the blocks of every step are merged by the
 // log-sum-exp update as they come and no per-step partial leaves the
 // registers. Waves w and w+4 share a SIMD; waves 0-3 form group 0 and waves
 // 4-7 group 1. Each wave owns 32 query rows of one head; with G query heads
@@ -338,7 +338,7 @@ void attn_step_bf16_kernel(const AttnArgs a) {
 //    MFMA, so the memory queue never stalls the matrix work.
 //  * Masks of diagonal and span-edge tiles are built as a 64-bit lane mask
 //    and applied with bitfield selects, keeping scalar registers free.
-// Scalar walk over an entry's 64-key tiles: up to three key spans, each
+// Scalar walk over a unit's 64-key tiles, span after span, each span
 // walked from its start rounded down to 8 keys. Holds the current tile
 // start kt and its span's [k0, k1).
 struct TileCursor {
@@ -390,7 +390,8 @@ void attn_rank_bf16_d128_kernel(const AttnArgs a) {
   const int lrow = tile.local0 + rin;
   const int grow = tile.g0 + rin;
   const int wave_lo = tile.g0 + rsub * 32;
-  // The unit's key spans: every step's spans, contiguous and in step order.
+  // The unit's key spans, contiguous in the span list: the union of its
+  // steps' spans in key order (row-tile schedule) or one step's spans.
   const const_ptr<SpanRec> spans = scalar_view(a.spans) + steps[0].span_begin;
   const int n_spans = steps[n_steps - 1].span_end - steps[0].span_begin;
   const int n_tiles = unit.n_tiles;  // the planner counted the unit's 64-key tiles

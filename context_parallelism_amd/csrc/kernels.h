@@ -19,7 +19,8 @@ struct AttnArgs {
   const TileRec* tiles;
   const EntryRec* entries;
   const SpanRec* spans;
-  const EntryRec* tile_entries;  // entries in (tile, step) order (unit kernel)
+  const EntryRec* tile_entries;  // the units' entries: unit entries (row-tile schedule) or
+                                 // (tile, step) entries (per-step schedule)
   const UnitRec* units;          // unit kernel work list
   void* out;                     // [R, H, D] in the input dtype (unit kernel)
   float* lse;                    // [H, R] fp32 (unit kernel)
@@ -50,7 +51,7 @@ struct BwdArgs {
   float* dv;           // [T, Hkv, 128]
   const TileRec* tiles;
   const SpanRec* spans;
-  const EntryRec* tile_entries;
+  const EntryRec* tile_entries;  // the dQ units' entries (each the union of a row tile's step spans)
   const UnitRec* units;
   const KeyTileRec* ktiles;
   int32_t R, H, Hkv, n_hg, group, nrb;

@@ -202,6 +202,36 @@ void build_plan(const Meta& m, int32_t bm, int32_t bn, Plan& p) {
     units.back().u.e1 = e + 1;
     units.back().cost += pend[i].cost;
   }
+  // A row-tile unit carries one online softmax across all ring steps, so it
+  // may walk the union of its steps' key ranges in any order: the ranges of
+  // different steps are disjoint, and softmax over a union of disjoint key
+  // sets is the same whatever order the sets come in. Its unit entry lists
+  // the step spans sorted by key and joined where one ends at the next's
+  // start, which leaves one range per row tile of a single-sample text share
+  // (the sample's start up to the tile's last row) and saves the key-tile
+  // rounding at each range end that does not fall on a tile boundary.
+  p.unit_entries.reserve(units.size());
+  std::vector<SpanRec> steps_spans;
+  for (PendingUnit& u : units) {
+    const EntryRec& first = p.tile_entries[size_t(u.u.e0)];
+    const EntryRec& last = p.tile_entries[size_t(u.u.e1 - 1)];
+    steps_spans.assign(p.spans.begin() + first.span_begin, p.spans.begin() + last.span_end);
+    std::sort(steps_spans.begin(), steps_spans.end(),
+              [](const SpanRec& x, const SpanRec& y) { return x.k0 < y.k0; });
+    EntryRec ue{u.u.tile, -1, int32_t(p.spans.size()), 0};
+    int64_t cost = 0;
+    for (size_t i = 0; i < steps_spans.size();) {
+      SpanRec sp = steps_spans[i++];
+      while (i < steps_spans.size() && steps_spans[i].k0 == sp.k1) sp.k1 = steps_spans[i++].k1;
+      p.spans.push_back(sp);
+      cost += (int64_t(sp.k1) - (sp.k0 & ~7) + bn - 1) / bn;
+    }
+    ue.span_end = int32_t(p.spans.size());
+    u.u.e0 = int32_t(p.unit_entries.size());
+    u.u.e1 = u.u.e0 + 1;
+    u.cost = cost;
+    p.unit_entries.push_back(ue);
+  }
   std::stable_sort(units.begin(), units.end(),
                    [](const PendingUnit& x, const PendingUnit& y) { return x.cost > y.cost; });
   p.units.reserve(units.size());

@@ -78,12 +78,16 @@ std::vector<Segment> segments(const Meta& m);
 
 // Device-side plan records (plain int32 so the same bytes serve host and GPU).
 struct TileRec { int32_t local0, nrows, g0, pad; };          // a row tile
-struct EntryRec { int32_t tile, step, span_begin, span_end; };  // (tile, step) work
-struct SpanRec { int32_t k0, k1; };                          // global keys [k0, k1)
-// All ring steps of one row tile: tile_entries[e0, e1), in step order; their
-// key spans are contiguous in the span list. n_tiles: the key tiles of the
-// plan's bn keys a kernel walks over those spans, each span from its start
-// rounded down to 8 keys (counted here so the kernel need not walk the spans).
+// (tile, step) work; step is -1 in a unit entry, which covers all steps
+struct EntryRec { int32_t tile, step, span_begin, span_end; };
+struct SpanRec { int32_t k0, k1; };  // global keys [k0, k1)
+// Work of one workgroup: entries [e0, e1) of the entry list its launch
+// uploads, whose key spans are contiguous in the span list. A row-tile unit
+// (`units`) has one unit entry (unit_entries[e0], e1 = e0 + 1): the union
+// of the tile's step spans in key order. A step unit (`step_units`) has one
+// (tile, step) entry of tile_entries. n_tiles: the key tiles of the plan's
+// bn keys a kernel walks over those spans, each span from its start rounded
+// down to 8 keys (counted here so the kernel need not walk the spans).
 struct UnitRec { int32_t tile, e0, e1, n_tiles; };
 
 struct Plan {
@@ -91,6 +95,9 @@ struct Plan {
   std::vector<TileRec> tiles;
   std::vector<EntryRec> entries;  // launch order: longest first
   std::vector<EntryRec> tile_entries;  // the same entries in (tile, step) order
+  // one per row tile that has entries, in tile order: all of its steps'
+  // spans, sorted by key and joined where one ends at the next's start
+  std::vector<EntryRec> unit_entries;
   std::vector<UnitRec> units;          // one per row tile, launch order: longest first
   std::vector<UnitRec> step_units;     // one per entry (a single step), longest first
   int64_t pad_rows = 0;                // rank-local rows with index -1
@@ -107,7 +114,8 @@ void step_ranges(const Meta& m, int32_t sample, int32_t step, std::vector<SpanRe
 
 // Row tiles of `bm` rows cut per segment; for each tile and step the key
 // spans it can see (clipped to the tile's last row), entries sorted by
-// descending key-tile count (`bn` keys per tile).
+// descending key-tile count (`bn` keys per tile); for each tile the union of
+// those spans (its unit entry).
 void build_plan(const Meta& m, int32_t bm, int32_t bn, Plan& p);
 
 // Workgroup order of the row-tile kernel (and of the backward's dQ and

@@ -133,28 +133,51 @@ int32_t check_plan(const Meta& m, const Plan& p) {
     std::sort(a.begin(), a.end());
     if (a != b) return CP_EINVAL;  // tile_entries is sorted by (tile, step) above
   }
-  // units: one per tile that has entries, its entries contiguous, all of
-  // that tile, spans contiguous across the unit's steps
-  std::vector<uint8_t> unit_seen(p.tiles.size(), 0);
-  // key tiles of p.bn keys over a unit's spans, each from its start rounded down to 8
-  auto walk_tiles = [&](int32_t e0, int32_t e1) {
+  // key tiles of p.bn keys over entries [e0, e1) of `list` (their spans
+  // contiguous), each span from its start rounded down to 8
+  auto walk_tiles = [&](const std::vector<EntryRec>& list, int32_t e0, int32_t e1) {
     int64_t n = 0;
-    for (int32_t i = p.tile_entries[size_t(e0)].span_begin; i < p.tile_entries[size_t(e1 - 1)].span_end; ++i)
+    for (int32_t i = list[size_t(e0)].span_begin; i < list[size_t(e1 - 1)].span_end; ++i)
       n += (int64_t(p.spans[size_t(i)].k1) - (p.spans[size_t(i)].k0 & ~7) + p.bn - 1) / p.bn;
     return n;
   };
+  // units: one per tile that has entries, each with its own unit entry,
+  // whose spans are the tile's step spans in key order, joined where one
+  // ends at the next's start: sorted, apart, and covered exactly by them
+  if (p.unit_entries.size() != p.units.size()) return CP_EINVAL;
+  std::vector<uint8_t> unit_seen(p.tiles.size(), 0), ue_seen(p.unit_entries.size(), 0);
+  std::vector<SpanRec> tile_spans;
   for (const UnitRec& u : p.units) {
     if (u.tile < 0 || size_t(u.tile) >= p.tiles.size() || unit_seen[size_t(u.tile)]) return CP_EINVAL;
     unit_seen[size_t(u.tile)] = 1;
-    if (u.e0 < 0 || u.e0 >= u.e1 || size_t(u.e1) > p.tile_entries.size()) return CP_EINVAL;
-    if (int64_t(u.n_tiles) != walk_tiles(u.e0, u.e1)) return CP_EINVAL;
-    for (int32_t e = u.e0; e < u.e1; ++e) {
-      if (p.tile_entries[size_t(e)].tile != u.tile) return CP_EINVAL;
-      if (e > u.e0 && p.tile_entries[size_t(e)].span_begin != p.tile_entries[size_t(e - 1)].span_end)
-        return CP_EINVAL;
+    if (u.e0 < 0 || u.e1 != u.e0 + 1 || size_t(u.e0) >= p.unit_entries.size() || ue_seen[size_t(u.e0)])
+      return CP_EINVAL;
+    ue_seen[size_t(u.e0)] = 1;
+    const EntryRec& ue = p.unit_entries[size_t(u.e0)];
+    if (ue.tile != u.tile || ue.step != -1) return CP_EINVAL;
+    if (ue.span_begin < 0 || ue.span_begin >= ue.span_end || size_t(ue.span_end) > p.spans.size())
+      return CP_EINVAL;
+    if (int64_t(u.n_tiles) != walk_tiles(p.unit_entries, u.e0, u.e1)) return CP_EINVAL;
+    tile_spans.clear();
+    for (const EntryRec& e : p.tile_entries)
+      if (e.tile == u.tile)
+        for (int32_t i = e.span_begin; i < e.span_end; ++i) tile_spans.push_back(p.spans[size_t(i)]);
+    std::sort(tile_spans.begin(), tile_spans.end(),
+              [](const SpanRec& x, const SpanRec& y) { return x.k0 < y.k0; });
+    size_t j = 0;
+    int64_t prev_k1 = INT64_MIN;
+    for (int32_t i = ue.span_begin; i < ue.span_end; ++i) {
+      const SpanRec& sp = p.spans[size_t(i)];
+      if (sp.k0 >= sp.k1 || int64_t(sp.k0) <= prev_k1) return CP_EINVAL;  // sorted and apart
+      prev_k1 = sp.k1;
+      int64_t cur = sp.k0;
+      while (cur < sp.k1) {
+        if (j >= tile_spans.size() || tile_spans[j].k0 != cur) return CP_EINVAL;
+        cur = tile_spans[j++].k1;
+      }
+      if (cur != sp.k1) return CP_EINVAL;
     }
-    if (u.e0 > 0 && p.tile_entries[size_t(u.e0 - 1)].tile == u.tile) return CP_EINVAL;
-    if (size_t(u.e1) < p.tile_entries.size() && p.tile_entries[size_t(u.e1)].tile == u.tile) return CP_EINVAL;
+    if (j != tile_spans.size()) return CP_EINVAL;
   }
   for (size_t t = 0; t < p.tiles.size(); ++t)
     if (bool(unit_seen[t]) != (p.row_mask[size_t(p.tiles[t].local0)] != 0)) return CP_EINVAL;
@@ -164,7 +187,7 @@ int32_t check_plan(const Meta& m, const Plan& p) {
       return CP_EINVAL;
     su_seen[size_t(u.e0)] = 1;
     if (p.tile_entries[size_t(u.e0)].tile != u.tile) return CP_EINVAL;
-    if (int64_t(u.n_tiles) != walk_tiles(u.e0, u.e1)) return CP_EINVAL;
+    if (int64_t(u.n_tiles) != walk_tiles(p.tile_entries, u.e0, u.e1)) return CP_EINVAL;
   }
 
   // the spans expose every visible pair once: the rank's real pair count

@@ -45,8 +45,6 @@ int32_t prepare_workspace(int64_t seq_len, const int32_t* n_img, const int32_t* 
   off = align256(off + w.plan.entries.size() * sizeof(EntryRec));
   w.off_spans = off;
   off = align256(off + w.plan.spans.size() * sizeof(SpanRec));
-  w.off_tile_entries = off;
-  off = align256(off + w.plan.tile_entries.size() * sizeof(EntryRec));
   w.unit_kernel = has_row_tile;
   if (w.unit_kernel) {
     const int64_t n_hg = heads / w.shape.heads_per_wg;
@@ -59,6 +57,8 @@ int32_t prepare_workspace(int64_t seq_len, const int32_t* n_img, const int32_t* 
   st = check_plan(w.meta, w.plan);  // the plan as launched (units in their final order)
   if (st != CP_OK) return st;
 #endif
+  w.off_tile_entries = off;
+  off = align256(off + w.launch_entries().size() * sizeof(EntryRec));
   w.off_units = off;
   off = align256(off + w.launch_units().size() * sizeof(UnitRec));
   w.plan_bytes = off;
@@ -85,8 +85,8 @@ void pack_plan(const Workspace& w, uint8_t* dst) {
   if (!p.entries.empty())
     std::memcpy(dst + w.off_entries, p.entries.data(), p.entries.size() * sizeof(EntryRec));
   if (!p.spans.empty()) std::memcpy(dst + w.off_spans, p.spans.data(), p.spans.size() * sizeof(SpanRec));
-  if (!p.tile_entries.empty())
-    std::memcpy(dst + w.off_tile_entries, p.tile_entries.data(), p.tile_entries.size() * sizeof(EntryRec));
+  const std::vector<EntryRec>& e = w.launch_entries();
+  if (!e.empty()) std::memcpy(dst + w.off_tile_entries, e.data(), e.size() * sizeof(EntryRec));
   const std::vector<UnitRec>& u = w.launch_units();
   if (!u.empty()) std::memcpy(dst + w.off_units, u.data(), u.size() * sizeof(UnitRec));
 }
@@ -146,8 +146,8 @@ int32_t prepare_bwd_workspace(int64_t seq_len, const int32_t* n_img, const int32
   off = align256(off + p.tiles.size() * sizeof(TileRec));
   w.off_spans = off;
   off = align256(off + p.spans.size() * sizeof(SpanRec));
-  w.off_tile_entries = off;
-  off = align256(off + p.tile_entries.size() * sizeof(EntryRec));
+  w.off_tile_entries = off;  // the units' entries
+  off = align256(off + p.unit_entries.size() * sizeof(EntryRec));
   w.off_units = off;
   off = align256(off + p.units.size() * sizeof(UnitRec));
   w.off_ktiles = off;
@@ -177,7 +177,7 @@ void pack_bwd_plan(const BwdWorkspace& w, uint8_t* dst) {
   put(w.off_index, p.index.data(), p.index.size() * sizeof(int32_t));
   put(w.off_tiles, p.tiles.data(), p.tiles.size() * sizeof(TileRec));
   put(w.off_spans, p.spans.data(), p.spans.size() * sizeof(SpanRec));
-  put(w.off_tile_entries, p.tile_entries.data(), p.tile_entries.size() * sizeof(EntryRec));
+  put(w.off_tile_entries, p.unit_entries.data(), p.unit_entries.size() * sizeof(EntryRec));
   put(w.off_units, p.units.data(), p.units.size() * sizeof(UnitRec));
   put(w.off_ktiles, w.plan.ktiles.data(), w.plan.ktiles.size() * sizeof(KeyTileRec));
   put(w.off_row_lo, w.plan.row_lo.data(), w.plan.row_lo.size() * sizeof(int32_t));

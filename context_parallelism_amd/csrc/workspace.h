@@ -1,7 +1,9 @@
 // Workspace layout of cp_attn_rank_fwd (host only, no HIP). The device
 // workspace holds, each region 256-byte aligned:
 //   plan   : index int32[R], step mask uint32[R], tiles, entries, spans,
-//            step-ordered entries, units (uploaded from the host in one copy);
+//            the launched units' entries (step-ordered entries for step
+//            units, unit entries for row-tile units), units (uploaded from
+//            the host in one copy);
 //   part_o : per-step partial outputs fp32 [P, R, H, D] and
 //   part_l : per-step log-sum-exps fp32 [P, H, R], for the per-step kernels
 //            and the merge pass. The unit kernel (bf16, head_dim 128, large
@@ -29,6 +31,10 @@ struct Workspace {
   const std::vector<UnitRec>& launch_units() const {
     return unit_per_step ? plan.step_units : plan.units;
   }
+  // the entries the launched units index
+  const std::vector<EntryRec>& launch_entries() const {
+    return unit_kernel && !unit_per_step ? plan.unit_entries : plan.tile_entries;
+  }
   size_t plan_bytes = 0;
   size_t off_po = 0, off_pl = 0, total = 0;
 };
@@ -47,7 +53,7 @@ int32_t prepare_workspace(int64_t seq_len, const int32_t* n_img, const int32_t* 
                           int32_t split, int32_t schedule);
 
 // Backward workspace, each region 256-byte aligned:
-//   plan  : index int32[R], dQ row tiles, spans, step-ordered entries, units,
+//   plan  : index int32[R], dQ row tiles, spans, unit entries, units,
 //           dK/dV key tiles, sample start per row int32[R], per 32-row
 //           block bounds int32[nrb][2] (uploaded from the host in one copy);
 //   qr    : gathered rank-local Q rows [R, H, D] in the input dtype;
