@@ -661,6 +661,24 @@ void attn_rank_bf16_d128_kernel(const AttnArgs a) {
   // softmax work. The kernel is power-bound, so work skipped on some waves
   // raises the clock of all.
   const bool idle = tile.nrows <= rsub * 32;
+  // The walk visits keys in increasing order, and no span reaches past the
+  // tile's last row, so the key tiles that lie wholly past this wave's last
+  // row (none of its rows can see them) are the last ones of the walk, all
+  // in the last span: on a tile that ends on the causal diagonal, up to
+  // three of the four diagonal tiles for the first waves. The wave does its
+  // matrix and softmax work up to its last visible tile, rounded up to a
+  // whole loop iteration (two tiles), and only the barriers (and its loads)
+  // after that. The skipped tiles would add exact zeros.
+  int t_work = 0;
+  if (!idle) {
+    const int last_k0 = spans[n_spans - 1].k0, last_k1 = spans[n_spans - 1].k1;
+    const int first_kt = last_k0 & ~7;
+    const int wave_hi = tile.g0 + min(rsub * 32 + 32, tile.nrows);  // keys >= wave_hi: unseen
+    const int in_last = (last_k1 - first_kt + BN - 1) / BN;
+    const int seen_last = max(wave_hi - first_kt + BN - 1, 0) / BN;
+    const int skip = max(in_last - seen_last, 0);
+    t_work = min(n_tiles, (n_tiles - skip + 1) & ~1);
+  }
 
   if (grp == 0) {
     // prologue: K(0) into the slot of group -1 (k1s), group 0 into slot 0
@@ -678,22 +696,7 @@ void attn_rank_bf16_d128_kernel(const AttnArgs a) {
     if (!idle) qk(k1s);  // phase 0
     fence_s();
     sync();
-    for (int t = 0; idle && t < n_tiles; t += 2) {  // (idle wave: loads only)
-      advance(ck);
-      advance(cv);
-      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-      sync();
-      load_group(krsrc(ck), vrsrc(cv), k1s, v1s);
-      sync();
-      if (t + 1 >= n_tiles) break;
-      advance(ck);
-      advance(cv);
-      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-      sync();
-      load_group(krsrc(ck), vrsrc(cv), k0s, v0s);
-      sync();
-    }
-    for (int t = 0; !idle && t < n_tiles; t += 2) {
+    for (int t = 0; t < t_work; t += 2) {
       // phase 2t+1: S(t); prepare load group t+1
       advance(ck);
       advance(cv);
@@ -715,6 +718,21 @@ void attn_rank_bf16_d128_kernel(const AttnArgs a) {
       matrix(v1s, k1s, true, k0s, v0s);
       sync();
     }
+    for (int t = t_work; t < n_tiles; t += 2) {  // (nothing left to see: loads only)
+      advance(ck);
+      advance(cv);
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      sync();
+      load_group(krsrc(ck), vrsrc(cv), k1s, v1s);
+      sync();
+      if (t + 1 >= n_tiles) break;
+      advance(ck);
+      advance(cv);
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      sync();
+      load_group(krsrc(ck), vrsrc(cv), k0s, v0s);
+      sync();
+    }
     // The last matrix phase's loads (past the end of the keys) still write
     // their slots; they land before the barrier, as the epilogue reuses the
     // slots.
@@ -726,14 +744,7 @@ void attn_rank_bf16_d128_kernel(const AttnArgs a) {
     if (!idle) qk(k1s);  // phase 1
     fence_s();
     sync();
-    for (int t = 0; idle && t < n_tiles; t += 2) {  // (idle wave: barriers only)
-      sync();
-      sync();
-      if (t + 1 >= n_tiles) break;
-      sync();
-      sync();
-    }
-    for (int t = 0; !idle && t < n_tiles; t += 2) {
+    for (int t = 0; t < t_work; t += 2) {
       softmax(cs);
       advance(cs);
       fence_p();
@@ -746,6 +757,13 @@ void attn_rank_bf16_d128_kernel(const AttnArgs a) {
       fence_p();
       sync();
       matrix(v1s, k1s, false, nullptr, nullptr);
+      sync();
+    }
+    for (int t = t_work; t < n_tiles; t += 2) {  // (nothing left to see: barriers only)
+      sync();
+      sync();
+      if (t + 1 >= n_tiles) break;
+      sync();
       sync();
     }
   }
