@@ -89,8 +89,10 @@ enum { CP_SPLIT_HEAD_TAIL = 0, CP_SPLIT_CONTIGUOUS = 1 };
  * rounding order (the log-sum-exp merge is an exact refactoring of the
  * softmax, Ring Attention's blockwise combination).
  *   CP_SCHED_ROW_TILE: one workgroup takes every ring step of a row tile
- *     in order and carries one online softmax across them; no per-step
- *     partial is written. bf16 with head_dim 128 only.
+ *     and carries one online softmax across them, walking the union of the
+ *     steps' key ranges in key order (the ranges are disjoint, so this is
+ *     the same set of keys); no per-step partial is written. bf16 with
+ *     head_dim 128 only.
  *   CP_SCHED_PER_STEP: one workgroup per (row tile, ring step); each writes
  *     its step's partial output and log-sum-exp into the workspace, and a
  *     second pass merges them. The only schedule of fp32 and head_dim 64.
@@ -179,11 +181,11 @@ cp_status cp_attn_rank_plan_stats(int64_t seq_len, const int32_t *n_img, const i
  *   4. merge the partials of each row by their log-sum-exp (Ring
  *      Attention's combination of blockwise results).
  * With bf16 and head_dim 128, steps 3 and 4 run in one kernel: a workgroup
- * takes all ring steps of a row tile in order and merges every key block
- * into one running output by the online-softmax (log-sum-exp) update,
- * across step boundaries too, so no partial leaves its registers; the
- * result equals the per-step partials merged by log-sum-exp up to rounding
- * order. Other dtypes, head_dim 64 and small grids write per-step partials
+ * takes all ring steps of a row tile, walks the union of their key ranges
+ * in key order and merges every key block into one running output by the
+ * online-softmax (log-sum-exp) update, so no partial leaves its registers;
+ * the result equals the per-step partials merged by log-sum-exp up to
+ * rounding order. Other dtypes, head_dim 64 and small grids write per-step partials
  * for all rows and merge them in a separate pass (cp_lse_merge's kernel).
  *
  * q, k, v: device, dtype CP_DTYPE_BF16 or CP_DTYPE_F32, THD layout.
