@@ -1,6 +1,7 @@
 """GPU parity: the HIP library (through the C ABI) against the fp64 oracle.
 
-Small problems, and workloads 2, 3 and 5 at full size, are compared on
+Small problems, and workloads 2, 3 and 5 at full size (3 and 5 under both
+schedules), are compared on
 every output element. Workload 4 (64K tokens) is compared on every row for
 one query head of each KV group, and on sampled rows (both ends of every
 run of rows, random rows) for all heads. Whole-output properties are
@@ -309,6 +310,16 @@ def test_workload_full(cp, num):
         eo, el = compare(out, lse, ro, rl, w.dtype, f"workload {num} r={r}")
         print(f"workload {num} rank {r}: max-abs out {eo:.3e} lse {el:.3e} "
               f"(oracle {st['wall_s']:.1f} s on {st['workers']} threads)", flush=True)
+        if num != 2:
+            # the other schedule on the same share (workload 2 takes it by
+            # default): one ring step per workgroup, partials and the merge pass
+            del out, lse
+            out_s, lse_s = cp.rank_fwd(qd, kd, vd, cp_size=w.cp_size, cp_rank=r, n_img=n_img,
+                                       cu_seqlens=cu, schedule="per_step")
+            torch.cuda.synchronize()
+            eo, el = compare(out_s, lse_s, ro, rl, w.dtype, f"workload {num} r={r} per_step")
+            print(f"workload {num} rank {r} per_step: max-abs out {eo:.3e} lse {el:.3e}", flush=True)
+            del out_s, lse_s
 
 
 def test_workload4_every_row_one_head_per_kv_group(cp):
