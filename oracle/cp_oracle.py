@@ -295,7 +295,8 @@ def attend_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, allowed: np.nda
 
 
 def rank_attention_backward(q, k, v, dout, n_img, cu_seqlens, cp_size: int, cp_rank: int,
-                            split: str = "head_tail") -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+                            split: str = "head_tail", local_rows: Optional[Sequence[int]] = None
+                            ) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
     """Gradients of one CP rank's share of causal attention.
 
     The share is the rank's rows of full-sequence causal attention
@@ -306,6 +307,12 @@ def rank_attention_backward(q, k, v, dout, n_img, cu_seqlens, cp_size: int, cp_r
     ranks (and scattering every rank's dq back by its index) gives the
     gradients of the whole sequence -- the reduction the reverse ring or an
     all-reduce performs across GPUs.
+
+    With ``local_rows`` (a subset of local row numbers) only those rows'
+    terms are taken: their dq rows (the others stay 0), and dk, dv summed
+    over them alone. A row's dq and its terms of dk and dv depend on that
+    row only (its P, dP and Delta), so the results of disjoint subsets add
+    up to the whole share's.
     """
     q, k, v, dout = _to64(q), _to64(k), _to64(v), _to64(dout)
     T, H, D = q.shape
@@ -318,9 +325,13 @@ def rank_attention_backward(q, k, v, dout, n_img, cu_seqlens, cp_size: int, cp_r
     dv = np.zeros((T, Hkv, D))
     ids = index.astype(np.int64)
     sample_of = np.searchsorted(cu, np.maximum(ids, 0), side="right") - 1
+    taken = np.ones(len(ids), dtype=bool)
+    if local_rows is not None:
+        taken[:] = False
+        taken[np.asarray(local_rows, dtype=np.int64)] = True
     for s in range(len(cu) - 1):
         a, b = int(cu[s]), int(cu[s + 1])
-        sel = np.nonzero((ids >= 0) & (sample_of == s))[0]
+        sel = np.nonzero((ids >= 0) & (sample_of == s) & taken)[0]
         if len(sel) == 0:
             continue
         rows = ids[sel]

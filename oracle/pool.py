@@ -28,7 +28,7 @@ import numpy as np
 
 from . import cp_oracle
 
-__all__ = ["default_workers", "rank_attention_pooled"]
+__all__ = ["default_workers", "rank_attention_pooled", "rank_attention_backward_pooled"]
 
 _W = {}  # per worker: the memory-mapped inputs and the BLAS limiter
 
@@ -206,3 +206,62 @@ def _as_array(x) -> np.ndarray:
         pass
     a = np.asarray(x)
     return np.ascontiguousarray(a if a.dtype in (np.float32, np.float64) else a.astype(np.float64))
+
+
+def _backward_task(inputs, job):
+    """One rank_attention_backward call: the query heads ``heads`` of KV head
+    ``kvh``, the terms of the local rows ``rows``."""
+    heads, kvh, n_img, cu, P, r, rows, split = job
+    q = np.asarray(inputs["q"][:, heads], dtype=np.float64)
+    k = np.asarray(inputs["k"][:, [kvh]], dtype=np.float64)
+    v = np.asarray(inputs["v"][:, [kvh]], dtype=np.float64)
+    do = np.asarray(inputs["dout"][:, heads], dtype=np.float64)
+    dq, dk, dv = cp_oracle.rank_attention_backward(q, k, v, do, n_img, cu, P, r, split=split,
+                                                   local_rows=rows)
+    return dq[rows], dk[:, 0], dv[:, 0]
+
+
+def rank_attention_backward_pooled(q, k, v, dout, n_img, cu_seqlens, cp_size: int, cp_rank: int,
+                                   split: str = "head_tail", workers: Optional[int] = None,
+                                   row_chunk: int = 256, timeout_s: float = 900.0):
+    """``cp_oracle.rank_attention_backward`` over (KV head, row chunk) tasks
+    in threads of this process (see ``rank_attention_pooled``). Each task
+    calls it unchanged on one KV head's query heads and a chunk of the
+    rank's rows; the parent places the chunks' dq rows and adds up their
+    dk, dv (the row terms are independent; see its docstring). Returns
+    dq [R, H, D], dk and dv [T, Hkv, D]."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    q, k, v, dout = (_as_array(x) for x in (q, k, v, dout))
+    T, H, D = q.shape
+    Hkv = k.shape[1]
+    G = H // Hkv
+    n_img = None if n_img is None else np.asarray(n_img)
+    cu = None if cu_seqlens is None else np.asarray(cu_seqlens)
+    index, _ = cp_oracle.partition_index(T, n_img, cu, cp_size, cp_rank, split)
+    R = len(index)
+    jobs = [(list(range(g * G, (g + 1) * G)), g, n_img, cu, int(cp_size), int(cp_rank),
+             np.arange(r0, min(R, r0 + row_chunk)), split)
+            for g in range(Hkv) for r0 in range(0, R, row_chunk)]
+    dq = np.zeros((R, H, D))
+    dk = np.zeros((T, Hkv, D))
+    dv = np.zeros((T, Hkv, D))
+    inputs = {"q": q, "k": k, "v": v, "dout": dout}
+    limit = threadpool_limits(1) if threadpool_limits else None
+    try:
+        with ThreadPoolExecutor(min(workers or default_workers(), max(len(jobs), 1))) as ex:
+            futs = [ex.submit(_backward_task, inputs, job) for job in jobs]
+            for job, f in zip(jobs, futs):
+                heads, g, rows = job[0], job[1], job[6]
+                gq, gk, gv = f.result(timeout=timeout_s)
+                dq[rows[0]:rows[-1] + 1, heads[0]:heads[-1] + 1] = gq
+                dk[:, g] += gk
+                dv[:, g] += gv
+    finally:
+        if limit is not None:
+            limit.restore_original_limits()
+    return dq, dk, dv

@@ -1,5 +1,7 @@
 """GPU parity of the per-rank backward (cp_attn_rank_bwd) against the fp64
-oracle's gradients (oracle.rank_attention_backward).
+oracle's gradients (oracle.rank_attention_backward): small cases for every
+rank, workloads 3 and 4 on every element, workloads 4 and 5 on sampled rows
+and keys with whole-tensor properties.
 
 Inputs q, k, v and dout are bf16 (the oracle reads the same values); out
 and lse come from the library's own forward, as in training. Two bounds:
@@ -298,6 +300,47 @@ def test_backward_workload_sampled(cp, num):
     worst = float((np.abs(got - want) / bound).max())
     print(f"  sum_keys dv vs sum_rows dout: worst |diff| / bound {worst:.3f}", flush=True)
     assert worst <= 1.0
+
+
+@pytest.mark.parametrize("num", [3, 4])
+def test_backward_workload_full(cp, num):
+    # every element of dq, dk and dv against the oracle's gradients, computed
+    # over (KV head, 256-row) tasks in threads (oracle.pool; the row terms of
+    # the backward are independent), with the per-tensor and per-row/key
+    # bounds of the small cases
+    import workloads
+    from gpu_common import pooled_oracle
+    from oracle.pool import rank_attention_backward_pooled
+
+    w = workloads.get(num)
+    q, k, v = workloads.make_inputs(w)
+    r = w.ranks[0]
+    cu = w.cu_seqlens if w.n_samples > 1 else None
+    n_img = w.n_img_array if any(w.n_img) else None
+    idx, _ = oracle.partition_index(w.seq_len, n_img, cu, w.cp_size, r)
+    H, D = w.heads, w.head_dim
+    rng = np.random.default_rng(w.seed + 7)
+    dout = torch.from_numpy(rng.standard_normal((len(idx), H, D), dtype=np.float32)).to(torch.bfloat16)
+    dout[torch.from_numpy(idx < 0)] = 0
+    print(f"bwd workload {num} rank {r}: R={len(idx)} T={w.seq_len}, every element", flush=True)
+    qd, kd, vd, dd = (t.to(DEV) for t in (q, k, v, dout))
+    out, lse = cp.rank_fwd(qd, kd, vd, cp_size=w.cp_size, cp_rank=r, n_img=n_img, cu_seqlens=cu)
+    dq, dk, dv = cp.rank_bwd(qd, kd, vd, out, lse, dd, cp_size=w.cp_size, cp_rank=r, n_img=n_img,
+                             cu_seqlens=cu)
+    torch.cuda.synchronize()
+    rq, rk, rv = rank_attention_backward_pooled(q, k, v, dout, n_img, cu, w.cp_size, r)
+    print(f"  oracle gradients done", flush=True)
+    # the Delta slack of dq (see ROW_RTOL's note), from the pooled oracle's
+    # rows of out and of attention with the keys as values
+    o, _ = pooled_oracle(q, k, v, n_img, cu, w.cp_size, r)
+    pk, _ = pooled_oracle(q, k, k, n_img, cu, w.cp_size, r)
+    do = dout.double().numpy()
+    slack = 2 * U_BF16 * np.abs(do * o).sum(axis=-1) * np.abs(pk).max(axis=-1) / np.sqrt(D)
+    errs = (rel_err(dq, rq), rel_err(dk, rk), rel_err(dv, rv))
+    rows = (row_err(dq, rq, ROW_RTOL, slack), row_err(dk, rk, ROW_RTOL), row_err(dv, rv, ROW_RTOL))
+    print(f"  rel max-abs error dq {errs[0]:.2e} dk {errs[1]:.2e} dv {errs[2]:.2e}; per row/key, "
+          f"fraction of the bound: dq {rows[0]:.2f} dk {rows[1]:.2f} dv {rows[2]:.2f}", flush=True)
+    assert max(errs) <= BWD_RTOL and max(rows) <= 1.0
 
 
 def test_backward_rank_sum_is_the_unsplit_gradient(cp):

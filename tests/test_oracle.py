@@ -554,6 +554,35 @@ def test_backward_reassembly():
     assert pin_backward_reassembly() < 1e-12
 
 
+def test_backward_row_subsets_add_up_and_pool():
+    # the row terms of the backward are independent: dq rows of a subset are
+    # the full share's, and dk, dv of disjoint subsets sum to the full
+    # share's -- so the threaded (KV head, row chunk) pool, which places and
+    # adds those pieces, reproduces the single call
+    from oracle.pool import rank_attention_backward_pooled
+
+    rng = np.random.default_rng(12)
+    n_img = np.array([7, 0, 3], np.int32)
+    cu = np.array([0, 60, 101, 190], np.int32)
+    T, H, Hkv, D, P, r = 190, 4, 2, 8, 3, 1
+    q, k, v = rand_qkv(rng, T, H, Hkv, D)
+    idx, _ = oracle.partition_index(T, n_img, cu, P, r)
+    dout = rng.standard_normal((len(idx), H, D))
+    dout[idx < 0] = 0
+    fq, fk, fv = oracle.rank_attention_backward(q, k, v, dout, n_img, cu, P, r)
+    half = np.arange(0, len(idx), 2)
+    rest = np.arange(1, len(idx), 2)
+    aq, ak, av = oracle.rank_attention_backward(q, k, v, dout, n_img, cu, P, r, local_rows=half)
+    bq, bk, bv = oracle.rank_attention_backward(q, k, v, dout, n_img, cu, P, r, local_rows=rest)
+    assert np.array_equal(aq[half], fq[half]) and np.all(aq[rest] == 0)
+    assert np.abs(ak + bk - fk).max() < 1e-12 and np.abs(av + bv - fv).max() < 1e-12
+    for chunk in (5, 16, 1000):
+        pq, pk, pv = rank_attention_backward_pooled(q, k, v, dout, n_img, cu, P, r, row_chunk=chunk,
+                                                    workers=3)
+        assert np.abs(pq - fq).max() < 1e-12
+        assert np.abs(pk - fk).max() < 1e-12 and np.abs(pv - fv).max() < 1e-12
+
+
 def test_backward_single_key_row():
     # a row that sees one key has P = 1 and dS = 0: its dq is exactly zero
     rng = np.random.default_rng(10)
